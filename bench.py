@@ -1,0 +1,252 @@
+"""Benchmark: paged decode attention on one MI355X.
+
+A step is one pass of the whole hot path for one layer of a Llama-3-8B-shaped
+decode batch (h_q 32, h_kv 8, d_h 128, bf16, block size 16, 64 requests with
+contexts uniform on [512, 4096]): the host allocator reserves blocks and maps
+the slots of the new token of every request (once per model step, i.e. every
+`layers` steps), the table/length/slot arrays go to the device, kv_append writes
+the new token's K and V, and paged_attention_decode reads the whole cache.
+The pool holds `layers` layers (32, as in Llama-3-8B) and the steps walk them in
+order, so each step reads a layer whose 0.6 GB of K/V was last touched
+`layers - 1` steps earlier, well beyond the 256 MB last-level cache, as in a real
+decode step.
+
+Prints one JSON line.  `value` is KV GB/s: K+V bytes of the valid tokens read
+by the decodes of the timed steps over their wall time.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode-attention KV GB/s (% of HBM peak) + µs/step, Llama-3-8B shape"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1024)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--seed", type=int, default=2)
+    ap.add_argument("--partition", type=int, default=512)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the paged decode "
+              "path shards by request or by KV head with no exchange, and only the one-GPU "
+              "measurement is built.", flush=True)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import paged_kv_cache_271_amd as pk
+
+    pk.load_library()
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+
+    w = synth.WORKLOADS["llama3_8b"]
+    B, H, h_q, D = w["batch"], w["h_kv"], w["h_q"], w["head_dim"]
+    L = args.layers
+    total = args.warmup + args.steps
+    model_steps = (total + L - 1) // L
+    rng = synth.streams(args.seed)
+    ctx0 = synth.uniform_contexts(rng["contexts"], B, *w["ctx_range"]).astype(np.int32)
+    final = ctx0 + model_steps          # every request grows by one token per model step
+    MB = int((final.max() + 15) // 16)
+    N = int(((final + 15) // 16).sum())
+    order = synth.permutation(rng["free_order"], N)
+    log(f"pool: {L} layers x {N} blocks ({N * H * 16 * D * 2 * 2 * L / 1e9:.1f} GB), "
+        f"B={B}, ctx {ctx0.min()}..{ctx0.max()}, {model_steps} model steps")
+
+    pool = pk.Pool(L, N, H, D, "bf16", dev, initial_free_order=order)
+    table = np.zeros((B, MB), np.int32)
+    lens = np.zeros(B, np.int32)
+    # prefill ctx0 - 1 tokens per request; each step appends one more
+    slots0 = pool.batch_reserve(table, lens, ctx0 - 1)
+    d_slots0 = torch.from_numpy(slots0).to(dev)
+    T0 = len(slots0)
+    for layer in range(L):
+        k = synth.device_normal((T0, H, D), 1000 + 2 * layer, dev, torch.bfloat16)
+        v = synth.device_normal((T0, H, D), 1001 + 2 * layer, dev, torch.bfloat16)
+        pool.append(layer, k, v, d_slots0)
+        del k, v
+    torch.cuda.synchronize()
+    log("prefill done")
+
+    # per (model step, layer) new-token K/V and queries, resident before timing
+    k_new = synth.device_normal((model_steps, L, B, H, D), 7, dev, torch.bfloat16)
+    v_new = synth.device_normal((model_steps, L, B, H, D), 8, dev, torch.bfloat16)
+    q_all = synth.device_normal((model_steps, L, B, h_q, D), 9, dev, torch.bfloat16)
+    out = torch.empty((B, h_q, D), dtype=torch.bfloat16, device=dev)
+    ws_bytes = pool.workspace_bytes(B, h_q, int(final.max()), args.partition)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    d_table = torch.empty((B, MB), dtype=torch.int32, device=dev)
+    d_lens = torch.empty(B, dtype=torch.int32, device=dev)
+    d_slots = torch.empty(B, dtype=torch.int32, device=dev)
+    scale = 1.0 / math.sqrt(D)
+    stream = torch.cuda.current_stream()
+    per_step_kv = []          # algorithmic K+V bytes of each step's decode
+    state = {"max_ctx": 0, "kv": 0}
+
+    def host_reserve():
+        slots = pool.batch_reserve(table, lens, np.ones(B, np.int32))
+        pinned = torch.empty(B * MB + 2 * B, dtype=torch.int32, pin_memory=True)
+        pn = pinned.numpy()
+        pn[:B * MB] = table.reshape(-1)
+        pn[B * MB:B * MB + B] = lens
+        pn[B * MB + B:] = slots
+        dev_buf = pinned.to(dev, non_blocking=True)
+        d_table.copy_(dev_buf[:B * MB].view(B, MB))
+        d_lens.copy_(dev_buf[B * MB:B * MB + B])
+        d_slots.copy_(dev_buf[B * MB + B:])
+        state["max_ctx"] = int(lens.max())
+        state["kv"] = int(lens.astype(np.int64).sum()) * H * D * 2 * 2
+
+    def step(i, ev=None):
+        s, r = divmod(i, L)
+        if r == 0:
+            host_reserve()
+        pool.append(r, k_new[s, r], v_new[s, r], d_slots)
+        if ev is not None:
+            ev[0].record(stream)
+        pool.decode(r, q_all[s, r], d_table, d_lens, state["max_ctx"], scale, args.partition,
+                    out=out, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+        return state["kv"]
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(args.steps):
+        per_step_kv.append(step(args.warmup + j, events[j]))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    dec_ms = np.array([a.elapsed_time(b) for a, b in events])
+    kv_total = float(sum(per_step_kv))
+    value = kv_total / wall / 1e9
+    ms_per_step = wall / args.steps * 1e3
+    mean_kv = kv_total / args.steps
+    dec_mean_s = float(dec_ms.mean()) / 1e3
+    achieved = mean_kv / dec_mean_s / 1e9
+    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step, {value:.0f} GB/s; "
+        f"decode call {dec_mean_s * 1e6:.1f} us mean (p10 {np.percentile(dec_ms, 10) * 1e3:.1f}, "
+        f"p90 {np.percentile(dec_ms, 90) * 1e3:.1f}), {achieved:.0f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(ctx0, T0, k_new, v_new, q_all, args, B, H, h_q, D, L, dev)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "llama3_8b_decode_layer",
+            "batch": B, "h_q": h_q, "h_kv": H, "head_dim": D, "block_size": 16,
+            "ctx_range": list(w["ctx_range"]), "mean_ctx": round(mean_kv / (H * D * 4) / B, 1),
+            "layers_in_pool": L, "partition_tokens": args.partition,
+            "us_per_step": round(ms_per_step * 1e3, 2),
+            "hbm_fraction": round(value / HBM_PEAK_GBS, 4),
+            "kv_bytes_per_step": int(mean_kv),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged_attention_decode (decode_mfma_kernel + reduce_kernel)",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "us_per_call": round(dec_mean_s * 1e6, 2),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(ctx0, slots0_len, k_new, v_new, q_all, args, B, H, h_q, D, L, dev):
+    """The fp64 oracle on the host cores, on a bounded sample of the same
+    workload: 8 of the requests of the last decoded layer, repeated until about
+    `cpu_seconds` have passed.  Its inputs are regenerated from the same seeded
+    generator (never read back from the pool)."""
+    import torch
+    import oracle
+    import synth
+    from threadpoolctl import threadpool_limits
+
+    last = args.warmup + args.steps - 1
+    s_last, layer = divmod(last, L)
+    to_bits = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    k_pre = synth.device_normal((slots0_len, H, D), 1000 + 2 * layer, dev, torch.bfloat16)
+    v_pre = synth.device_normal((slots0_len, H, D), 1001 + 2 * layer, dev, torch.bfloat16)
+    starts = np.concatenate([[0], np.cumsum(ctx0.astype(np.int64) - 1)])
+    q = oracle.bf16_bits_to_f64(to_bits(q_all[s_last, layer]))
+    seqs = []
+    for b in range(0, B, 8):
+        kb = torch.cat([k_pre[starts[b]:starts[b + 1]], k_new[:s_last + 1, layer, b]])
+        vb = torch.cat([v_pre[starts[b]:starts[b + 1]], v_new[:s_last + 1, layer, b]])
+        seqs.append((b, oracle.bf16_bits_to_f64(to_bits(kb)), oracle.bf16_bits_to_f64(to_bits(vb))))
+    del k_pre, v_pre
+    kv_bytes = sum(kk.shape[0] for _, kk, _ in seqs) * H * D * 2 * 2
+    reps = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            for b, kk, vv in seqs:
+                oracle.attention_fp64(q[b], kk, vv, 1.0 / math.sqrt(D))
+            reps += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        dt = time.perf_counter() - t0
+    return {
+        "value": round(kv_bytes * reps / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"fp64 oracle decode of {len(seqs)} of {B} requests of one layer "
+                  f"({kv_bytes / 1e6:.0f} MB of bf16 K/V), {reps} repetitions in {dt:.1f} s, "
+                  "BLAS limited to 1 thread",
+    }
+
+
+if __name__ == "__main__":
+    main()

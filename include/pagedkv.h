@@ -1,0 +1,225 @@
+/*
+ * pagedkv.h -- C ABI of libpagedkv: single-token decode attention over a paged
+ * KV cache on AMD Instinct MI355X (gfx950).
+ *
+ * What the operations are (from the pages this library follows):
+ *  - The cache keeps, for every layer and every token, one key and one value
+ *    vector per KV head; each decode step appends the new token's K and V and
+ *    then attends over the whole cache, the new token included
+ *    ("KV cache and PagedAttention", askaiml.pages.dev, §1 "The setup";
+ *    "Memoizing Context via KV Caching", blog.sanjeevnode.in).
+ *  - Storage is a pool of fixed-size pages; each request owns a table of page
+ *    indices and the attention kernel gathers K/V through it; pages are
+ *    uniform so handing one out is O(1); requests with a common prefix may map
+ *    the same pages (askaiml page, §4 "PagedAttention"; "KV Cache" glossary,
+ *    inferensys.com, PagedAttention block management).
+ *  - Several query heads may share one KV head (GQA; MQA when there is a single
+ *    KV head) ("KV Cache" glossary, GQA and MQA entries).
+ *  - The cache may be held in fp8 E4M3 to halve its bytes (askaiml page, §7
+ *    "KV cache quantisation").
+ *
+ * Conventions for every function:
+ *  - Every status-returning function returns a kv_status; nothing aborts or
+ *    throws.  On a non-OK return, kv_last_error() gives a message for the
+ *    calling thread.  Host-side state is unchanged by a failed call unless the
+ *    function says otherwise.
+ *  - Device pointers are HIP device addresses on the current device; host
+ *    pointers are ordinary process memory.  The library never allocates,
+ *    frees or copies device memory itself: the caller owns every buffer, and
+ *    the buffers given to kv_pool_create must outlive the pool.
+ *  - Device work is enqueued on the caller's HIP stream (`hip_stream`, a
+ *    hipStream_t; NULL means the default stream) and is asynchronous; argument
+ *    checks are synchronous.  A failed launch returns KV_E_HIP.
+ *  - Values stored in device memory (block-table entries, context lengths,
+ *    slot mappings) are a caller contract: they are not bounds-checked by the
+ *    kernels.  Every table entry a decode reads must name a block in
+ *    [0, num_blocks); every slot must be -1 or lie in [0, num_blocks*block_size).
+ *  - Host functions are not thread-safe for one pool (one scheduler thread).
+ *
+ * Pool layout in device memory, one array for K and one for V, each indexed
+ *   K: [num_layers][num_blocks][num_kv_heads][block_size][head_dim]  token-major
+ *   V: [num_layers][num_blocks][num_kv_heads][head_dim][block_size]  dim-major
+ * Element type: float (KV_F32), bfloat16 (KV_BF16) or E4M3 code bytes
+ * (KV_FP8_E4M3).  Each (block, kv-head) tile of K and of V is contiguous.
+ * fp8 pools also take two fp32 scale arrays [num_layers][num_blocks][num_kv_heads],
+ * one for K and one for V; a stored element means decode(code) * scale.
+ * Supported: block_size 16, head_dim 64 or 128.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct kv_pool kv_pool; /* opaque; holds host allocator state only */
+
+typedef enum { KV_F32 = 0, KV_BF16 = 1, KV_FP8_E4M3 = 2 } kv_dtype;
+
+typedef enum {
+  KV_OK = 0,
+  KV_E_INVALID = -1,     /* bad argument (null pointer, size, range)          */
+  KV_E_UNSUPPORTED = -2, /* shape or dtype not built into the library          */
+  KV_E_NO_BLOCKS = -3,   /* the free list is empty                             */
+  KV_E_BAD_BLOCK = -4,   /* block id out of range, or not currently allocated  */
+  KV_E_SHARED = -5,      /* write into a block mapped by more than one table   */
+  KV_E_WORKSPACE = -6,   /* workspace missing or smaller than required         */
+  KV_E_HIP = -7          /* a HIP runtime call or kernel launch failed         */
+} kv_status;
+
+typedef struct {
+  int32_t num_layers;   /* >= 1                                     */
+  int32_t num_blocks;   /* physical pages per layer, >= 1           */
+  int32_t block_size;   /* tokens per page; must be 16              */
+  int32_t num_kv_heads; /* >= 1                                     */
+  int32_t head_dim;     /* 64 or 128                                */
+  int32_t cache_dtype;  /* a kv_dtype                               */
+} kv_pool_desc;
+
+/* ---------------------------------------------------------------- sizes -- */
+
+/* Bytes of K plus V one token occupies across all layers:
+ * 2 * num_layers * num_kv_heads * head_dim * element bytes (fp8 scales not
+ * included) -- the per-token memory formula of the askaiml page, §2
+ * "Memory cost".  Returns -1 for an invalid descriptor. */
+int64_t kv_bytes_per_token(const kv_pool_desc* desc);
+
+/* Pages needed for n tokens: ceil(n / block_size) (askaiml page, §4: a
+ * 17-token request holds 2 pages of 16).  Returns -1 if n < 0 or
+ * block_size <= 0. */
+int32_t kv_blocks_for_tokens(int32_t n, int32_t block_size);
+
+/* Bytes the caller must allocate for the K array (the V array is the same
+ * size) and for each fp8 scale array (0 for non-fp8 pools).  Either output
+ * pointer may be NULL. */
+int kv_pool_buffer_bytes(const kv_pool_desc* desc, int64_t* cache_bytes, int64_t* scale_bytes);
+
+/* ----------------------------------------------------------------- pool -- */
+
+/* Create a pool over caller-owned device arrays (layout above).  k_scale and
+ * v_scale are device fp32 arrays for fp8 pools and must be NULL otherwise.
+ * initial_free_order: host array of num_blocks distinct ids (a permutation of
+ * 0..num_blocks-1) giving the order in which a fresh pool hands blocks out
+ * (first kv_block_alloc returns initial_free_order[0]); NULL means 0,1,2,...
+ * The pool copies what it needs from the descriptor and the order array. */
+int kv_pool_create(const kv_pool_desc* desc, void* k_cache, void* v_cache, float* k_scale,
+                   float* v_scale, const int32_t* initial_free_order, kv_pool** out);
+
+/* Release the host state.  The device arrays are untouched. NULL is accepted. */
+int kv_pool_destroy(kv_pool* pool);
+
+/* ------------------------------------------------------------ allocator -- */
+/* O(1) free-list allocator with reference counts (askaiml page, §4: uniform
+ * pages, O(1) allocation, prefix pages shared between requests).  Free blocks
+ * form a LIFO stack: a released block is the next one handed out. */
+
+/* Pop a free block into *block and set its count to 1.  KV_E_NO_BLOCKS when
+ * none is free. */
+int kv_block_alloc(kv_pool* pool, int32_t* block);
+
+/* Add one mapping to an allocated block (another block table now lists it).
+ * KV_E_BAD_BLOCK if out of range or free. */
+int kv_block_retain(kv_pool* pool, int32_t block);
+
+/* Drop one mapping; at zero the block is pushed on the free stack.
+ * KV_E_BAD_BLOCK if out of range or already free (double release). */
+int kv_block_release(kv_pool* pool, int32_t block);
+
+/* Current reference count (0 for a free block).  KV_E_BAD_BLOCK if out of range. */
+int kv_block_refcount(const kv_pool* pool, int32_t block, int32_t* rc);
+
+/* Number of free blocks. */
+int kv_num_free_blocks(const kv_pool* pool, int32_t* n);
+
+/* --------------------------------------------------------- slot mapping -- */
+
+/* Host: slots_out[i] = table_row[positions[i] / block_size] * block_size
+ *                      + positions[i] % block_size,
+ * the physical slot that position i of a request writes (askaiml page, §4:
+ * per-request page table).  table_row: host [n_table]; positions, slots_out:
+ * host [n].  Errors: KV_E_INVALID for a negative position or one beyond the
+ * table; KV_E_BAD_BLOCK if the block is out of range or free; KV_E_SHARED if
+ * it is mapped more than once (a shared page is never written in place).
+ * slots_out is unspecified after an error. */
+int kv_slot_mapping(const kv_pool* pool, const int32_t* table_row, int32_t n_table,
+                    const int32_t* positions, int32_t n, int32_t* slots_out);
+
+/* Host: the allocator and slot-mapping half of one decode step for a batch.
+ * For each request b in [0, B): it currently holds lens[b] tokens and will
+ * append n_new[b] more.  Blocks that positions lens[b] .. lens[b]+n_new[b]-1
+ * need and that the request does not hold yet are allocated (in request
+ * order, then block order) and written into table[b * max_blocks + j]; the
+ * slots of those positions are written to slots_out, request after request
+ * (sum of n_new entries); lens[b] is advanced by n_new[b].
+ * table, lens: host, read and written; n_new: host [B]; slots_out: host.
+ * Errors: KV_E_INVALID (negative sizes, a request outgrowing max_blocks),
+ * KV_E_NO_BLOCKS, KV_E_BAD_BLOCK / KV_E_SHARED for a held last block that is
+ * free or shared.  On error every block allocated by this call is released
+ * again in reverse order (the free stack is exactly as before) and table and
+ * lens are restored. */
+int kv_batch_reserve(kv_pool* pool, int32_t B, int32_t* table, int32_t max_blocks, int32_t* lens,
+                     const int32_t* n_new, int32_t* slots_out);
+
+/* --------------------------------------------------------------- append -- */
+
+/* Device: write T new tokens into layer `layer` of the pool.
+ * k_new, v_new: device [T][num_kv_heads][head_dim], float for KV_F32 pools and
+ * bfloat16 for KV_BF16 and KV_FP8_E4M3 pools.  slot_mapping: device int32 [T];
+ * token t goes to block slot/block_size, offset slot%block_size; -1 skips it.
+ * f32 and bf16 pools store the bits unchanged.  fp8 pools quantise per
+ * (block, kv-head) tile, separately for K and V: the tokens of one call that
+ * land in one tile (which must be consecutive tokens of the call, at
+ * increasing offsets) form a run; a run starting at offset 0 starts a fresh
+ * tile (old scale ignored), otherwise s0 is the stored scale; the new scale is
+ * s1 = max(s0, max|x| / 448) in fp32; when s1 != s0 the codes already below
+ * the run's first offset are re-encoded from decode(code)*s0; each new code is
+ * the E4M3 encoding (round to nearest even, saturating at 448) of
+ * x * (1/s1), all code 0 when s1 == 0.
+ * Two tokens of one call must not share a slot.  T == 0 is a no-op. */
+int kv_append(kv_pool* pool, int32_t layer, const void* k_new, const void* v_new,
+              const int32_t* slot_mapping, int32_t T, void* hip_stream);
+
+/* ------------------------------------------------------------ attention -- */
+
+/* Workspace bytes paged_attention_decode needs for this batch (0 when one
+ * partition covers max_ctx).  partition_tokens 0 means the default (512).
+ * Returns -1 on invalid arguments. */
+int64_t paged_attention_workspace_bytes(const kv_pool* pool, int32_t B, int32_t h_q,
+                                        int32_t max_ctx, int32_t partition_tokens);
+
+/* Device: one decode step of attention for B requests in layer `layer`.
+ * For request b and query head h (group g = h / (h_q / num_kv_heads)), with
+ * n = context_lens[b] tokens cached (the token appended this step included):
+ *   out[b][h] = sum_t softmax_t(scale * <q[b][h], K_t>) * V_t  over t < n,
+ * K_t, V_t read through block_tables[b][t / block_size]; n == 0 gives zeros.
+ * q: device [B][h_q][head_dim] of q_dtype (KV_F32 with f32 pools, KV_BF16 with
+ * bf16 and fp8 pools); out: device, same shape and dtype as q.
+ * block_tables: device int32 [B][max_blocks_per_seq]; context_lens: device
+ * int32 [B], each in [0, max_ctx]; max_ctx: host bound used to size the grid,
+ * <= max_blocks_per_seq * block_size.  h_q must be a multiple of num_kv_heads.
+ * The context is split into partitions of partition_tokens tokens (0 = 512; a
+ * multiple of block_size); when max_ctx needs more than one, the partitions
+ * keep (max, sum, weighted sum) states in `workspace` (device, at least
+ * paged_attention_workspace_bytes) and a second kernel merges them.
+ * Accumulation is fp32; the result is rounded to nearest even into out. */
+int paged_attention_decode(kv_pool* pool, int32_t layer, void* out, const void* q, int32_t q_dtype,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t B, int32_t h_q, int32_t max_ctx,
+                           float scale, int32_t partition_tokens, void* workspace,
+                           int64_t workspace_bytes, void* hip_stream);
+
+/* -------------------------------------------------------------- errors -- */
+
+/* Static name of a status code. */
+const char* kv_status_string(int status);
+
+/* Detail of the last non-OK status returned on this thread ("" if none). */
+const char* kv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,187 @@
+// kv_append: write each new token's K and V into its slot of the paged pool.
+//
+// "KV cache and PagedAttention" (askaiml.pages.dev), §1 "The setup": every
+// decode step appends the new token's K and V to the cache; §4
+// "PagedAttention": position p of a request lives in page table[p / 16] at
+// offset p % 16 (the slot the caller computed).  §7 "KV cache quantisation":
+// the cache may be held as fp8 E4M3.
+//
+// Layout per layer: K [block][kv_head][16][head_dim], V [block][kv_head][head_dim][16].
+// f32 and bf16 pools copy bits.  fp8 pools quantise one (block, kv-head) tile
+// per workgroup with one fp32 scale per tile; the rule is spelled out in
+// pagedkv.h at kv_append.
+
+#include <cstdint>
+
+#include "internal.h"
+
+namespace pagedkv {
+namespace {
+
+constexpr int kBS = kBlockSize;
+
+// ---------------------------------------------------------------- copy ----
+// One workgroup per (token, kv-head); thread d moves element d of K (to a
+// contiguous row) and of V (to a column of the dim-major tile).
+template <typename T>
+__global__ void __launch_bounds__(128) append_copy_kernel(T* __restrict__ kc, T* __restrict__ vc,
+                                                          const T* __restrict__ k_new,
+                                                          const T* __restrict__ v_new,
+                                                          const int32_t* __restrict__ slots,
+                                                          int H, int D) {
+  const int t = blockIdx.x;
+  const int g = blockIdx.y;
+  const int32_t slot = slots[t];
+  if (slot < 0) return;
+  const int64_t blk = slot / kBS;
+  const int off = slot % kBS;
+  const int64_t tile = (blk * H + g) * int64_t(kBS) * D;
+  const T* ks = k_new + (int64_t(t) * H + g) * D;
+  const T* vs = v_new + (int64_t(t) * H + g) * D;
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    kc[tile + int64_t(off) * D + d] = ks[d];
+    vc[tile + int64_t(d) * kBS + off] = vs[d];
+  }
+}
+
+// ----------------------------------------------------------------- fp8 ----
+// OCP E4M3: bias 7, subnormals m * 2^-9, S.1111.111 = NaN, max 448.
+__device__ inline float e4m3_to_float(uint32_t c) {
+  const uint32_t s = (c & 0x80u) << 24;
+  const uint32_t e = (c >> 3) & 0xFu;
+  const uint32_t m = c & 0x7u;
+  float v;
+  if (e == 0xFu && m == 0x7u) {
+    v = __uint_as_float(0x7FC00000u);
+  } else if (e == 0) {
+    v = float(m) * 0.001953125f;  // m * 2^-9, exact
+  } else {
+    v = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  }
+  return __uint_as_float(__float_as_uint(v) | s);
+}
+
+// Round to nearest even, saturate to +-448, NaN -> S.1111.111, sign kept.
+__device__ inline uint32_t float_to_e4m3(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a_bits = u & 0x7FFFFFFFu;
+  if (a_bits > 0x7F800000u) return 0x7Fu | sign;  // NaN
+  const float a = __uint_as_float(a_bits);
+  if (a >= 448.0f) return 0x7Eu | sign;
+  uint32_t code;
+  if (a < 0.015625f) {  // below the smallest normal: quantum 2^-9
+    code = uint32_t(rintf(a * 512.0f));  // 0..8; 8 is the smallest normal
+  } else {
+    // keep 3 mantissa bits, round to nearest even at bit 20
+    uint32_t r = a_bits + 0x7FFFFu + ((a_bits >> 20) & 1u);
+    r &= 0xFFF00000u;
+    const int e = int(r >> 23) - 127 + 7;  // 1..15
+    code = (uint32_t(e) << 3) | ((r >> 20) & 7u);
+  }
+  return code | sign;
+}
+
+__device__ inline float bf16_bits_to_float(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// Max over the workgroup (blockDim.x = 128 = two waves).
+__device__ inline float block_max(float v, float* red) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  return fmaxf(red[0], red[1]);
+}
+
+// One workgroup per (token t, kv-head g); only the first token of a run (the
+// consecutive tokens of this call landing in one block) does the work, for
+// the whole run.  Thread d owns dimension d of the tile.
+__global__ void __launch_bounds__(128) append_fp8_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
+                                                         float* __restrict__ ks, float* __restrict__ vs,
+                                                         const uint16_t* __restrict__ k_new,
+                                                         const uint16_t* __restrict__ v_new,
+                                                         const int32_t* __restrict__ slots, int T,
+                                                         int H, int D) {
+  __shared__ float red[2];
+  const int t = blockIdx.x;
+  const int g = blockIdx.y;
+  const int32_t slot = slots[t];
+  if (slot < 0) return;
+  const int32_t blk = slot / kBS;
+  if (t > 0) {
+    const int32_t prev = slots[t - 1];
+    if (prev >= 0 && prev / kBS == blk) return;  // not the first token of its run
+  }
+  int u = t;
+  while (u + 1 < T && slots[u + 1] >= 0 && slots[u + 1] / kBS == blk) ++u;
+  const int first_off = slot % kBS;
+  const int d = threadIdx.x;
+  const bool on = d < D;
+  const int64_t tile = (int64_t(blk) * H + g) * int64_t(kBS) * D;
+  const int64_t sidx = int64_t(blk) * H + g;
+
+  for (int which = 0; which < 2; ++which) {  // 0: K (token-major), 1: V (dim-major)
+    const uint16_t* src = which == 0 ? k_new : v_new;
+    uint8_t* cache = which == 0 ? kc : vc;
+    float* scales = which == 0 ? ks : vs;
+    auto at = [&](int off) -> int64_t {
+      return which == 0 ? tile + int64_t(off) * D + d : tile + int64_t(d) * kBS + off;
+    };
+    float amax = 0.0f;
+    if (on)
+      for (int r = t; r <= u; ++r)
+        amax = fmaxf(amax, fabsf(bf16_bits_to_float(src[(int64_t(r) * H + g) * D + d])));
+    amax = block_max(amax, red);
+    const float s0 = first_off == 0 ? 0.0f : scales[sidx];
+    const float s1 = fmaxf(s0, amax / 448.0f);
+    if (on) {
+      if (s1 == 0.0f) {
+        for (int r = t; r <= u; ++r) cache[at(slots[r] % kBS)] = 0;
+      } else {
+        const float inv = 1.0f / s1;
+        if (s1 != s0 && first_off > 0)
+          for (int off = 0; off < first_off; ++off) {
+            const float x = e4m3_to_float(cache[at(off)]) * s0;
+            cache[at(off)] = uint8_t(float_to_e4m3(x * inv));
+          }
+        for (int r = t; r <= u; ++r) {
+          const float x = bf16_bits_to_float(src[(int64_t(r) * H + g) * D + d]);
+          cache[at(slots[r] % kBS)] = uint8_t(float_to_e4m3(x * inv));
+        }
+      }
+    }
+    if (d == 0) scales[sidx] = s1;
+  }
+}
+
+}  // namespace
+
+int launch_append(const kv_pool* p, int32_t layer, const void* k_new, const void* v_new,
+                  const int32_t* slots, int32_t T, hipStream_t stream) {
+  const kv_pool_desc& d = p->desc;
+  const int64_t lo = int64_t(layer) * layer_elems(d);
+  const dim3 grid(T, d.num_kv_heads);
+  if (d.cache_dtype == KV_F32) {
+    append_copy_kernel<float><<<grid, 128, 0, stream>>>(
+        static_cast<float*>(p->k_cache) + lo, static_cast<float*>(p->v_cache) + lo,
+        static_cast<const float*>(k_new), static_cast<const float*>(v_new), slots, d.num_kv_heads,
+        d.head_dim);
+  } else if (d.cache_dtype == KV_BF16) {
+    append_copy_kernel<uint16_t><<<grid, 128, 0, stream>>>(
+        static_cast<uint16_t*>(p->k_cache) + lo, static_cast<uint16_t*>(p->v_cache) + lo,
+        static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), slots,
+        d.num_kv_heads, d.head_dim);
+  } else {
+    const int64_t so = int64_t(layer) * d.num_blocks * d.num_kv_heads;
+    append_fp8_kernel<<<grid, 128, 0, stream>>>(
+        static_cast<uint8_t*>(p->k_cache) + lo, static_cast<uint8_t*>(p->v_cache) + lo,
+        p->k_scale + so, p->v_scale + so, static_cast<const uint16_t*>(k_new),
+        static_cast<const uint16_t*>(v_new), slots, T, d.num_kv_heads, d.head_dim);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(KV_E_HIP, "kv_append launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace pagedkv

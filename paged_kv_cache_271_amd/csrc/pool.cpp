@@ -1,0 +1,331 @@
+// Host half of libpagedkv: pool descriptor checks, the O(1) LIFO block
+// allocator with reference counts, slot mapping, the batched per-step
+// reservation, argument checks of the device entry points, and error strings.
+//
+// The allocator follows "KV cache and PagedAttention" (askaiml.pages.dev),
+// §4 "PagedAttention": uniform pages make allocation O(1) and let requests
+// with a common prefix share pages; the slot of position p of a request is
+// table[p / block_size] * block_size + p % block_size.
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "internal.h"
+
+namespace {
+thread_local std::string g_last_error;
+
+bool desc_valid(const kv_pool_desc* d) {
+  return d && d->num_layers >= 1 && d->num_blocks >= 1 && d->block_size >= 1 &&
+         d->num_kv_heads >= 1 && d->head_dim >= 1 && d->cache_dtype >= KV_F32 &&
+         d->cache_dtype <= KV_FP8_E4M3;
+}
+
+bool block_live(const kv_pool* p, int32_t b) {
+  return b >= 0 && b < p->desc.num_blocks && p->rc[b] > 0;
+}
+}  // namespace
+
+namespace pagedkv {
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() { return KV_OK; }
+
+int64_t workspace_bytes(int32_t B, int32_t h_q, int32_t head_dim, int32_t num_part) {
+  if (num_part <= 1) return 0;
+  const int64_t states = int64_t(B) * h_q * num_part;
+  return states * (2 + head_dim) * int64_t(sizeof(float));
+}
+
+}  // namespace pagedkv
+
+using namespace pagedkv;
+
+extern "C" {
+
+int64_t kv_bytes_per_token(const kv_pool_desc* d) {
+  if (!desc_valid(d)) return -1;
+  return 2 * int64_t(d->num_layers) * d->num_kv_heads * d->head_dim * elem_bytes(d->cache_dtype);
+}
+
+int32_t kv_blocks_for_tokens(int32_t n, int32_t block_size) {
+  if (n < 0 || block_size <= 0) return -1;
+  return int32_t((int64_t(n) + block_size - 1) / block_size);
+}
+
+int kv_pool_buffer_bytes(const kv_pool_desc* d, int64_t* cache_bytes, int64_t* scale_bytes) {
+  if (!desc_valid(d)) return fail(KV_E_INVALID, "invalid pool descriptor");
+  const int64_t cb = int64_t(d->num_layers) * layer_elems(*d) * elem_bytes(d->cache_dtype);
+  const int64_t sb = d->cache_dtype == KV_FP8_E4M3
+                         ? int64_t(d->num_layers) * d->num_blocks * d->num_kv_heads * 4
+                         : 0;
+  if (cache_bytes) *cache_bytes = cb;
+  if (scale_bytes) *scale_bytes = sb;
+  return ok();
+}
+
+int kv_pool_create(const kv_pool_desc* d, void* k_cache, void* v_cache, float* k_scale,
+                   float* v_scale, const int32_t* order, kv_pool** out) {
+  if (!out) return fail(KV_E_INVALID, "out is NULL");
+  *out = nullptr;
+  if (!desc_valid(d)) return fail(KV_E_INVALID, "invalid pool descriptor");
+  if (d->block_size != kBlockSize)
+    return fail(KV_E_UNSUPPORTED, "block_size %d not supported (16 only)", d->block_size);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(KV_E_UNSUPPORTED, "head_dim %d not supported (64 or 128)", d->head_dim);
+  if (!k_cache || !v_cache) return fail(KV_E_INVALID, "k_cache and v_cache are required");
+  const bool fp8 = d->cache_dtype == KV_FP8_E4M3;
+  if (fp8 && (!k_scale || !v_scale))
+    return fail(KV_E_INVALID, "fp8 pools need k_scale and v_scale");
+  if (!fp8 && (k_scale || v_scale))
+    return fail(KV_E_INVALID, "scale arrays are only for fp8 pools");
+  const int32_t n = d->num_blocks;
+  std::vector<int32_t> seen(n, 0);
+  auto* p = new (std::nothrow) kv_pool();
+  if (!p) return fail(KV_E_INVALID, "out of host memory");
+  p->desc = *d;
+  p->k_cache = k_cache;
+  p->v_cache = v_cache;
+  p->k_scale = k_scale;
+  p->v_scale = v_scale;
+  p->rc.assign(n, 0);
+  p->stack.resize(n);
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t b = order ? order[i] : i;
+    if (b < 0 || b >= n || seen[b]) {
+      delete p;
+      return fail(KV_E_INVALID, "initial_free_order is not a permutation (entry %d = %d)", i, b);
+    }
+    seen[b] = 1;
+    p->stack[n - 1 - i] = b;  // order[0] ends on top
+  }
+  *out = p;
+  return ok();
+}
+
+int kv_pool_destroy(kv_pool* p) {
+  delete p;
+  return ok();
+}
+
+int kv_block_alloc(kv_pool* p, int32_t* block) {
+  if (!p || !block) return fail(KV_E_INVALID, "NULL argument");
+  if (p->stack.empty()) return fail(KV_E_NO_BLOCKS, "no free block (pool of %d)", p->desc.num_blocks);
+  const int32_t b = p->stack.back();
+  p->stack.pop_back();
+  p->rc[b] = 1;
+  *block = b;
+  return ok();
+}
+
+int kv_block_retain(kv_pool* p, int32_t b) {
+  if (!p) return fail(KV_E_INVALID, "NULL pool");
+  if (!block_live(p, b)) return fail(KV_E_BAD_BLOCK, "retain of block %d that is out of range or free", b);
+  ++p->rc[b];
+  return ok();
+}
+
+int kv_block_release(kv_pool* p, int32_t b) {
+  if (!p) return fail(KV_E_INVALID, "NULL pool");
+  if (!block_live(p, b)) return fail(KV_E_BAD_BLOCK, "release of block %d that is out of range or free", b);
+  if (--p->rc[b] == 0) p->stack.push_back(b);
+  return ok();
+}
+
+int kv_block_refcount(const kv_pool* p, int32_t b, int32_t* rc) {
+  if (!p || !rc) return fail(KV_E_INVALID, "NULL argument");
+  if (b < 0 || b >= p->desc.num_blocks) return fail(KV_E_BAD_BLOCK, "block %d out of range", b);
+  *rc = p->rc[b];
+  return ok();
+}
+
+int kv_num_free_blocks(const kv_pool* p, int32_t* n) {
+  if (!p || !n) return fail(KV_E_INVALID, "NULL argument");
+  *n = int32_t(p->stack.size());
+  return ok();
+}
+
+int kv_slot_mapping(const kv_pool* p, const int32_t* table_row, int32_t n_table,
+                    const int32_t* positions, int32_t n, int32_t* slots_out) {
+  if (!p) return fail(KV_E_INVALID, "NULL pool");
+  if (n < 0 || n_table < 0) return fail(KV_E_INVALID, "negative size");
+  if (n > 0 && (!positions || !slots_out || (n_table > 0 && !table_row)))
+    return fail(KV_E_INVALID, "NULL array");
+  const int32_t bs = p->desc.block_size;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t pos = positions[i];
+    if (pos < 0 || pos / bs >= n_table)
+      return fail(KV_E_INVALID, "position %d (index %d) outside a table of %d blocks", pos, i, n_table);
+    const int32_t b = table_row[pos / bs];
+    if (!block_live(p, b)) return fail(KV_E_BAD_BLOCK, "position %d maps to block %d that is out of range or free", pos, b);
+    if (p->rc[b] > 1) return fail(KV_E_SHARED, "position %d maps to block %d shared by %d tables", pos, b, p->rc[b]);
+    slots_out[i] = b * bs + pos % bs;
+  }
+  return ok();
+}
+
+int kv_batch_reserve(kv_pool* p, int32_t B, int32_t* table, int32_t max_blocks, int32_t* lens,
+                     const int32_t* n_new, int32_t* slots_out) {
+  if (!p) return fail(KV_E_INVALID, "NULL pool");
+  if (B < 0 || max_blocks < 0) return fail(KV_E_INVALID, "negative size");
+  if (B == 0) return ok();
+  if (!table || !lens || !n_new || !slots_out) return fail(KV_E_INVALID, "NULL array");
+  const int32_t bs = p->desc.block_size;
+  // (request, block index, previous table value) of every block taken here
+  std::vector<int64_t> taken_at;
+  std::vector<int32_t> taken_prev, taken_blk;
+  int status = KV_OK;
+  int64_t o = 0;
+  int32_t b = 0;
+  for (; b < B && status == KV_OK; ++b) {
+    const int32_t len = lens[b], add = n_new[b];
+    if (len < 0 || add < 0) {
+      status = fail(KV_E_INVALID, "request %d: negative length", b);
+      break;
+    }
+    const int64_t end = int64_t(len) + add;
+    if (kv_blocks_for_tokens(int32_t(end), bs) > max_blocks || end > INT32_MAX) {
+      status = fail(KV_E_INVALID, "request %d grows to %lld tokens, beyond %d blocks", b,
+                    (long long)end, max_blocks);
+      break;
+    }
+    if (add == 0) continue;
+    int32_t* row = table + int64_t(b) * max_blocks;
+    const int32_t have = kv_blocks_for_tokens(len, bs);
+    if (len % bs != 0) {  // the partially filled last block is written in place
+      const int32_t last = row[have - 1];
+      if (!block_live(p, last)) {
+        status = fail(KV_E_BAD_BLOCK, "request %d: last block %d out of range or free", b, last);
+        break;
+      }
+      if (p->rc[last] > 1) {
+        status = fail(KV_E_SHARED, "request %d: last block %d is shared", b, last);
+        break;
+      }
+    }
+    const int32_t need = kv_blocks_for_tokens(int32_t(end), bs);
+    for (int32_t j = have; j < need; ++j) {
+      if (p->stack.empty()) {
+        status = fail(KV_E_NO_BLOCKS, "request %d: no free block for logical block %d", b, j);
+        break;
+      }
+      const int32_t nb = p->stack.back();
+      p->stack.pop_back();
+      p->rc[nb] = 1;
+      taken_at.push_back(int64_t(b) * max_blocks + j);
+      taken_prev.push_back(row[j]);
+      taken_blk.push_back(nb);
+      row[j] = nb;
+    }
+    if (status != KV_OK) break;
+    for (int32_t i = 0; i < add; ++i) {
+      const int32_t pos = len + i;
+      slots_out[o++] = row[pos / bs] * bs + pos % bs;
+    }
+  }
+  if (status != KV_OK) {
+    for (size_t i = taken_blk.size(); i-- > 0;) {  // undo in reverse: stack as before
+      p->rc[taken_blk[i]] = 0;
+      p->stack.push_back(taken_blk[i]);
+      table[taken_at[i]] = taken_prev[i];
+    }
+    return status;
+  }
+  for (int32_t i = 0; i < B; ++i) lens[i] += n_new[i];
+  return ok();
+}
+
+int kv_append(kv_pool* p, int32_t layer, const void* k_new, const void* v_new,
+              const int32_t* slots, int32_t T, void* stream) {
+  if (!p) return fail(KV_E_INVALID, "NULL pool");
+  if (layer < 0 || layer >= p->desc.num_layers) return fail(KV_E_INVALID, "layer %d out of range", layer);
+  if (T < 0) return fail(KV_E_INVALID, "negative token count");
+  if (T == 0) return ok();
+  if (!k_new || !v_new || !slots) return fail(KV_E_INVALID, "NULL device array");
+  return launch_append(p, layer, k_new, v_new, slots, T, static_cast<hipStream_t>(stream));
+}
+
+int64_t paged_attention_workspace_bytes(const kv_pool* p, int32_t B, int32_t h_q, int32_t max_ctx,
+                                        int32_t part) {
+  if (!p || B < 0 || h_q <= 0 || max_ctx < 0 || part < 0) return -1;
+  if (part == 0) part = kDefaultPartition;
+  if (part % p->desc.block_size != 0) return -1;
+  const int32_t np = max_ctx == 0 ? 1 : int32_t((int64_t(max_ctx) + part - 1) / part);
+  return workspace_bytes(B, h_q, p->desc.head_dim, np);
+}
+
+int paged_attention_decode(kv_pool* p, int32_t layer, void* out, const void* q, int32_t q_dtype,
+                           const int32_t* tables, int32_t max_blocks, const int32_t* ctx, int32_t B,
+                           int32_t h_q, int32_t max_ctx, float scale, int32_t part, void* ws,
+                           int64_t ws_bytes, void* stream) {
+  if (!p) return fail(KV_E_INVALID, "NULL pool");
+  const kv_pool_desc& d = p->desc;
+  if (layer < 0 || layer >= d.num_layers) return fail(KV_E_INVALID, "layer %d out of range", layer);
+  if (B < 0) return fail(KV_E_INVALID, "negative batch");
+  if (B == 0) return ok();
+  if (B > 65535) return fail(KV_E_UNSUPPORTED, "batch %d above 65535", B);
+  if (!out || !q || !tables || !ctx) return fail(KV_E_INVALID, "NULL device array");
+  const int32_t want_q = d.cache_dtype == KV_F32 ? KV_F32 : KV_BF16;
+  if (q_dtype != want_q)
+    return fail(KV_E_UNSUPPORTED, "q dtype %d does not match the pool (needs %d)", q_dtype, want_q);
+  if (h_q <= 0 || h_q % d.num_kv_heads != 0)
+    return fail(KV_E_INVALID, "h_q %d is not a positive multiple of %d KV heads", h_q, d.num_kv_heads);
+  if (max_blocks <= 0 || max_ctx < 0 || int64_t(max_ctx) > int64_t(max_blocks) * d.block_size)
+    return fail(KV_E_INVALID, "max_ctx %d outside [0, %d blocks * %d]", max_ctx, max_blocks, d.block_size);
+  if (part == 0) part = kDefaultPartition;
+  if (part < 0 || part % d.block_size != 0)
+    return fail(KV_E_INVALID, "partition_tokens %d is not a positive multiple of %d", part, d.block_size);
+  const int32_t np = max_ctx == 0 ? 1 : int32_t((int64_t(max_ctx) + part - 1) / part);
+  const int64_t need = workspace_bytes(B, h_q, d.head_dim, np);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(KV_E_WORKSPACE, "workspace of %lld bytes, %lld needed", (long long)ws_bytes, (long long)need);
+  if (int64_t(d.num_kv_heads) * ((h_q / d.num_kv_heads + 15) / 16) > 65535)
+    return fail(KV_E_UNSUPPORTED, "too many heads");
+  DecodeArgs a{};
+  a.pool = p;
+  a.layer = layer;
+  a.out = out;
+  a.q = q;
+  a.tables = tables;
+  a.max_blocks = max_blocks;
+  a.ctx = ctx;
+  a.B = B;
+  a.h_q = h_q;
+  a.max_ctx = max_ctx;
+  a.scale = scale;
+  a.part = part;
+  a.num_part = np;
+  if (need > 0) {
+    a.ws_ml = static_cast<float*>(ws);
+    a.ws_acc = a.ws_ml + int64_t(B) * h_q * np * 2;
+  }
+  return launch_decode(a, static_cast<hipStream_t>(stream));
+}
+
+const char* kv_status_string(int s) {
+  switch (s) {
+    case KV_OK: return "KV_OK";
+    case KV_E_INVALID: return "KV_E_INVALID";
+    case KV_E_UNSUPPORTED: return "KV_E_UNSUPPORTED";
+    case KV_E_NO_BLOCKS: return "KV_E_NO_BLOCKS";
+    case KV_E_BAD_BLOCK: return "KV_E_BAD_BLOCK";
+    case KV_E_SHARED: return "KV_E_SHARED";
+    case KV_E_WORKSPACE: return "KV_E_WORKSPACE";
+    case KV_E_HIP: return "KV_E_HIP";
+    default: return "KV_E_UNKNOWN";
+  }
+}
+
+const char* kv_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"
