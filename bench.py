@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--partition", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one plain 1 GiB device copy before timing (scales HBM byte counters)")
     return ap.parse_args()
 
 
@@ -136,6 +138,15 @@ def main():
         if ev is not None:
             ev[1].record(stream)
         return state["kv"]
+
+    if args.copy_calibration:
+        src = torch.empty(2 ** 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("copy calibration: 1 GiB read + 1 GiB written by one copy kernel")
 
     for i in range(args.warmup):
         step(i)

@@ -127,6 +127,14 @@ int kv_block_retain(kv_pool* pool, int32_t block);
  * KV_E_BAD_BLOCK if out of range or already free (double release). */
 int kv_block_release(kv_pool* pool, int32_t block);
 
+/* Retain, or release, each of the n blocks of `blocks` (host array) in order:
+ * one mapping more (or less) per entry, as when a request that shares a
+ * prefix is admitted (or retired).  On an error the entries already processed
+ * are undone in reverse order, so counts and the free stack are exactly as
+ * before the call, and the status of the failing entry is returned. */
+int kv_block_retain_n(kv_pool* pool, const int32_t* blocks, int32_t n);
+int kv_block_release_n(kv_pool* pool, const int32_t* blocks, int32_t n);
+
 /* Current reference count (0 for a free block).  KV_E_BAD_BLOCK if out of range. */
 int kv_block_refcount(const kv_pool* pool, int32_t block, int32_t* rc);
 

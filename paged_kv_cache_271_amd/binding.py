@@ -42,6 +42,8 @@ SIGNATURES = {
     "kv_block_alloc": (ctypes.c_int, [_P, _PI32]),
     "kv_block_retain": (ctypes.c_int, [_P, _I32]),
     "kv_block_release": (ctypes.c_int, [_P, _I32]),
+    "kv_block_retain_n": (ctypes.c_int, [_P, _PI32, _I32]),
+    "kv_block_release_n": (ctypes.c_int, [_P, _PI32, _I32]),
     "kv_block_refcount": (ctypes.c_int, [_P, _I32, _PI32]),
     "kv_num_free_blocks": (ctypes.c_int, [_P, _PI32]),
     "kv_slot_mapping": (ctypes.c_int, [_P, _PI32, _I32, _PI32, _I32, _PI32]),
@@ -184,6 +186,16 @@ def kv_block_release(h, block):
     _check(_lib.kv_block_release(h, int(block)))
 
 
+def kv_block_retain_n(h, blocks):
+    a = _host_i32(blocks)
+    _check(_lib.kv_block_retain_n(h, _i32p(a), a.size))
+
+
+def kv_block_release_n(h, blocks):
+    a = _host_i32(blocks)
+    _check(_lib.kv_block_release_n(h, _i32p(a), a.size))
+
+
 def kv_block_refcount(h, block):
     rc = ctypes.c_int32()
     _check(_lib.kv_block_refcount(h, int(block), ctypes.byref(rc)))
@@ -317,6 +329,12 @@ class Pool:
 
     def release(self, b):
         kv_block_release(self.handle, b)
+
+    def retain_n(self, blocks):
+        kv_block_retain_n(self.handle, blocks)
+
+    def release_n(self, blocks):
+        kv_block_release_n(self.handle, blocks)
 
     def refcount(self, b):
         return kv_block_refcount(self.handle, b)

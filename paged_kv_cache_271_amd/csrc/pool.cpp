@@ -142,6 +142,36 @@ int kv_block_release(kv_pool* p, int32_t b) {
   return ok();
 }
 
+int kv_block_retain_n(kv_pool* p, const int32_t* blocks, int32_t n) {
+  if (!p || n < 0 || (n > 0 && !blocks)) return fail(KV_E_INVALID, "invalid arguments");
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t b = blocks[i];
+    if (!block_live(p, b)) {
+      for (int32_t j = i; j-- > 0;) --p->rc[blocks[j]];  // counts were >= 2, none freed
+      return fail(KV_E_BAD_BLOCK, "retain of block %d (entry %d) that is out of range or free", b, i);
+    }
+    ++p->rc[b];
+  }
+  return ok();
+}
+
+int kv_block_release_n(kv_pool* p, const int32_t* blocks, int32_t n) {
+  if (!p || n < 0 || (n > 0 && !blocks)) return fail(KV_E_INVALID, "invalid arguments");
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t b = blocks[i];
+    if (!block_live(p, b)) {
+      for (int32_t j = i; j-- > 0;) {  // undo in reverse: a freed block is on top
+        const int32_t u = blocks[j];
+        if (p->rc[u] == 0) p->stack.pop_back();
+        ++p->rc[u];
+      }
+      return fail(KV_E_BAD_BLOCK, "release of block %d (entry %d) that is out of range or free", b, i);
+    }
+    if (--p->rc[b] == 0) p->stack.push_back(b);
+  }
+  return ok();
+}
+
 int kv_block_refcount(const kv_pool* p, int32_t b, int32_t* rc) {
   if (!p || !rc) return fail(KV_E_INVALID, "NULL argument");
   if (b < 0 || b >= p->desc.num_blocks) return fail(KV_E_BAD_BLOCK, "block %d out of range", b);

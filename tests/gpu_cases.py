@@ -17,8 +17,10 @@ NAN_BITS = {"bf16": 0x7FC0, "fp8": 0x7F}
 TOL = {
     "f32": (1e-5, 0.0),
     "bf16": (2e-2, 2e-2),
-    "fp8": (6e-2, 0.0),      # end to end, against the values before quantisation
-    "fp8q": (2e-2, 2e-2),    # against the dequantised codes the kernel reads
+    # fp8 caches: against the oracle on the values the cache holds (the
+    # dequantised codes, produced bit-exactly by the oracle's own quantiser)
+    "fp8": (6e-2, 0.0),
+    "fp8q": (2e-2, 2e-2),    # a tighter bound the kernel also meets
 }
 
 

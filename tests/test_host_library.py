@@ -33,7 +33,7 @@ def _declared_functions():
 
 def test_exports_every_declared_function(lib):
     names = _declared_functions()
-    assert len(names) == 17
+    assert len(names) == 19
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(pk.SIGNATURES) == names
@@ -256,4 +256,34 @@ def test_batch_reserve_refuses_shared_last_block_and_rolls_back(lib):
     assert pk.kv_num_free_blocks(h) == free
     assert np.array_equal(table, t0) and np.array_equal(lens, l0)
     assert pk.kv_block_alloc(h) == 4                 # the stack is exactly as before
+    pk.kv_pool_destroy(h)
+
+
+def test_retain_release_n_and_rollback(lib):
+    order = list(range(10))
+    h, _ = _pool(lib, 10, order)
+    ref = oracle.RefAllocator(10, order)
+    blocks = [pk.kv_block_alloc(h) for _ in range(6)]
+    for _ in range(6):
+        ref.alloc()
+    pk.kv_block_retain_n(h, blocks[:4] + blocks[:2])
+    for b in blocks[:4] + blocks[:2]:
+        ref.retain(b)
+    pk.kv_block_release_n(h, blocks[1:6])
+    for b in blocks[1:6]:
+        ref.release(b)
+    for b in range(10):
+        assert pk.kv_block_refcount(h, b) == ref.refcount(b)
+    assert pk.kv_num_free_blocks(h) == ref.num_free()
+    # a failing entry undoes the whole call: counts and free order unchanged
+    before = [pk.kv_block_refcount(h, b) for b in range(10)]
+    free_before = pk.kv_num_free_blocks(h)
+    with pytest.raises(pk.KVError, match="BAD_BLOCK"):
+        pk.kv_block_release_n(h, [blocks[0], blocks[0], blocks[0], blocks[0], 9])
+    with pytest.raises(pk.KVError, match="BAD_BLOCK"):
+        pk.kv_block_retain_n(h, [blocks[0], blocks[1], 8])
+    assert [pk.kv_block_refcount(h, b) for b in range(10)] == before
+    assert pk.kv_num_free_blocks(h) == free_before
+    assert [pk.kv_block_alloc(h) for _ in range(free_before)] == \
+        [ref.alloc() for _ in range(free_before)]
     pk.kv_pool_destroy(h)

@@ -1,0 +1,181 @@
+"""Multi-step drivers of the paged decode path, shared by the tests and the
+benchmark.  They call only the library (through its binding) and draw inputs
+from `synth`; they hold no attention arithmetic.
+
+PrefixChurn -- continuous batching over a shared prefix ("KV cache and
+PagedAttention", askaiml.pages.dev, §4 "PagedAttention" page sharing, §5
+"Continuous batching", §6 "Prefix caching"): `batch` live requests map the
+same prefix blocks (reference count 1 for the prefix entry plus one per live
+request) followed by private suffix blocks.  Each step retires `churn`
+requests (their blocks released: the prefix count drops, suffix blocks return
+to the free list), admits as many new ones with fresh suffixes, and then, for
+every layer, one kv_append call writes the new suffixes and one new token of
+every other live request, and paged_attention_decode reads all of them.
+"""
+
+import math
+
+import numpy as np
+
+import synth
+
+H, D, HQ = 8, 128, 32
+
+
+class PrefixChurn:
+    def __init__(self, dev, layers=32, batch=256, prefix=2000, suffix=(5, 500), steps=64,
+                 churn=26, seed=4, record_layers=(), record_slots=(), mirror=None):
+        import torch
+        import paged_kv_cache_271_amd as pk
+        self.torch, self.pk, self.dev = torch, pk, dev
+        assert prefix % 16 == 0, "the shared prefix must fill whole blocks"
+        self.layers, self.batch, self.prefix_len = layers, batch, prefix
+        self.suffix, self.steps, self.churn = suffix, steps, churn
+        self.rng = synth.streams(seed)
+        self.seed = seed
+        self.pb = prefix // 16
+        max_suffix_blocks = (suffix[1] + steps + 15) // 16
+        self.MB = self.pb + max_suffix_blocks
+        self.N = self.pb + batch * max_suffix_blocks + 16
+        order = synth.permutation(self.rng["free_order"], self.N)
+        self.pool = pk.Pool(layers, self.N, H, D, "bf16", dev, initial_free_order=order)
+        self.mirror = mirror           # optional reference allocator driven in lockstep
+        if mirror is not None:
+            mirror.__init__(self.N, order)
+        self.record_layers = tuple(record_layers)
+        self.record_slots = tuple(record_slots)
+        self.scale = 1.0 / math.sqrt(D)
+
+        # the prefix entry: allocate and fill the shared blocks once per layer
+        ptab = np.zeros((1, self.pb), np.int32)
+        plen = np.zeros(1, np.int32)
+        slots = self.pool.batch_reserve(ptab, plen, np.array([prefix], np.int32))
+        self._mirror_reserve(ptab, np.zeros(1, np.int32), np.array([prefix], np.int32))
+        self.prefix_blocks = ptab[0].copy()
+        d_slots = torch.from_numpy(slots).to(dev)
+        self.prefix_bits = {}
+        for layer in range(layers):
+            k = synth.device_normal((prefix, H, D), self._seed("prefix_k", layer), dev, torch.bfloat16)
+            v = synth.device_normal((prefix, H, D), self._seed("prefix_v", layer), dev, torch.bfloat16)
+            self.pool.append(layer, k, v, d_slots)
+            if layer in self.record_layers:
+                self.prefix_bits[layer] = (_bits(k), _bits(v))
+
+        self.table = np.zeros((batch, self.MB), np.int32)
+        self.lens = np.zeros(batch, np.int32)
+        self.history = {(l, b): [] for l in self.record_layers for b in self.record_slots}
+        self.d_table = torch.empty((batch, self.MB), dtype=torch.int32, device=dev)
+        self.d_lens = torch.empty(batch, dtype=torch.int32, device=dev)
+        self.out = torch.empty((batch, HQ, D), dtype=torch.bfloat16, device=dev)
+        max_ctx = prefix + suffix[1] + steps + 1
+        self.ws = torch.empty(max(self.pool.workspace_bytes(batch, HQ, max_ctx), 1),
+                              dtype=torch.uint8, device=dev)
+        # admit the first batch (an append pass without a decode)
+        n_new = np.zeros(batch, np.int32)
+        for b in range(batch):
+            n_new[b] = self._admit(b)
+        self._write(-1, n_new, decode=False)
+
+    # -- helpers -------------------------------------------------------------
+    def _seed(self, what, *idx):
+        key = {"prefix_k": 1, "prefix_v": 2, "k": 3, "v": 4, "q": 5}[what]
+        h = self.seed * 1_000_003 + key
+        for i in idx:
+            h = h * 10_007 + (i + 2)
+        return h % (2 ** 62)
+
+    def _mirror_reserve(self, table, lens, n_new):
+        if self.mirror is None:
+            return
+        for b in range(len(lens)):
+            need = (int(lens[b]) + int(n_new[b]) + 15) // 16
+            have = (int(lens[b]) + 15) // 16
+            for j in range(have, need):
+                got = self.mirror.alloc()
+                assert got == table[b, j], (b, j, got, table[b, j])
+
+    def _admit(self, b):
+        self.table[b, :self.pb] = self.prefix_blocks
+        self.pool.retain_n(self.prefix_blocks)
+        if self.mirror is not None:
+            for blk in self.prefix_blocks:
+                self.mirror.retain(int(blk))
+        self.lens[b] = self.prefix_len
+        for l in self.record_layers:
+            if (l, b) in self.history:
+                self.history[(l, b)] = []
+        return int(self.rng["churn"].integers(self.suffix[0], self.suffix[1] + 1))
+
+    def _retire(self, b):
+        nb = (int(self.lens[b]) + 15) // 16
+        blocks = self.table[b, :nb].copy()
+        self.pool.release_n(blocks)
+        if self.mirror is not None:
+            for blk in blocks:
+                self.mirror.release(int(blk))
+        self.lens[b] = 0
+
+    def _write(self, step, n_new, decode=True):
+        torch = self.torch
+        lens_before = self.lens.copy()
+        slots = self.pool.batch_reserve(self.table, self.lens, n_new)
+        self._mirror_reserve(self.table, lens_before, n_new)
+        T = len(slots)
+        offs = np.concatenate([[0], np.cumsum(n_new)]).astype(np.int64)
+        d_slots = torch.from_numpy(slots).to(self.dev)
+        self.d_table.copy_(torch.from_numpy(self.table))
+        self.d_lens.copy_(torch.from_numpy(self.lens))
+        max_ctx = int(self.lens.max())
+        nb = (self.lens.astype(np.int64) + 15) // 16
+        used = self.table[np.arange(self.MB)[None, :] < nb[:, None]]
+        assert used.size == 0 or (used.min() >= 0 and used.max() < self.N)
+        assert max_ctx <= self.MB * 16
+        outs = {}
+        for layer in range(self.layers):
+            k = synth.device_normal((T, H, D), self._seed("k", step, layer), self.dev, torch.bfloat16)
+            v = synth.device_normal((T, H, D), self._seed("v", step, layer), self.dev, torch.bfloat16)
+            self.pool.append(layer, k, v, d_slots)
+            if layer in self.record_layers:
+                for b in self.record_slots:
+                    s, e = offs[b], offs[b + 1]
+                    if e > s:
+                        self.history[(layer, b)].append((_bits(k[s:e]), _bits(v[s:e])))
+            if decode:
+                q = synth.device_normal((self.batch, HQ, D), self._seed("q", step, layer), self.dev,
+                                        torch.bfloat16)
+                self.pool.decode(layer, q, self.d_table, self.d_lens, max_ctx, self.scale,
+                                 out=self.out, workspace=self.ws)
+                if layer in self.record_layers:
+                    outs[layer] = (_bits(q), _bits(self.out))
+        return outs
+
+    # -- one step --------------------------------------------------------------
+    def step(self, s):
+        """Retire and admit `churn` requests, then append + decode every layer.
+        Returns {layer: (q bits, out bits)} for the recorded layers."""
+        n_new = np.ones(self.batch, np.int32)
+        for b in self.rng["churn"].choice(self.batch, self.churn, replace=False):
+            self._retire(int(b))
+            n_new[b] = self._admit(int(b))
+        return self._write(s, n_new)
+
+    def logical_kv_bytes(self):
+        return int(self.lens.astype(np.int64).sum()) * H * D * 2 * 2
+
+    def unique_kv_bytes(self):
+        suffix_blocks = int(sum((int(n) + 15) // 16 - self.pb for n in self.lens))
+        return (self.pb + suffix_blocks) * 16 * H * D * 2 * 2
+
+    def request_bits(self, layer, b):
+        """Input bits of the tokens of the request in batch slot b (recorded
+        layers and slots only): prefix, then every chunk appended since its
+        admission."""
+        pk_, pv_ = self.prefix_bits[layer]
+        ks = [pk_] + [c[0] for c in self.history[(layer, b)]]
+        vs = [pv_] + [c[1] for c in self.history[(layer, b)]]
+        return np.concatenate(ks), np.concatenate(vs)
+
+
+def _bits(t):
+    import torch
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
