@@ -191,9 +191,9 @@ int kv_append(kv_pool* pool, int32_t layer, const void* k_new, const void* v_new
 
 /* ------------------------------------------------------------ attention -- */
 
-/* Workspace bytes paged_attention_decode needs for this batch (0 when one
- * partition covers max_ctx).  partition_tokens 0 means the default (512).
- * Returns -1 on invalid arguments. */
+/* Workspace bytes paged_attention_decode needs for this batch shape, -1 on
+ * invalid arguments.  fp32 caches: 0 when one partition covers max_ctx.
+ * bf16 and fp8 caches: always > 0 (split states plus B + 1 integers). */
 int64_t paged_attention_workspace_bytes(const kv_pool* pool, int32_t B, int32_t h_q,
                                         int32_t max_ctx, int32_t partition_tokens);
 
@@ -201,17 +201,27 @@ int64_t paged_attention_workspace_bytes(const kv_pool* pool, int32_t B, int32_t 
  * For request b and query head h (group g = h / (h_q / num_kv_heads)), with
  * n = context_lens[b] tokens cached (the token appended this step included):
  *   out[b][h] = sum_t softmax_t(scale * <q[b][h], K_t>) * V_t  over t < n,
- * K_t, V_t read through block_tables[b][t / block_size]; n == 0 gives zeros.
+ * K_t, V_t read through block_tables[b][t / block_size]; n == 0 gives zeros
+ * (the attention step of "Memoizing Context via KV Caching" and of the askaiml
+ * page, §1, over the paged layout of its §4).
  * q: device [B][h_q][head_dim] of q_dtype (KV_F32 with f32 pools, KV_BF16 with
  * bf16 and fp8 pools); out: device, same shape and dtype as q.
  * block_tables: device int32 [B][max_blocks_per_seq]; context_lens: device
- * int32 [B], each in [0, max_ctx]; max_ctx: host bound used to size the grid,
- * <= max_blocks_per_seq * block_size.  h_q must be a multiple of num_kv_heads.
- * The context is split into partitions of partition_tokens tokens (0 = 512; a
- * multiple of block_size); when max_ctx needs more than one, the partitions
- * keep (max, sum, weighted sum) states in `workspace` (device, at least
- * paged_attention_workspace_bytes) and a second kernel merges them.
- * Accumulation is fp32; the result is rounded to nearest even into out. */
+ * int32 [B]; max_ctx: host bound, <= max_blocks_per_seq * block_size.  Each
+ * context length is clamped to [0, max_ctx] before use, so a length beyond
+ * the bound is truncated, never read past the table or the workspace.
+ * h_q must be a multiple of num_kv_heads.
+ * Work split (partition_tokens, a multiple of block_size):
+ *  - fp32 caches: partitions of partition_tokens tokens (0 = 512) per request
+ *    and kv-head; with more than one, their (max, sum, weighted sum) states go
+ *    to the workspace and a second kernel merges them.
+ *  - bf16 and fp8 caches (B <= 8192): 0 splits the blocks of the whole batch
+ *    evenly over the kernel's waves; otherwise each piece covers at most
+ *    partition_tokens tokens.  Pieces that do not cover a whole request leave
+ *    states in the workspace, merged by a second kernel in piece order.
+ * Results depend on the context lengths of the batch (through the split) but
+ * not on which physical blocks hold the data.  Accumulation is fp32; the
+ * result is rounded to nearest even into out. */
 int paged_attention_decode(kv_pool* pool, int32_t layer, void* out, const void* q, int32_t q_dtype,
                            const int32_t* block_tables, int32_t max_blocks_per_seq,
                            const int32_t* context_lens, int32_t B, int32_t h_q, int32_t max_ctx,

@@ -9,26 +9,23 @@
 // through the request's page table.  Query head h reads KV head
 // h / (h_q / h_kv) ("KV Cache" glossary, inferensys.com, GQA entry).
 //
-// Work split: the context of each request is cut into partitions of `part`
-// tokens.  One workgroup handles one (partition, kv-head, request) and keeps,
-// per query head, the running max m (in log2 units), the sum l of
-// exp2(s - m) and the weighted sum acc of V.  With one partition the
-// workgroup writes the output directly; otherwise it stores (m, l, acc) and
-// `reduce_kernel` merges the partitions by rescaling to the common maximum.
+// Every (request, kv-head) keeps, per query head, the running max m of the
+// scores (log2 units), the sum l of 2^(s - m) and the weighted sum acc of V
+// (the online softmax).  Pieces of one request's context are merged by
+// rescaling to the common maximum.
 //
-// bf16 / fp8 caches use MFMA (v_mfma_f32_16x16x32_bf16).  A wave handles four
-// 16-token blocks per step; lane group q = lane/16 owns block q of the four.
-//   scores  S^T[token][head] = K[token][:] . Q^T[:][head]   (4 MFMA row groups
-//           j = 0..3, row 4q+i <-> block q, token 4j+i; D/32 k-steps)
-//   output  O^T[dim][head] += V^T[dim][token] . P^T[token][head]
-//           (the dim-major V tile gives each lane 8 consecutive tokens of one
-//           dimension in one 16-byte load; the k-slots of lane group q are
-//           block q's tokens 8h..8h+7, exactly the scores that lane holds)
-// so scores never cross lanes except for the per-head max and sum.  Padding
-// columns (heads beyond the group) carry zero queries and are not stored.
-// fp8 codes are widened to bf16 exactly (every E4M3 value is a bf16 value);
-// the K scale multiplies the scores and the V scale multiplies p.
+// bf16 / fp8 caches: decode_stream_kernel splits the blocks of the whole
+// batch evenly over its waves (details at the kernel) and uses MFMA
+// (v_mfma_f32_16x16x32_bf16) for q.K^T and p.V; stream_reduce_kernel merges
+// the pieces.  fp8 codes are widened to bf16 exactly (every E4M3 value is a
+// bf16 value); the K scale multiplies the scores and the V scale multiplies p.
+// Padding columns of the MFMA (query heads beyond the group) carry zero
+// queries and are never stored.
+//
+// fp32 caches: decode_f32_kernel (VALU) over fixed partitions per (request,
+// kv-head), reduce_kernel merges the partitions.
 
+#include <algorithm>
 #include <cstdint>
 
 #include "internal.h"
@@ -74,6 +71,12 @@ __device__ inline u32x4 mask_tail(u32x4 v, int valid) {
   return v;
 }
 
+// Context length of request b, clamped to [0, max_ctx] so that no kernel can
+// index past the table row or the workspace sized from max_ctx.
+__device__ inline int clamp_ctx(const int32_t* ctx_lens, int b, int max_ctx) {
+  return min(max(ctx_lens[b], 0), max_ctx);
+}
+
 __device__ inline float wave_max16(float x) {  // over lanes r, r+16, r+32, r+48
   x = fmaxf(x, __shfl_xor(x, 16));
   return fmaxf(x, __shfl_xor(x, 32));
@@ -91,107 +94,101 @@ template <>
 __device__ inline uint16_t to_out<uint16_t>(float x) { return uint16_t(f2bf_bits(x)); }
 
 // ------------------------------------------------------------------------
-// MFMA partition kernel for bf16 and fp8 caches (queries and output bf16).
-// grid (num_part, H * n_hgroups, B), 256 threads (4 waves).
+// Balanced decode for bf16 and fp8 caches (queries and output bf16).
+//
+// The work of the whole batch is a list of units (request b, kv-head group gh,
+// block j), ordered by b, then gh, then j; one kv-head group is a kv-head and
+// up to 16 of its query heads.  The list is cut into equal chunks of C units
+// and every wave streams whole chunks: a chunk is a run of segments, each a
+// range of blocks of one (b, gh).  A segment that covers all of its (b, gh)
+// is finished in place and written to `out`; the others (at most the first
+// and the last of a chunk) store their (m, l, acc) state in the workspace and
+// stream_reduce_kernel merges the pieces of each (b, gh) in chunk order.
+// C = ceil(units / workers) by default, so every wave gets the same number
+// of blocks whatever the context lengths; a caller-chosen chunk length forces
+// more pieces (each wave then takes every workers-th chunk).
+//
+// Inside a segment a wave takes NB = 2 blocks per step.  Lane group q (lanes
+// 16q..16q+15) owns tokens 8(q&1)..8(q&1)+7 of block q>>1 of the step:
+//   scores  S^T[token][head] = K[token][:] . Q^T[:][head]   (2 MFMA row groups
+//           j = 0, 1; row 4q+i is token 8(q&1) + 4j + i of block q>>1)
+//   output  O^T[dim][head] += V^T[dim][token] . P^T[token][head]
+// The dim-major V tile gives a lane its 8 tokens of one dimension in one
+// 16-byte load; those are exactly the 8 scores the lane holds, so p never
+// crosses lanes.  Only the per-head max and sum are reduced across the four
+// lane groups.
+constexpr int kStreamNB = 2;
+constexpr int kMaxStreamB = 8192;
+
+template <int D>
+struct WaveState {
+  float m = -INFINITY;  // running max, log2 units
+  float l = 0.0f;       // running sum of 2^(s - m) (this lane group's tokens)
+  f32x4 acc[D / 16];    // lane (r, q): head r, dims 16t + 4q + i
+};
+
 template <bool FP8, int D>
-__global__ void __launch_bounds__(256, 2)
-decode_mfma_kernel(const void* __restrict__ kc_, const void* __restrict__ vc_,
-                   const float* __restrict__ kscale, const float* __restrict__ vscale,
-                   const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
-                   const int32_t* __restrict__ tables, int max_blocks,
-                   const int32_t* __restrict__ ctx_lens, int H, int h_q, int G, int n_hgroups,
-                   float scale_log2, int part_blocks, int num_part, float* __restrict__ ws_ml,
-                   float* __restrict__ ws_acc) {
-  constexpr int KK = D / 32;  // k-steps of the score MFMA
-  constexpr int T8 = D / 16;  // 16-dim tiles of the output
-  constexpr int EB = FP8 ? 1 : 2;
-  constexpr int DP = D + 4;   // padded LDS row
-  __shared__ float s_m[4][16], s_l[4][16];
-  __shared__ __attribute__((aligned(16))) float s_acc[4][16][DP];
-
-  const int p = blockIdx.x;
-  const int g = blockIdx.y / n_hgroups;
-  const int hg = blockIdx.y - g * n_hgroups;
-  const int b = blockIdx.z;
-  const int head0 = g * G + hg * 16;
-  const int nh = min(16, G - hg * 16);
-  const int ctx = ctx_lens[b];
-  const int nblk = (ctx + kBS - 1) / kBS;
-  const int blk_begin = p * part_blocks;
-  if (blk_begin >= nblk) {
-    if (num_part == 1 && ctx == 0)
-      for (int i = threadIdx.x; i < nh * D; i += 256)
-        out[(int64_t(b) * h_q + head0 + i / D) * D + i % D] = 0;
-    return;
-  }
-  const int blk_end = min(nblk, blk_begin + part_blocks);
-
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int r = lane & 15;
-  const int grp = lane >> 4;
-
-  // query operand: column r = head head0 + r; k-slots of lane group grp
-  bf16x8 qv[KK];
+__device__ inline void load_q(bf16x8 (&qv)[D / 32], const uint16_t* q, int64_t row0, int r, int grp, int nh) {
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
+  for (int kk = 0; kk < D / 32; ++kk) {
     const int dim0 = FP8 ? (D / 4) * grp + 8 * kk : 32 * kk + 8 * grp;
     u32x4 v = {0, 0, 0, 0};
-    if (r < nh) v = ld16(q + (int64_t(b) * h_q + head0 + r) * D + dim0);
+    if (r < nh) v = ld16(q + (row0 + r) * D + dim0);
     qv[kk] = __builtin_bit_cast(bf16x8, v);
   }
+}
 
-  const uint8_t* kc = static_cast<const uint8_t*>(kc_);
-  const uint8_t* vc = static_cast<const uint8_t*>(vc_);
-  const int32_t* trow = tables + int64_t(b) * max_blocks;
+// Stream blocks [j0, j1) of one (request, kv-head) into the wave state.
+template <bool FP8, int D>
+__device__ inline void run_segment(WaveState<D>& st, const uint8_t* __restrict__ kc,
+                                   const uint8_t* __restrict__ vc, const float* __restrict__ kscale,
+                                   const float* __restrict__ vscale, const int32_t* __restrict__ trow,
+                                   int ctx, int H, int g, int j0, int j1, float scale_log2,
+                                   const bf16x8 (&qv)[D / 32], int r, int grp) {
+  constexpr int NB = kStreamNB;
+  constexpr int KK = D / 32;
+  constexpr int T8 = D / 16;
+  constexpr int EB = FP8 ? 1 : 2;
   const int64_t tile_bytes = int64_t(kBS) * D * EB;
-
-  float m_run = -INFINITY, l_run = 0.0f;
-  f32x4 acc[T8];
-#pragma unroll
-  for (int t = 0; t < T8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int nb = blk_end - blk_begin;
-  for (int c = w; c * 4 < nb; c += 4) {
-    const int cb = blk_begin + c * 4;
-    const int bK = cb + (r >> 2);  // block feeding this lane's K row
-    const int bV = cb + grp;       // block whose scores / V this lane owns
-    const bool vK = bK < blk_end;
-    const bool vV = bV < blk_end;
-    const int64_t pK = vK ? trow[bK] : 0;
-    const int64_t pV = vV ? trow[bV] : 0;
+  const int kb_rel = r >> 3;    // block (of the step) feeding this lane's K row
+  const int vb_rel = grp >> 1;  // block whose scores / V this lane owns
+  const int vtok = 8 * (grp & 1);
+  const int jlast = j1 - 1;
+  int32_t tK = trow[min(j0 + kb_rel, jlast)];
+  int32_t tV = trow[min(j0 + vb_rel, jlast)];
+  for (int cb = j0; cb < j1; cb += NB) {
+    const int bK = cb + kb_rel;
+    const int bV = cb + vb_rel;
+    const bool vK = bK < j1;
+    const bool vV = bV < j1;
+    const int64_t pK = tK;
+    const int64_t pV = tV;
+    // next step's table entries, in flight while this step computes
+    tK = trow[min(cb + NB + kb_rel, jlast)];
+    tV = trow[min(cb + NB + vb_rel, jlast)];
     const uint8_t* ktile = kc + (pK * H + g) * tile_bytes;
     const uint8_t* vtile = vc + (pV * H + g) * tile_bytes;
 
-    // ---- loads: K rows (token 4j + r%4 of block bK), V rows (dims of block bV)
-    bf16x8 kop[4][KK];
-    u32x4 vraw[T8][FP8 ? 1 : 2];
-    if constexpr (!FP8) {
+    // ---- loads: K rows for the score MFMAs, this lane's V slice
+    bf16x8 kop[NB][KK];
+    u32x4 vraw[T8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NB; ++j) {
+      const int ktok = 8 * ((r >> 2) & 1) + 4 * j + (r & 3);
+      if constexpr (!FP8) {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           u32x4 v = {0, 0, 0, 0};
-          if (vK) v = ld16(ktile + ((4 * j + (r & 3)) * D + 32 * kk + 8 * grp) * 2);
+          if (vK) v = ld16(ktile + (ktok * D + 32 * kk + 8 * grp) * 2);
           kop[j][kk] = __builtin_bit_cast(bf16x8, v);
         }
-#pragma unroll
-      for (int t = 0; t < T8; ++t)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          u32x4 v = {0, 0, 0, 0};
-          if (vV) v = ld16(vtile + ((16 * t + r) * kBS + 8 * h) * 2);
-          vraw[t][h] = v;
-        }
-    } else {
-      constexpr int NSEG = D / 64;  // 16-byte pieces of a lane's D/4 codes
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      } else {
+        constexpr int NSEG = D / 64;  // 16-byte pieces of a lane's D/4 codes
         u32x4 seg[NSEG];
 #pragma unroll
         for (int s = 0; s < NSEG; ++s) {
           seg[s] = u32x4{0, 0, 0, 0};
-          if (vK) seg[s] = ld16(ktile + (4 * j + (r & 3)) * D + (D / 4) * grp + 16 * s);
+          if (vK) seg[s] = ld16(ktile + ktok * D + (D / 4) * grp + 16 * s);
         }
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
@@ -201,25 +198,31 @@ decode_mfma_kernel(const void* __restrict__ kc_, const void* __restrict__ vc_,
           kop[j][kk] = __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], bq[0], bq[1]});
         }
       }
+    }
 #pragma unroll
-      for (int t = 0; t < T8; ++t) {
+    for (int t = 0; t < T8; ++t) {
+      if constexpr (!FP8) {
         u32x4 v = {0, 0, 0, 0};
-        if (vV) v = ld16(vtile + (16 * t + r) * kBS);
-        vraw[t][0] = v;
+        if (vV) v = ld16(vtile + ((16 * t + r) * kBS + vtok) * 2);
+        vraw[t] = v;
+      } else {
+        u32x2 v = {0, 0};
+        if (vV) v = *reinterpret_cast<const u32x2*>(vtile + (16 * t + r) * kBS + vtok);
+        vraw[t] = u32x4{v[0], v[1], 0, 0};
       }
     }
 
     // ---- scores
-    f32x4 S[4];
+    f32x4 S[NB];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NB; ++j) {
       S[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
         S[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[j][kk], qv[kk], S[j], 0, 0, 0);
     }
 
-    // ---- online softmax over this step's 64 tokens
+    // ---- online softmax over the step's 32 tokens
     float kfac = scale_log2;
     float vfac = 1.0f;
     if constexpr (FP8) {
@@ -228,11 +231,10 @@ decode_mfma_kernel(const void* __restrict__ kc_, const void* __restrict__ vc_,
         vfac = vscale[pV * H + g];
       }
     }
-    const int tok0 = bV * kBS;
-    const int valid = vV ? min(kBS, ctx - tok0) : 0;  // valid tokens of block bV
+    const int valid = vV ? min(kBS, ctx - bV * kBS) - vtok : 0;  // valid among the lane's 8
     float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float s = (4 * j + i < valid) ? S[j][i] * kfac : -INFINITY;
@@ -240,78 +242,231 @@ decode_mfma_kernel(const void* __restrict__ kc_, const void* __restrict__ vc_,
         mx = fmaxf(mx, s);
       }
     mx = wave_max16(mx);
-    const float m_new = fmaxf(m_run, mx);  // finite: the step holds a valid token
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    const float m_new = fmaxf(st.m, mx);  // finite: the step holds a valid token
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
     float psum = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float e = __builtin_amdgcn_exp2f(S[j][i] - m_new);
         S[j][i] = e;
         psum += e;
       }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+    st.l = st.l * alpha + psum;
+    st.m = m_new;
 #pragma unroll
-    for (int t = 0; t < T8; ++t) acc[t] *= alpha;
+    for (int t = 0; t < T8; ++t) st.acc[t] *= alpha;
 
-    // ---- weighted sum of V
+    // ---- weighted sum of V: k-slot e is token vtok + e of block bV
+    const f32x4 lo = S[0] * vfac, hi = S[1] * vfac;
+    const u32x4 pw = {pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3]), pack_bf16(hi[0], hi[1]),
+                      pack_bf16(hi[2], hi[3])};
+    const bf16x8 pop = __builtin_bit_cast(bf16x8, pw);
+    const int vh = min(max(valid, 0), 8);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const f32x4 lo = S[2 * h] * vfac, hi = S[2 * h + 1] * vfac;
-      const u32x4 pw = {pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3]), pack_bf16(hi[0], hi[1]),
-                        pack_bf16(hi[2], hi[3])};
-      const bf16x8 pop = __builtin_bit_cast(bf16x8, pw);
-      const int vh = min(max(valid - 8 * h, 0), 8);  // valid tokens among 8h..8h+7
-#pragma unroll
-      for (int t = 0; t < T8; ++t) {
-        u32x4 v;
-        if constexpr (FP8) {
-          const u32x2 a = fp8x4_to_bf16x4(vraw[t][0][2 * h]);
-          const u32x2 c2 = fp8x4_to_bf16x4(vraw[t][0][2 * h + 1]);
-          v = u32x4{a[0], a[1], c2[0], c2[1]};
-        } else {
-          v = vraw[t][h];
-        }
-        if (vh < 8) v = mask_tail(v, vh);  // stale or poisoned slots past the context
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), pop, acc[t], 0, 0, 0);
+    for (int t = 0; t < T8; ++t) {
+      u32x4 v;
+      if constexpr (FP8) {
+        const u32x2 a = fp8x4_to_bf16x4(vraw[t][0]);
+        const u32x2 c2 = fp8x4_to_bf16x4(vraw[t][1]);
+        v = u32x4{a[0], a[1], c2[0], c2[1]};
+      } else {
+        v = vraw[t];
       }
+      if (vh < 8) v = mask_tail(v, vh);  // stale or poisoned slots past the context
+      st.acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), pop, st.acc[t], 0, 0, 0);
     }
   }
+}
 
-  // ---- merge the four waves of the workgroup
-  l_run = wave_sum16(l_run);
-  if (grp == 0) {
-    s_m[w][r] = m_run;
-    s_l[w][r] = l_run;
-  }
+// Exclusive prefix sums of blocks per request into s_pref[0..B] (256 threads).
+__device__ inline void block_prefix_blocks(int32_t* s_pref, int32_t* s_tmp, const int32_t* ctx_lens, int B,
+                                           int max_ctx) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int32_t carry = 0;
+  for (int base = 0; base < B; base += 256) {
+    const int b = base + tid;
+    const int32_t v = b < B ? (clamp_ctx(ctx_lens, b, max_ctx) + kBS - 1) / kBS : 0;
+    int32_t x = v;
 #pragma unroll
-  for (int t = 0; t < T8; ++t) *reinterpret_cast<f32x4*>(&s_acc[w][r][16 * t + 4 * grp]) = acc[t];
+    for (int o = 1; o < 64; o <<= 1) {
+      const int32_t y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) s_tmp[w] = x;
+    __syncthreads();
+    int32_t before = carry;
+    for (int k = 0; k < w; ++k) before += s_tmp[k];
+    if (b < B) s_pref[b + 1] = before + x;
+    const int32_t total = s_tmp[0] + s_tmp[1] + s_tmp[2] + s_tmp[3];
+    __syncthreads();
+    carry += total;
+  }
+  if (tid == 0) s_pref[0] = 0;
   __syncthreads();
-  for (int i = threadIdx.x; i < nh * D; i += 256) {
-    const int hh = i / D, d = i - hh * D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) M = fmaxf(M, s_m[k][hh]);
-    float L = 0.0f, A = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float e = __builtin_amdgcn_exp2f(s_m[k][hh] - M);  // 0 for idle waves
-      L += e * s_l[k][hh];
-      A += e * s_acc[k][hh][d];
+}
+
+// grid = workers / 4 workgroups of 256 threads; chunk_fixed = 0 for balanced chunks.
+template <bool FP8, int D>
+__global__ void __launch_bounds__(256, 3)
+decode_stream_kernel(const void* __restrict__ kc_, const void* __restrict__ vc_,
+                     const float* __restrict__ kscale, const float* __restrict__ vscale,
+                     const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
+                     const int32_t* __restrict__ tables, int max_blocks,
+                     const int32_t* __restrict__ ctx_lens, int B, int max_ctx, int H, int h_q,
+                     int G, int n_hgroups, int HS, float scale_log2, int chunk_fixed,
+                     float* __restrict__ ws_ml, float* __restrict__ ws_acc,
+                     int32_t* __restrict__ ws_pref) {
+  constexpr int T8 = D / 16;
+  __shared__ int32_t s_pref[kMaxStreamB + 1];
+  __shared__ int32_t s_tmp[4];
+  block_prefix_blocks(s_pref, s_tmp, ctx_lens, B, max_ctx);
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i <= B; i += 256) ws_pref[i] = s_pref[i];
+
+  const int hge = H * n_hgroups;
+  const int64_t U = int64_t(hge) * s_pref[B];
+  const int W = gridDim.x * 4;
+  const int64_t C = chunk_fixed > 0 ? chunk_fixed : max<int64_t>(1, (U + W - 1) / W);
+  const int64_t NC = (U + C - 1) / C;
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15;
+  const int grp = lane >> 4;
+  const uint8_t* kc = static_cast<const uint8_t*>(kc_);
+  const uint8_t* vc = static_cast<const uint8_t*>(vc_);
+
+  for (int64_t c = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6); c < NC; c += W) {
+    int64_t u = c * C;
+    const int64_t u_end = min(U, u + C);
+    // request holding unit u: the last b with hge * pref[b] <= u
+    const int64_t x = u / hge;
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_pref[mid] <= x) lo = mid;
+      else hi = mid - 1;
     }
-    const int64_t row = int64_t(b) * h_q + head0 + hh;
-    if (num_part == 1) {
-      out[row * D + d] = uint16_t(f2bf_bits(A / L));
-    } else {
-      const int64_t st = row * num_part + p;
-      ws_acc[st * D + d] = A;
-      if (d == 0) {
-        ws_ml[st * 2] = M;
-        ws_ml[st * 2 + 1] = L;
+    int b = lo;
+    int nb = s_pref[b + 1] - s_pref[b];
+    int64_t rem = u - int64_t(hge) * s_pref[b];
+    int gh = int(rem / nb);
+    int j = int(rem - int64_t(gh) * nb);
+    int role = 0;
+    while (true) {
+      const int j1 = int(min<int64_t>(nb, j + (u_end - u)));
+      const int g = gh / n_hgroups;
+      const int hg = gh - g * n_hgroups;
+      const int head0 = g * G + hg * 16;
+      const int nh = min(16, G - hg * 16);
+      const int64_t row0 = int64_t(b) * h_q + head0;
+      bf16x8 qv[D / 32];
+      load_q<FP8, D>(qv, q, row0, r, grp, nh);
+      WaveState<D> st;
+#pragma unroll
+      for (int t = 0; t < T8; ++t) st.acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      run_segment<FP8, D>(st, kc, vc, kscale, vscale, tables + int64_t(b) * max_blocks,
+                          clamp_ctx(ctx_lens, b, max_ctx), H, g, j, j1, scale_log2, qv, r, grp);
+      const float l = wave_sum16(st.l);
+      if (j == 0 && j1 == nb) {  // the whole (b, gh): finish here
+        if (r < nh) {
+          const float inv = 1.0f / l;
+#pragma unroll
+          for (int t = 0; t < T8; ++t) {
+            const f32x4 o = st.acc[t] * inv;
+            const u32x2 pk = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
+            *reinterpret_cast<u32x2*>(out + (row0 + r) * D + 16 * t + 4 * grp) = pk;
+          }
+        }
+      } else if (r < nh) {
+        const int64_t slot = (c * 2 + role) * HS + r;
+        if (grp == 0) {
+          ws_ml[slot * 2] = st.m;
+          ws_ml[slot * 2 + 1] = l;
+        }
+#pragma unroll
+        for (int t = 0; t < T8; ++t) *reinterpret_cast<f32x4*>(ws_acc + slot * D + 16 * t + 4 * grp) = st.acc[t];
+      }
+      u += j1 - j;
+      if (u >= u_end) break;
+      role = 1;
+      j = 0;
+      if (++gh == hge) {
+        gh = 0;
+        do {
+          ++b;
+        } while (s_pref[b + 1] == s_pref[b]);
+        nb = s_pref[b + 1] - s_pref[b];
       }
     }
+  }
+}
+
+// Merge the pieces of one (request, query head) left by decode_stream_kernel.
+// grid (h_q, B), 256 threads = (256 / (D/4)) piece lanes x D/4 dimension quads.
+template <int D>
+__global__ void __launch_bounds__(256)
+stream_reduce_kernel(uint16_t* __restrict__ out, const float* __restrict__ ws_ml,
+                     const float* __restrict__ ws_acc, const int32_t* __restrict__ ws_pref,
+                     const int32_t* __restrict__ ctx_lens, int B, int max_ctx, int h_q, int G,
+                     int n_hgroups, int H, int HS, int workers, int chunk_fixed) {
+  constexpr int DQ = D / 4;
+  constexpr int PL = 256 / DQ;
+  __shared__ float s_red[256];
+  __shared__ __attribute__((aligned(16))) float s_a[PL][D];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int64_t row = int64_t(b) * h_q + h;
+  const int nb = (clamp_ctx(ctx_lens, b, max_ctx) + kBS - 1) / kBS;
+  if (nb == 0) {
+    if (tid < D) out[row * D + tid] = 0;
+    return;
+  }
+  const int hge = H * n_hgroups;
+  const int64_t U = int64_t(hge) * ws_pref[B];
+  const int64_t C = chunk_fixed > 0 ? chunk_fixed : max<int64_t>(1, (U + workers - 1) / workers);
+  const int g = h / G;
+  const int hg = (h - g * G) / 16;
+  const int hh = (h - g * G) % 16;
+  const int64_t start = int64_t(hge) * ws_pref[b] + int64_t(g * n_hgroups + hg) * nb;
+  const int64_t c0 = start / C;
+  const int64_t c1 = (start + nb - 1) / C;
+  if (c0 == c1) return;  // finished inside one chunk by the decode kernel
+  const int K = int(c1 - c0 + 1);
+  const int first_role = start > c0 * C ? 1 : 0;
+  auto slot = [&](int k) -> int64_t { return ((c0 + k) * 2 + (k == 0 ? first_role : 0)) * HS + hh; };
+
+  float M = -INFINITY;
+  for (int k = tid; k < K; k += 256) M = fmaxf(M, ws_ml[slot(k) * 2]);
+  s_red[tid] = M;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) s_red[tid] = fmaxf(s_red[tid], s_red[tid + o]);
+    __syncthreads();
+  }
+  M = s_red[0];
+  __syncthreads();
+
+  const int pl = tid / DQ, dq = tid - pl * DQ;
+  f32x4 A = {0.f, 0.f, 0.f, 0.f};
+  float Lp = 0.0f;
+  for (int k = pl; k < K; k += PL) {
+    const int64_t s = slot(k);
+    const float e = __builtin_amdgcn_exp2f(ws_ml[s * 2] - M);
+    if (dq == 0) Lp += e * ws_ml[s * 2 + 1];
+    A += e * *reinterpret_cast<const f32x4*>(ws_acc + s * D + 4 * dq);
+  }
+  *reinterpret_cast<f32x4*>(&s_a[pl][4 * dq]) = A;
+  s_red[tid] = Lp;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) s_red[tid] += s_red[tid + o];
+    __syncthreads();
+  }
+  const float L = s_red[0];
+  if (tid < D) {
+    float a = 0.0f;
+    for (int k = 0; k < PL; ++k) a += s_a[k][tid];
+    out[row * D + tid] = uint16_t(f2bf_bits(a / L));
   }
 }
 
@@ -324,9 +479,9 @@ __global__ void __launch_bounds__(256)
 decode_f32_kernel(const float* __restrict__ kc, const float* __restrict__ vc,
                   const float* __restrict__ q, float* __restrict__ out,
                   const int32_t* __restrict__ tables, int max_blocks,
-                  const int32_t* __restrict__ ctx_lens, int H, int h_q, int G, int n_hgroups,
-                  float scale_log2, int part_blocks, int num_part, float* __restrict__ ws_ml,
-                  float* __restrict__ ws_acc) {
+                  const int32_t* __restrict__ ctx_lens, int max_ctx, int H, int h_q, int G,
+                  int n_hgroups, float scale_log2, int part_blocks, int num_part,
+                  float* __restrict__ ws_ml, float* __restrict__ ws_acc) {
   constexpr int CH = 256;
   __shared__ float s_q[16][D];
   __shared__ float s_s[16][CH];
@@ -340,7 +495,7 @@ decode_f32_kernel(const float* __restrict__ kc, const float* __restrict__ vc,
   const int b = blockIdx.z;
   const int head0 = g * G + hg * 16;
   const int nh = min(16, G - hg * 16);
-  const int ctx = ctx_lens[b];
+  const int ctx = clamp_ctx(ctx_lens, b, max_ctx);
   const int tok_begin = p * part_blocks * kBS;
   if (tok_begin >= ctx) {
     if (num_part == 1 && ctx == 0)
@@ -429,34 +584,66 @@ decode_f32_kernel(const float* __restrict__ kc, const float* __restrict__ vc,
 }
 
 // ------------------------------------------------------------------------
-// Merge the partitions of one (request, query head): M = max m_p,
-// L = sum l_p 2^(m_p - M), out = sum acc_p 2^(m_p - M) / L.  grid (h_q, B),
-// D threads, thread d owns output dimension d.
+// Merge the partitions of one (request, kv-head group): for each query head,
+// a single pass over the partition states in index order keeps a running
+// maximum M and rescales the running sums when it grows, giving
+// out = sum_p acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M).
+// grid (H * n_hgroups, B), 256 threads; thread i owns (head i / D, dim i % D).
 template <typename OutT, int D>
-__global__ void __launch_bounds__(D)
+__global__ void __launch_bounds__(256)
 reduce_kernel(OutT* __restrict__ out, const float* __restrict__ ws_ml,
-              const float* __restrict__ ws_acc, const int32_t* __restrict__ ctx_lens, int h_q,
-              int part_tokens, int num_part) {
-  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-  const int ctx = ctx_lens[b];
+              const float* __restrict__ ws_acc, const int32_t* __restrict__ ctx_lens, int max_ctx,
+              int h_q, int G, int n_hgroups, int part_tokens, int num_part) {
+  const int g = blockIdx.x / n_hgroups;
+  const int hg = blockIdx.x - g * n_hgroups;
+  const int b = blockIdx.y;
+  const int head0 = g * G + hg * 16;
+  const int nh = min(16, G - hg * 16);
+  const int ctx = clamp_ctx(ctx_lens, b, max_ctx);
   const int np = (ctx + part_tokens - 1) / part_tokens;
-  const int64_t row = int64_t(b) * h_q + h;
-  if (np == 0) {
-    out[row * D + d] = to_out<OutT>(0.0f);
-    return;
+  for (int i = threadIdx.x; i < nh * D; i += 256) {
+    const int hh = i / D, d = i - hh * D;
+    const int64_t row = int64_t(b) * h_q + head0 + hh;
+    if (np == 0) {
+      out[row * D + d] = to_out<OutT>(0.0f);
+      continue;
+    }
+    const float* ml = ws_ml + row * num_part * 2;
+    const float* acc = ws_acc + row * num_part * D + d;
+    float M = ml[0], L = ml[1], A = acc[0];
+    int p = 1;
+    for (; p + 4 <= np; p += 4) {  // four partitions' loads in flight
+      float m4[4], l4[4], a4[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        m4[k] = ml[2 * (p + k)];
+        l4[k] = ml[2 * (p + k) + 1];
+        a4[k] = acc[int64_t(p + k) * D];
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float Mn = fmaxf(M, m4[k]);
+        const float eo = __builtin_amdgcn_exp2f(M - Mn), en = __builtin_amdgcn_exp2f(m4[k] - Mn);
+        L = L * eo + l4[k] * en;
+        A = A * eo + a4[k] * en;
+        M = Mn;
+      }
+    }
+    for (; p < np; ++p) {
+      const float mp = ml[2 * p];
+      const float Mn = fmaxf(M, mp);
+      const float eo = __builtin_amdgcn_exp2f(M - Mn), en = __builtin_amdgcn_exp2f(mp - Mn);
+      L = L * eo + ml[2 * p + 1] * en;
+      A = A * eo + acc[int64_t(p) * D] * en;
+      M = Mn;
+    }
+    out[row * D + d] = to_out<OutT>(A / L);
   }
-  const float* ml = ws_ml + row * num_part * 2;
-  const float* acc = ws_acc + row * num_part * D + d;
-  float M = -INFINITY;
-  for (int p = 0; p < np; ++p) M = fmaxf(M, ml[2 * p]);
-  float L = 0.0f, A = 0.0f;
-  for (int p = 0; p < np; ++p) {
-    const float e = __builtin_amdgcn_exp2f(ml[2 * p] - M);
-    L += e * ml[2 * p + 1];
-    A += e * acc[int64_t(p) * D];
-  }
-  out[row * D + d] = to_out<OutT>(A / L);
 }
+
+// Waves of the balanced decode kernel: 256 compute units x 4 SIMDs x 3
+// resident waves, so one launch fills MI355X once.
+constexpr int kStreamWorkers = 256 * 4 * 3;
 
 template <int D>
 int launch_decode_d(const DecodeArgs& a, hipStream_t s) {
@@ -464,48 +651,80 @@ int launch_decode_d(const DecodeArgs& a, hipStream_t s) {
   const int H = d.num_kv_heads;
   const int G = a.h_q / H;
   const int nhg = (G + 15) / 16;
-  const int part_blocks = a.part / kBS;
   const int64_t lo = int64_t(a.layer) * layer_elems(d);
   const float sl = a.scale * kLog2e;
-  const dim3 grid(a.num_part, H * nhg, a.B);
+  hipError_t e;
   if (d.cache_dtype == KV_F32) {
+    const dim3 grid(a.num_part, H * nhg, a.B);
     decode_f32_kernel<D><<<grid, 256, 0, s>>>(
         static_cast<const float*>(a.pool->k_cache) + lo, static_cast<const float*>(a.pool->v_cache) + lo,
-        static_cast<const float*>(a.q), static_cast<float*>(a.out), a.tables, a.max_blocks, a.ctx, H,
-        a.h_q, G, nhg, sl, part_blocks, a.num_part, a.ws_ml, a.ws_acc);
-  } else {
-    const int64_t lb = lo * elem_bytes(d.cache_dtype);
-    const uint8_t* kc = static_cast<const uint8_t*>(a.pool->k_cache) + lb;
-    const uint8_t* vc = static_cast<const uint8_t*>(a.pool->v_cache) + lb;
-    const int64_t so = int64_t(a.layer) * d.num_blocks * H;
-    if (d.cache_dtype == KV_BF16)
-      decode_mfma_kernel<false, D><<<grid, 256, 0, s>>>(
-          kc, vc, nullptr, nullptr, static_cast<const uint16_t*>(a.q), static_cast<uint16_t*>(a.out),
-          a.tables, a.max_blocks, a.ctx, H, a.h_q, G, nhg, sl, part_blocks, a.num_part, a.ws_ml,
-          a.ws_acc);
-    else
-      decode_mfma_kernel<true, D><<<grid, 256, 0, s>>>(
-          kc, vc, a.pool->k_scale + so, a.pool->v_scale + so, static_cast<const uint16_t*>(a.q),
-          static_cast<uint16_t*>(a.out), a.tables, a.max_blocks, a.ctx, H, a.h_q, G, nhg, sl,
-          part_blocks, a.num_part, a.ws_ml, a.ws_acc);
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(KV_E_HIP, "decode partition launch: %s", hipGetErrorString(e));
-  if (a.num_part > 1) {
-    const dim3 rg(a.h_q, a.B);
-    if (d.cache_dtype == KV_F32)
-      reduce_kernel<float, D><<<rg, D, 0, s>>>(static_cast<float*>(a.out), a.ws_ml, a.ws_acc, a.ctx,
-                                               a.h_q, a.part, a.num_part);
-    else
-      reduce_kernel<uint16_t, D><<<rg, D, 0, s>>>(static_cast<uint16_t*>(a.out), a.ws_ml, a.ws_acc,
-                                                  a.ctx, a.h_q, a.part, a.num_part);
+        static_cast<const float*>(a.q), static_cast<float*>(a.out), a.tables, a.max_blocks, a.ctx,
+        a.max_ctx, H, a.h_q, G, nhg, sl, a.part / kBS, a.num_part, a.ws_ml, a.ws_acc);
     e = hipGetLastError();
-    if (e != hipSuccess) return fail(KV_E_HIP, "decode reduce launch: %s", hipGetErrorString(e));
+    if (e != hipSuccess) return fail(KV_E_HIP, "decode partition launch: %s", hipGetErrorString(e));
+    if (a.num_part > 1) {
+      reduce_kernel<float, D><<<dim3(H * nhg, a.B), 256, 0, s>>>(
+          static_cast<float*>(a.out), a.ws_ml, a.ws_acc, a.ctx, a.max_ctx, a.h_q, G, nhg, a.part,
+          a.num_part);
+      e = hipGetLastError();
+      if (e != hipSuccess) return fail(KV_E_HIP, "decode reduce launch: %s", hipGetErrorString(e));
+    }
+    return ok();
   }
+  const int64_t lb = lo * elem_bytes(d.cache_dtype);
+  const uint8_t* kc = static_cast<const uint8_t*>(a.pool->k_cache) + lb;
+  const uint8_t* vc = static_cast<const uint8_t*>(a.pool->v_cache) + lb;
+  const int64_t so = int64_t(a.layer) * d.num_blocks * H;
+  const dim3 grid(a.workers / 4);
+  auto* q = static_cast<const uint16_t*>(a.q);
+  auto* out = static_cast<uint16_t*>(a.out);
+  if (d.cache_dtype == KV_BF16)
+    decode_stream_kernel<false, D><<<grid, 256, 0, s>>>(
+        kc, vc, nullptr, nullptr, q, out, a.tables, a.max_blocks, a.ctx, a.B, a.max_ctx, H, a.h_q, G, nhg,
+        a.hs, sl, a.chunk, a.ws_ml, a.ws_acc, a.ws_pref);
+  else
+    decode_stream_kernel<true, D><<<grid, 256, 0, s>>>(
+        kc, vc, a.pool->k_scale + so, a.pool->v_scale + so, q, out, a.tables, a.max_blocks, a.ctx, a.B,
+        a.max_ctx, H, a.h_q, G, nhg, a.hs, sl, a.chunk, a.ws_ml, a.ws_acc, a.ws_pref);
+  e = hipGetLastError();
+  if (e != hipSuccess) return fail(KV_E_HIP, "decode launch: %s", hipGetErrorString(e));
+  stream_reduce_kernel<D><<<dim3(a.h_q, a.B), 256, 0, s>>>(out, a.ws_ml, a.ws_acc, a.ws_pref, a.ctx, a.B,
+                                                           a.max_ctx, a.h_q, G, nhg, H, a.hs, a.workers,
+                                                           a.chunk);
+  e = hipGetLastError();
+  if (e != hipSuccess) return fail(KV_E_HIP, "decode reduce launch: %s", hipGetErrorString(e));
   return ok();
 }
 
 }  // namespace
+
+int64_t plan_decode(const kv_pool_desc& d, int32_t B, int32_t h_q, int32_t max_ctx,
+                    int32_t partition_tokens, DecodeArgs* a) {
+  const int H = d.num_kv_heads;
+  const int G = h_q / H;
+  const int nhg = (G + 15) / 16;
+  const int64_t hge = int64_t(H) * nhg;
+  if (hge > 65535) return fail(KV_E_UNSUPPORTED, "too many heads");
+  const int64_t fsz = int64_t(sizeof(float));
+  if (d.cache_dtype == KV_F32) {
+    const int32_t part = partition_tokens == 0 ? kDefaultPartition : partition_tokens;
+    const int32_t np = max_ctx == 0 ? 1 : int32_t((int64_t(max_ctx) + part - 1) / part);
+    if (hge * B * np > INT32_MAX) return fail(KV_E_UNSUPPORTED, "too many partitions");
+    a->part = part;
+    a->num_part = np;
+    a->slots = np > 1 ? int64_t(B) * h_q * np : 0;
+    return a->slots * (2 + d.head_dim) * fsz;
+  }
+  if (B > kMaxStreamB) return fail(KV_E_UNSUPPORTED, "batch %d above %d for bf16/fp8 caches", B, kMaxStreamB);
+  const int32_t chunk = partition_tokens / kBS;  // 0: balanced
+  const int64_t umax = int64_t(B) * hge * ((int64_t(max_ctx) + kBS - 1) / kBS);
+  const int64_t chunks = chunk > 0 ? std::max<int64_t>(1, (umax + chunk - 1) / chunk) : kStreamWorkers;
+  a->chunk = chunk;
+  a->workers = kStreamWorkers;
+  a->hs = std::min(16, G);
+  a->slots = 2 * chunks * a->hs;
+  return a->slots * (2 + d.head_dim) * fsz + (int64_t(B) + 1) * int64_t(sizeof(int32_t));
+}
 
 int launch_decode(const DecodeArgs& a, hipStream_t s) {
   if (a.pool->desc.head_dim == 128) return launch_decode_d<128>(a, s);

@@ -41,12 +41,6 @@ int fail(int status, const char* fmt, ...) {
 
 int ok() { return KV_OK; }
 
-int64_t workspace_bytes(int32_t B, int32_t h_q, int32_t head_dim, int32_t num_part) {
-  if (num_part <= 1) return 0;
-  const int64_t states = int64_t(B) * h_q * num_part;
-  return states * (2 + head_dim) * int64_t(sizeof(float));
-}
-
 }  // namespace pagedkv
 
 using namespace pagedkv;
@@ -288,10 +282,10 @@ int kv_append(kv_pool* p, int32_t layer, const void* k_new, const void* v_new,
 int64_t paged_attention_workspace_bytes(const kv_pool* p, int32_t B, int32_t h_q, int32_t max_ctx,
                                         int32_t part) {
   if (!p || B < 0 || h_q <= 0 || max_ctx < 0 || part < 0) return -1;
-  if (part == 0) part = kDefaultPartition;
-  if (part % p->desc.block_size != 0) return -1;
-  const int32_t np = max_ctx == 0 ? 1 : int32_t((int64_t(max_ctx) + part - 1) / part);
-  return workspace_bytes(B, h_q, p->desc.head_dim, np);
+  if (h_q % p->desc.num_kv_heads != 0) return -1;
+  DecodeArgs plan{};
+  const int64_t need = plan_decode(p->desc, B, h_q, max_ctx, part, &plan);
+  return need < 0 ? -1 : need;
 }
 
 int paged_attention_decode(kv_pool* p, int32_t layer, void* out, const void* q, int32_t q_dtype,
@@ -312,16 +306,13 @@ int paged_attention_decode(kv_pool* p, int32_t layer, void* out, const void* q, 
     return fail(KV_E_INVALID, "h_q %d is not a positive multiple of %d KV heads", h_q, d.num_kv_heads);
   if (max_blocks <= 0 || max_ctx < 0 || int64_t(max_ctx) > int64_t(max_blocks) * d.block_size)
     return fail(KV_E_INVALID, "max_ctx %d outside [0, %d blocks * %d]", max_ctx, max_blocks, d.block_size);
-  if (part == 0) part = kDefaultPartition;
   if (part < 0 || part % d.block_size != 0)
-    return fail(KV_E_INVALID, "partition_tokens %d is not a positive multiple of %d", part, d.block_size);
-  const int32_t np = max_ctx == 0 ? 1 : int32_t((int64_t(max_ctx) + part - 1) / part);
-  const int64_t need = workspace_bytes(B, h_q, d.head_dim, np);
+    return fail(KV_E_INVALID, "partition_tokens %d is not a multiple of %d", part, d.block_size);
+  DecodeArgs a{};
+  const int64_t need = plan_decode(d, B, h_q, max_ctx, part, &a);
+  if (need < 0) return int(need);  // plan_decode recorded the message
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(KV_E_WORKSPACE, "workspace of %lld bytes, %lld needed", (long long)ws_bytes, (long long)need);
-  if (int64_t(d.num_kv_heads) * ((h_q / d.num_kv_heads + 15) / 16) > 65535)
-    return fail(KV_E_UNSUPPORTED, "too many heads");
-  DecodeArgs a{};
   a.pool = p;
   a.layer = layer;
   a.out = out;
@@ -333,11 +324,10 @@ int paged_attention_decode(kv_pool* p, int32_t layer, void* out, const void* q, 
   a.h_q = h_q;
   a.max_ctx = max_ctx;
   a.scale = scale;
-  a.part = part;
-  a.num_part = np;
   if (need > 0) {
     a.ws_ml = static_cast<float*>(ws);
-    a.ws_acc = a.ws_ml + int64_t(B) * h_q * np * 2;
+    a.ws_acc = a.ws_ml + a.slots * 2;
+    a.ws_pref = reinterpret_cast<int32_t*>(a.ws_acc + a.slots * d.head_dim);
   }
   return launch_decode(a, static_cast<hipStream_t>(stream));
 }

@@ -124,29 +124,39 @@ def test_error_codes(lib):
 
 def test_device_entry_argument_checks(lib):
     """Checks that fail before any launch (no device is touched)."""
-    h, desc = _pool(lib, 8, H=2, D=64)
-    P = ctypes.c_void_p
-    # layer out of range, negative T
-    assert lib.kv_append(h, 1, FAKE, FAKE, FAKE, 4, None) == -1
-    assert lib.kv_append(h, 0, FAKE, FAKE, FAKE, -1, None) == -1
-    assert lib.kv_append(h, 0, None, FAKE, FAKE, 4, None) == -1
-    assert lib.kv_append(h, 0, FAKE, FAKE, FAKE, 0, None) == 0          # no-op
-    dec = lambda **kw: lib.paged_attention_decode(
-        h, kw.get("layer", 0), FAKE, FAKE, kw.get("qd", pk.KV_BF16), FAKE, kw.get("mb", 4), FAKE,
-        kw.get("B", 2), kw.get("hq", 4), kw.get("mc", 64), ctypes.c_float(0.1), kw.get("part", 0),
-        kw.get("ws", None), kw.get("wb", 0), None)
-    assert dec(qd=pk.KV_F32) == -2             # q dtype must match the pool
-    assert dec(hq=3) == -1                     # not a multiple of h_kv
-    assert dec(mc=65) == -1                    # beyond max_blocks * 16
-    assert dec(part=24) == -1                  # not a multiple of 16
-    assert dec(mc=64, part=16) == -6           # needs a workspace
-    need = lib.paged_attention_workspace_bytes(h, 2, 4, 64, 16)
-    assert need == 2 * 4 * 4 * (2 + 64) * 4
-    assert dec(mc=64, part=16, ws=FAKE, wb=need - 4) == -6
-    assert dec(B=0) == 0                       # empty batch is a no-op
-    assert lib.paged_attention_workspace_bytes(h, 2, 4, 64, 0) == 0
-    assert lib.paged_attention_workspace_bytes(h, 2, 4, 513, 0) == 2 * 4 * 2 * 66 * 4
-    pk.kv_pool_destroy(h)
+    for dtype in (pk.KV_BF16, pk.KV_F32):
+        h, desc = _pool(lib, 8, H=2, D=64, dtype=dtype)
+        assert lib.kv_append(h, 1, FAKE, FAKE, FAKE, 4, None) == -1          # layer
+        assert lib.kv_append(h, 0, FAKE, FAKE, FAKE, -1, None) == -1         # negative T
+        assert lib.kv_append(h, 0, None, FAKE, FAKE, 4, None) == -1
+        assert lib.kv_append(h, 0, FAKE, FAKE, FAKE, 0, None) == 0           # no-op
+        qd = pk.KV_F32 if dtype == pk.KV_F32 else pk.KV_BF16
+        dec = lambda **kw: lib.paged_attention_decode(
+            h, kw.get("layer", 0), FAKE, FAKE, kw.get("qd", qd), FAKE, kw.get("mb", 4), FAKE,
+            kw.get("B", 2), kw.get("hq", 4), kw.get("mc", 64), ctypes.c_float(0.1), kw.get("part", 0),
+            kw.get("ws", None), kw.get("wb", 0), None)
+        assert dec(qd=pk.KV_F32 + pk.KV_BF16 - qd) == -2   # q dtype must match the pool
+        assert dec(hq=3) == -1                               # not a multiple of h_kv
+        assert dec(mc=65) == -1                              # beyond max_blocks * 16
+        assert dec(part=24) == -1                            # not a multiple of 16
+        assert dec(mc=64, part=16) == -6                     # needs a workspace
+        need = lib.paged_attention_workspace_bytes(h, 2, 4, 64, 16)
+        assert dec(mc=64, part=16, ws=FAKE, wb=need - 4) == -6
+        assert dec(B=0) == 0                                 # empty batch is a no-op
+        assert lib.paged_attention_workspace_bytes(h, 2, 3, 64, 0) == -1
+        if dtype == pk.KV_F32:
+            # partitions of 16 tokens: 2 x 4 heads x 4 partitions of (2 + 64) floats
+            assert need == 2 * 4 * 4 * (2 + 64) * 4
+            assert lib.paged_attention_workspace_bytes(h, 2, 4, 64, 0) == 0
+            assert lib.paged_attention_workspace_bytes(h, 2, 4, 513, 0) == 2 * 4 * 2 * 66 * 4
+        else:
+            # pieces of 1 block: 2 requests x 2 kv-heads x 4 blocks = 16 pieces, two
+            # state slots each, 2 query heads per slot; plus B + 1 prefix integers
+            assert need == 2 * 16 * 2 * (2 + 64) * 4 + 3 * 4
+            w = (lib.paged_attention_workspace_bytes(h, 2, 4, 64, 0) - 3 * 4) // (2 * 2 * 66 * 4)
+            assert w >= 256                                  # one slot pair per wave
+            assert lib.paged_attention_workspace_bytes(h, 9000, 4, 64, 0) == -1   # batch cap
+        pk.kv_pool_destroy(h)
 
 
 @settings(max_examples=60, deadline=None)
