@@ -1,15 +1,21 @@
 """Benchmark: paged decode attention on one MI355X.
 
-A step is one pass of the whole hot path for one layer of a Llama-3-8B-shaped
-decode batch (h_q 32, h_kv 8, d_h 128, bf16, block size 16, 64 requests with
-contexts uniform on [512, 4096]): the host allocator reserves blocks and maps
-the slots of the new token of every request (once per model step, i.e. every
-`layers` steps), the table/length/slot arrays go to the device, kv_append writes
-the new token's K and V, and paged_attention_decode reads the whole cache.
-The pool holds `layers` layers (32, as in Llama-3-8B) and the steps walk them in
-order, so each step reads a layer whose 0.6 GB of K/V was last touched
-`layers - 1` steps earlier, well beyond the 256 MB last-level cache, as in a real
-decode step.
+Default workload (the one the metric is quoted on): one layer of a
+Llama-3-8B-shaped decode batch -- h_q 32, h_kv 8, d_h 128, bf16, block size 16,
+64 requests with contexts uniform on [512, 4096].  A step is one pass of the
+whole hot path for one layer: the host allocator reserves blocks and maps the
+slot of every request's new token (once per model step, i.e. every `layers`
+steps), the table/length/slot arrays go to the device, kv_append writes the new
+token's K and V, and paged_attention_decode reads the whole cache.  The pool
+holds `layers` layers (32, as in Llama-3-8B) and the steps walk them in order,
+so each step reads a layer whose K/V was last touched `layers - 1` steps
+earlier, far beyond the 256 MB last-level cache, as in a real decode step.
+
+Other workloads (--workload) are measured the same way: llama3_70b_long
+(h_q 64, 4 requests of 32k-128k tokens), fp8 (E4M3 cache, 128 requests of
+1k-8k tokens with x8 outliers) and prefix_churn (32 layers x 256 requests
+sharing a 2000-token prefix, 26 retired and admitted per step; a step there
+is one model step over all 32 layers).
 
 Prints one JSON line.  `value` is KV GB/s: K+V bytes of the valid tokens read
 by the decodes of the timed steps over their wall time.
@@ -30,6 +36,8 @@ sys.path.insert(0, ROOT)
 METRIC = "paged decode-attention KV GB/s (% of HBM peak) + µs/step, Llama-3-8B shape"
 HBM_PEAK_GBS = 8000.0
 EVENT_EVERY = 8
+DEFAULT_LAYERS = {"llama3_8b": 32, "llama3_70b_long": 8, "fp8": 16}
+DEFAULT_SEED = {"llama3_8b": 2, "llama3_70b_long": 3, "fp8": 5, "prefix_churn": 4}
 
 
 def parse():
@@ -37,14 +45,20 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1024)
     ap.add_argument("--warmup", type=int, default=64)
-    ap.add_argument("--layers", type=int, default=32)
-    ap.add_argument("--seed", type=int, default=2)
-    ap.add_argument("--partition", type=int, default=512)
+    ap.add_argument("--workload", default="llama3_8b",
+                    choices=["llama3_8b", "llama3_70b_long", "fp8", "prefix_churn"])
+    ap.add_argument("--layers", type=int, default=0, help="layers in the pool (0: workload default)")
+    ap.add_argument("--seed", type=int, default=-1, help="input seed (-1: workload default)")
+    ap.add_argument("--partition", type=int, default=0,
+                    help="tokens per piece (0: split the batch evenly over the decode waves)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain 1 GiB device copy before timing (scales HBM byte counters)")
-    return ap.parse_args()
+    a = ap.parse_args()
+    if a.seed < 0:
+        a.seed = DEFAULT_SEED[a.workload]
+    return a
 
 
 def log(msg):
@@ -88,6 +102,161 @@ class TimingEvent:
             pass
 
 
+def copy_calibration(torch, dev):
+    src = torch.empty(2 ** 30, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    log("copy calibration: 1 GiB read + 1 GiB written by one copy kernel")
+
+
+def decode_workload(args, torch, synth, pk, dev):
+    """Single-layer decode steps over a multi-layer pool (see the module doc)."""
+    name = args.workload
+    w = synth.WORKLOADS[name]
+    dtype = w["dtype"]
+    B, H, h_q, D = w["batch"], w["h_kv"], w["h_q"], w["head_dim"]
+    L = args.layers or DEFAULT_LAYERS[name]
+    elem = 1 if dtype == "fp8" else 2
+    outlier = w.get("outlier_p", 0.0)
+    total = args.warmup + args.steps
+    model_steps = (total + L - 1) // L
+    rng = synth.streams(args.seed)
+    if "contexts" in w:
+        ctx0 = np.array(w["contexts"], np.int32)
+    else:
+        ctx0 = synth.uniform_contexts(rng["contexts"], B, *w["ctx_range"]).astype(np.int32)
+    final = ctx0 + model_steps          # every request grows by one token per model step
+    MB = int((final.max() + 15) // 16)
+    N = int(((final + 15) // 16).sum())
+    order = synth.permutation(rng["free_order"], N)
+    log(f"{name}: pool {L} layers x {N} blocks ({N * H * 16 * D * elem * 2 * L / 1e9:.1f} GB), "
+        f"B={B}, ctx {ctx0.min()}..{ctx0.max()}, {model_steps} model steps")
+
+    pool = pk.Pool(L, N, H, D, dtype, dev, initial_free_order=order)
+    table = np.zeros((B, MB), np.int32)
+    lens = np.zeros(B, np.int32)
+    # prefill ctx0 - 1 tokens per request; each step appends one more
+    slots0 = pool.batch_reserve(table, lens, ctx0 - 1)
+    d_slots0 = torch.from_numpy(slots0).to(dev)
+    T0 = len(slots0)
+    in_dt = torch.bfloat16
+    for layer in range(L):
+        k = synth.device_normal((T0, H, D), 1000 + 2 * layer, dev, in_dt, outlier, 8.0)
+        v = synth.device_normal((T0, H, D), 1001 + 2 * layer, dev, in_dt, outlier, 8.0)
+        pool.append(layer, k, v, d_slots0)
+        del k, v
+    torch.cuda.synchronize()
+    log("prefill done")
+
+    # per (model step, layer) new-token K/V and queries, resident before timing
+    k_new = synth.device_normal((model_steps, L, B, H, D), 7, dev, in_dt, outlier, 8.0)
+    v_new = synth.device_normal((model_steps, L, B, H, D), 8, dev, in_dt, outlier, 8.0)
+    q_all = synth.device_normal((model_steps, L, B, h_q, D), 9, dev, in_dt)
+    out = torch.empty((B, h_q, D), dtype=in_dt, device=dev)
+    ws_bytes = pool.workspace_bytes(B, h_q, int(final.max()), args.partition)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    d_table = torch.empty((B, MB), dtype=torch.int32, device=dev)
+    d_lens = torch.empty(B, dtype=torch.int32, device=dev)
+    d_slots = torch.empty(B, dtype=torch.int32, device=dev)
+    scale = 1.0 / math.sqrt(D)
+    stream = torch.cuda.current_stream()
+    state = {"max_ctx": 0, "kv": 0}
+
+    def host_reserve():
+        slots = pool.batch_reserve(table, lens, np.ones(B, np.int32))
+        pinned = torch.empty(B * MB + 2 * B, dtype=torch.int32, pin_memory=True)
+        pn = pinned.numpy()
+        pn[:B * MB] = table.reshape(-1)
+        pn[B * MB:B * MB + B] = lens
+        pn[B * MB + B:] = slots
+        dev_buf = pinned.to(dev, non_blocking=True)
+        d_table.copy_(dev_buf[:B * MB].view(B, MB))
+        d_lens.copy_(dev_buf[B * MB:B * MB + B])
+        d_slots.copy_(dev_buf[B * MB + B:])
+        state["max_ctx"] = int(lens.max())
+        state["kv"] = int(lens.astype(np.int64).sum()) * H * D * elem * 2
+
+    def step(i, ev=None):
+        s, r = divmod(i, L)
+        if r == 0:
+            host_reserve()
+        pool.append(r, k_new[s, r], v_new[s, r], d_slots)
+        if ev is not None:
+            ev[0].record(stream)
+        pool.decode(r, q_all[s, r], d_table, d_lens, state["max_ctx"], scale, args.partition,
+                    out=out, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+        return state["kv"]
+
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    # events bracket the decode call of every EVENT_EVERY-th timed step (an
+    # event record still idles the GPU briefly, so not every step pays it)
+    events = [(TimingEvent(), TimingEvent()) if j % EVENT_EVERY == 0 else None
+              for j in range(args.steps)]
+    per_step_kv = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(args.steps):
+        per_step_kv.append(step(args.warmup + j, events[j]))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec_ms = np.array([e[0].elapsed_ms(e[1]) for e in events if e is not None])
+    dec_kv = np.array([per_step_kv[j] for j in range(args.steps) if events[j] is not None], float)
+
+    cpu = None
+    if name == "llama3_8b" and not args.no_cpu_baseline:
+        cpu = cpu_baseline(ctx0, T0, k_new, v_new, q_all, args, B, H, h_q, D, L, dev)
+    config = {
+        "workload": f"{name}_decode_layer",
+        "cache_dtype": dtype, "batch": B, "h_q": h_q, "h_kv": H, "head_dim": D, "block_size": 16,
+        "contexts": (list(w["contexts"]) if "contexts" in w else {"uniform": list(w["ctx_range"])}),
+        "layers_in_pool": L, "partition_tokens": args.partition,
+    }
+    return dict(wall=wall, kv_total=float(sum(per_step_kv)), dec_ms=dec_ms, dec_kv=dec_kv,
+                config=config, cpu=cpu, dtype="bf16" if dtype != "fp8" else "fp8-e4m3 K/V, bf16 q",
+                kernel="paged_attention_decode (decode_stream_kernel + stream_reduce_kernel)")
+
+
+def churn_workload(args, torch, synth, pk, dev):
+    """Model steps of the shared-prefix batch with churn: each step retires and
+    admits 26 requests, then appends and decodes every one of the 32 layers."""
+    import workloads
+    w = synth.WORKLOADS["prefix_churn"]
+    total = args.warmup + args.steps
+    run = workloads.PrefixChurn(dev, layers=w["num_layers"], batch=w["batch"],
+                                prefix=w["prefix_tokens"], suffix=w["suffix_range"], steps=total,
+                                churn=w["churn"], seed=args.seed, reuse_inputs=True)
+    log(f"prefix_churn: {run.N} blocks x {w['num_layers']} layers")
+    for s in range(args.warmup):
+        run.step(s)
+    torch.cuda.synchronize()
+    logical, unique = [], []
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        run.step(args.warmup + s)
+        logical.append(run.logical_kv_bytes() * w["num_layers"])
+        unique.append(run.unique_kv_bytes() * w["num_layers"])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    config = {"workload": "prefix_churn_model_step", "batch": w["batch"], "layers": w["num_layers"],
+              "prefix_tokens": w["prefix_tokens"], "suffix_range": list(w["suffix_range"]),
+              "churn_per_step": w["churn"], "partition_tokens": 0,
+              "unique_kv_bytes_per_step": int(np.mean(unique)),
+              "unique_kv_GBs": round(float(sum(unique)) / wall / 1e9, 1)}
+    return dict(wall=wall, kv_total=float(sum(logical)), dec_ms=None, dec_kv=None, config=config,
+                cpu=None, dtype="bf16", kernel=None)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -106,117 +275,36 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
 
-    w = synth.WORKLOADS["llama3_8b"]
-    B, H, h_q, D = w["batch"], w["h_kv"], w["h_q"], w["head_dim"]
-    L = args.layers
-    total = args.warmup + args.steps
-    model_steps = (total + L - 1) // L
-    rng = synth.streams(args.seed)
-    ctx0 = synth.uniform_contexts(rng["contexts"], B, *w["ctx_range"]).astype(np.int32)
-    final = ctx0 + model_steps          # every request grows by one token per model step
-    MB = int((final.max() + 15) // 16)
-    N = int(((final + 15) // 16).sum())
-    order = synth.permutation(rng["free_order"], N)
-    log(f"pool: {L} layers x {N} blocks ({N * H * 16 * D * 2 * 2 * L / 1e9:.1f} GB), "
-        f"B={B}, ctx {ctx0.min()}..{ctx0.max()}, {model_steps} model steps")
-
-    pool = pk.Pool(L, N, H, D, "bf16", dev, initial_free_order=order)
-    table = np.zeros((B, MB), np.int32)
-    lens = np.zeros(B, np.int32)
-    # prefill ctx0 - 1 tokens per request; each step appends one more
-    slots0 = pool.batch_reserve(table, lens, ctx0 - 1)
-    d_slots0 = torch.from_numpy(slots0).to(dev)
-    T0 = len(slots0)
-    for layer in range(L):
-        k = synth.device_normal((T0, H, D), 1000 + 2 * layer, dev, torch.bfloat16)
-        v = synth.device_normal((T0, H, D), 1001 + 2 * layer, dev, torch.bfloat16)
-        pool.append(layer, k, v, d_slots0)
-        del k, v
-    torch.cuda.synchronize()
-    log("prefill done")
-
-    # per (model step, layer) new-token K/V and queries, resident before timing
-    k_new = synth.device_normal((model_steps, L, B, H, D), 7, dev, torch.bfloat16)
-    v_new = synth.device_normal((model_steps, L, B, H, D), 8, dev, torch.bfloat16)
-    q_all = synth.device_normal((model_steps, L, B, h_q, D), 9, dev, torch.bfloat16)
-    out = torch.empty((B, h_q, D), dtype=torch.bfloat16, device=dev)
-    ws_bytes = pool.workspace_bytes(B, h_q, int(final.max()), args.partition)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    d_table = torch.empty((B, MB), dtype=torch.int32, device=dev)
-    d_lens = torch.empty(B, dtype=torch.int32, device=dev)
-    d_slots = torch.empty(B, dtype=torch.int32, device=dev)
-    scale = 1.0 / math.sqrt(D)
-    stream = torch.cuda.current_stream()
-    per_step_kv = []          # algorithmic K+V bytes of each step's decode
-    state = {"max_ctx": 0, "kv": 0}
-
-    def host_reserve():
-        slots = pool.batch_reserve(table, lens, np.ones(B, np.int32))
-        pinned = torch.empty(B * MB + 2 * B, dtype=torch.int32, pin_memory=True)
-        pn = pinned.numpy()
-        pn[:B * MB] = table.reshape(-1)
-        pn[B * MB:B * MB + B] = lens
-        pn[B * MB + B:] = slots
-        dev_buf = pinned.to(dev, non_blocking=True)
-        d_table.copy_(dev_buf[:B * MB].view(B, MB))
-        d_lens.copy_(dev_buf[B * MB:B * MB + B])
-        d_slots.copy_(dev_buf[B * MB + B:])
-        state["max_ctx"] = int(lens.max())
-        state["kv"] = int(lens.astype(np.int64).sum()) * H * D * 2 * 2
-
-    def step(i, ev=None):
-        s, r = divmod(i, L)
-        if r == 0:
-            host_reserve()
-        pool.append(r, k_new[s, r], v_new[s, r], d_slots)
-        if ev is not None:
-            ev[0].record(stream)
-        pool.decode(r, q_all[s, r], d_table, d_lens, state["max_ctx"], scale, args.partition,
-                    out=out, workspace=ws)
-        if ev is not None:
-            ev[1].record(stream)
-        return state["kv"]
-
-    if args.copy_calibration:
-        src = torch.empty(2 ** 30, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-        log("copy calibration: 1 GiB read + 1 GiB written by one copy kernel")
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    log(f"warmup {args.warmup} steps done")
-
-    # events bracket the decode call of every EVENT_EVERY-th timed step (an
-    # event record still idles the GPU briefly, so not every step pays it)
-    events = [(TimingEvent(), TimingEvent()) if j % EVENT_EVERY == 0 else None
-              for j in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for j in range(args.steps):
-        per_step_kv.append(step(args.warmup + j, events[j]))
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    wall = t1 - t0
-    dec_ms = np.array([e[0].elapsed_ms(e[1]) for e in events if e is not None])
-    kv_total = float(sum(per_step_kv))
-    value = kv_total / wall / 1e9
-    ms_per_step = wall / args.steps * 1e3
-    mean_kv = kv_total / args.steps
-    dec_mean_s = float(dec_ms.mean()) / 1e3
-    achieved = mean_kv / dec_mean_s / 1e9
-    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step, {value:.0f} GB/s; "
-        f"decode call {dec_mean_s * 1e6:.1f} us mean (p10 {np.percentile(dec_ms, 10) * 1e3:.1f}, "
-        f"p90 {np.percentile(dec_ms, 90) * 1e3:.1f}), {achieved:.0f} GB/s")
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(ctx0, T0, k_new, v_new, q_all, args, B, H, h_q, D, L, dev)
-
+    if args.workload == "prefix_churn":
+        r = churn_workload(args, torch, synth, pk, dev)
+    else:
+        r = decode_workload(args, torch, synth, pk, dev)
+    value = r["kv_total"] / r["wall"] / 1e9
+    ms_per_step = r["wall"] / args.steps * 1e3
+    mean_kv = r["kv_total"] / args.steps
+    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step, {value:.0f} GB/s")
+    roofline = None
+    if r["dec_ms"] is not None:
+        dec_mean_s = float(r["dec_ms"].mean()) / 1e3
+        achieved = float(r["dec_kv"].mean()) / dec_mean_s / 1e9
+        log(f"decode call {dec_mean_s * 1e6:.1f} us mean over {len(r['dec_ms'])} calls "
+            f"(p10 {np.percentile(r['dec_ms'], 10) * 1e3:.1f}, p90 {np.percentile(r['dec_ms'], 90) * 1e3:.1f}), "
+            f"{achieved:.0f} GB/s")
+        roofline = {
+            "bound": "hbm",
+            "kernel": r["kernel"],
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "us_per_call": round(dec_mean_s * 1e6, 2),
+            "calls_timed": int(len(r["dec_ms"])),
+        }
+    config = dict(r["config"])
+    config["us_per_step"] = round(ms_per_step * 1e3, 2)
+    config["hbm_fraction"] = round(value / HBM_PEAK_GBS, 4)
+    config["kv_bytes_per_step"] = int(mean_kv)
     res = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -228,29 +316,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": r["dtype"],
         "data": "synthetic",
-        "config": {
-            "workload": "llama3_8b_decode_layer",
-            "batch": B, "h_q": h_q, "h_kv": H, "head_dim": D, "block_size": 16,
-            "ctx_range": list(w["ctx_range"]), "mean_ctx": round(mean_kv / (H * D * 4) / B, 1),
-            "layers_in_pool": L, "partition_tokens": args.partition,
-            "us_per_step": round(ms_per_step * 1e3, 2),
-            "hbm_fraction": round(value / HBM_PEAK_GBS, 4),
-            "kv_bytes_per_step": int(mean_kv),
-        },
-        "roofline": {
-            "bound": "hbm",
-            "kernel": "paged_attention_decode (decode_stream_kernel + stream_reduce_kernel)",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "us_per_call": round(dec_mean_s * 1e6, 2),
-            "calls_timed": int(len(dec_ms)),
-        },
-        "cpu_baseline": cpu,
+        "config": config,
+        "roofline": roofline,
+        "cpu_baseline": r["cpu"],
     }
     print(json.dumps(res), flush=True)
 

@@ -31,17 +31,17 @@ __global__ void __launch_bounds__(128) append_copy_kernel(T* __restrict__ kc, T*
                                                           int H, int D) {
   const int t = blockIdx.x;
   const int g = blockIdx.y;
+  const int d = threadIdx.x;  // blockDim.x == D
+  // the inputs do not depend on the slot: load them alongside it
+  const T kx = k_new[(int64_t(t) * H + g) * D + d];
+  const T vx = v_new[(int64_t(t) * H + g) * D + d];
   const int32_t slot = slots[t];
   if (slot < 0) return;
   const int64_t blk = slot / kBS;
   const int off = slot % kBS;
   const int64_t tile = (blk * H + g) * int64_t(kBS) * D;
-  const T* ks = k_new + (int64_t(t) * H + g) * D;
-  const T* vs = v_new + (int64_t(t) * H + g) * D;
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    kc[tile + int64_t(off) * D + d] = ks[d];
-    vc[tile + int64_t(d) * kBS + off] = vs[d];
-  }
+  kc[tile + int64_t(off) * D + d] = kx;
+  vc[tile + int64_t(d) * kBS + off] = vx;
 }
 
 // ----------------------------------------------------------------- fp8 ----
@@ -84,28 +84,35 @@ __device__ inline uint32_t float_to_e4m3(float y) {
 
 __device__ inline float bf16_bits_to_float(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
-// Max over the workgroup (blockDim.x = 128 = two waves).
+// Max over the workgroup (one or two waves).
 __device__ inline float block_max(float v, float* red) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   const int w = threadIdx.x >> 6;
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[w] = v;
   __syncthreads();
-  return fmaxf(red[0], red[1]);
+  return blockDim.x > 64 ? fmaxf(red[0], red[1]) : red[0];
 }
 
 // One workgroup per (token t, kv-head g); only the first token of a run (the
 // consecutive tokens of this call landing in one block) does the work, for
-// the whole run.  Thread d owns dimension d of the tile.
-__global__ void __launch_bounds__(128) append_fp8_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
-                                                         float* __restrict__ ks, float* __restrict__ vs,
-                                                         const uint16_t* __restrict__ k_new,
-                                                         const uint16_t* __restrict__ v_new,
-                                                         const int32_t* __restrict__ slots, int T,
-                                                         int H, int D) {
+// the whole run.  The run's K tile ([16][D] codes) and V tile ([D][16]) are
+// staged in LDS with one 16-byte load per thread, re-encoded and written
+// there, and the changed bytes go back with 16-byte stores.
+// blockDim.x = D (64 or 128); thread d owns dimension d.
+template <int D>
+__global__ void __launch_bounds__(D) append_fp8_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
+                                                       float* __restrict__ ks, float* __restrict__ vs,
+                                                       const uint16_t* __restrict__ k_new,
+                                                       const uint16_t* __restrict__ v_new,
+                                                       const int32_t* __restrict__ slots, int T, int H) {
+  constexpr int TILE = kBS * D;        // bytes of one tile
+  constexpr int CHUNKS = TILE / 16;    // 16-byte pieces of a tile (= D)
+  __shared__ __attribute__((aligned(16))) uint8_t s_tile[2][TILE];  // [0] K, [1] V
   __shared__ float red[2];
   const int t = blockIdx.x;
   const int g = blockIdx.y;
+  const int d = threadIdx.x;
   const int32_t slot = slots[t];
   if (slot < 0) return;
   const int32_t blk = slot / kBS;
@@ -116,42 +123,58 @@ __global__ void __launch_bounds__(128) append_fp8_kernel(uint8_t* __restrict__ k
   int u = t;
   while (u + 1 < T && slots[u + 1] >= 0 && slots[u + 1] / kBS == blk) ++u;
   const int first_off = slot % kBS;
-  const int d = threadIdx.x;
-  const bool on = d < D;
-  const int64_t tile = (int64_t(blk) * H + g) * int64_t(kBS) * D;
+  const int64_t tile = (int64_t(blk) * H + g) * TILE;
   const int64_t sidx = int64_t(blk) * H + g;
 
-  for (int which = 0; which < 2; ++which) {  // 0: K (token-major), 1: V (dim-major)
+  // stage the tiles: V always (its 16-byte rows mix the run's slots with the
+  // others and are written back whole), K only when rows below the run may be
+  // re-encoded (the run's own K rows are rewritten whole)
+  if (first_off > 0)
+    *reinterpret_cast<uint4*>(&s_tile[0][16 * d]) = *reinterpret_cast<const uint4*>(kc + tile + 16 * d);
+  *reinterpret_cast<uint4*>(&s_tile[1][16 * d]) = *reinterpret_cast<const uint4*>(vc + tile + 16 * d);
+  const float sk0 = first_off == 0 ? 0.0f : ks[sidx];
+  const float sv0 = first_off == 0 ? 0.0f : vs[sidx];
+  __syncthreads();
+
+  // byte position of (token offset o, dimension d) in each staged tile
+  auto pos = [&](int which, int o) { return which == 0 ? o * D + d : d * kBS + o; };
+  bool reenc[2];
+  for (int which = 0; which < 2; ++which) {
     const uint16_t* src = which == 0 ? k_new : v_new;
-    uint8_t* cache = which == 0 ? kc : vc;
-    float* scales = which == 0 ? ks : vs;
-    auto at = [&](int off) -> int64_t {
-      return which == 0 ? tile + int64_t(off) * D + d : tile + int64_t(d) * kBS + off;
-    };
+    const float s0 = which == 0 ? sk0 : sv0;
     float amax = 0.0f;
-    if (on)
-      for (int r = t; r <= u; ++r)
-        amax = fmaxf(amax, fabsf(bf16_bits_to_float(src[(int64_t(r) * H + g) * D + d])));
+    for (int r = t; r <= u; ++r)
+      amax = fmaxf(amax, fabsf(bf16_bits_to_float(src[(int64_t(r) * H + g) * D + d])));
     amax = block_max(amax, red);
-    const float s0 = first_off == 0 ? 0.0f : scales[sidx];
     const float s1 = fmaxf(s0, amax / 448.0f);
-    if (on) {
-      if (s1 == 0.0f) {
-        for (int r = t; r <= u; ++r) cache[at(slots[r] % kBS)] = 0;
-      } else {
-        const float inv = 1.0f / s1;
-        if (s1 != s0 && first_off > 0)
-          for (int off = 0; off < first_off; ++off) {
-            const float x = e4m3_to_float(cache[at(off)]) * s0;
-            cache[at(off)] = uint8_t(float_to_e4m3(x * inv));
-          }
-        for (int r = t; r <= u; ++r) {
-          const float x = bf16_bits_to_float(src[(int64_t(r) * H + g) * D + d]);
-          cache[at(slots[r] % kBS)] = uint8_t(float_to_e4m3(x * inv));
+    reenc[which] = s1 != s0 && first_off > 0;
+    uint8_t* st = s_tile[which];
+    if (s1 == 0.0f) {
+      for (int r = t; r <= u; ++r) st[pos(which, slots[r] % kBS)] = 0;
+    } else {
+      const float inv = 1.0f / s1;
+      if (reenc[which])
+        for (int o = 0; o < first_off; ++o) {
+          const float x = e4m3_to_float(st[pos(which, o)]) * s0;
+          st[pos(which, o)] = uint8_t(float_to_e4m3(x * inv));
         }
+      for (int r = t; r <= u; ++r) {
+        const float x = bf16_bits_to_float(src[(int64_t(r) * H + g) * D + d]);
+        st[pos(which, slots[r] % kBS)] = uint8_t(float_to_e4m3(x * inv));
       }
     }
-    if (d == 0) scales[sidx] = s1;
+    if (d == 0) (which == 0 ? ks : vs)[sidx] = s1;
+  }
+  __syncthreads();
+
+  // write back: K rows of the run (and the re-encoded rows below it); V is
+  // dim-major, so every 16-byte row changes
+  const int last_off = slots[u] % kBS;
+  for (int c = d; c < CHUNKS; c += D) {
+    const int o = (16 * c) / D;  // token row of this K chunk
+    if ((o >= first_off && o <= last_off) || (o < first_off && reenc[0]))
+      *reinterpret_cast<uint4*>(kc + tile + 16 * c) = *reinterpret_cast<const uint4*>(&s_tile[0][16 * c]);
+    *reinterpret_cast<uint4*>(vc + tile + 16 * c) = *reinterpret_cast<const uint4*>(&s_tile[1][16 * c]);
   }
 }
 
@@ -162,22 +185,29 @@ int launch_append(const kv_pool* p, int32_t layer, const void* k_new, const void
   const kv_pool_desc& d = p->desc;
   const int64_t lo = int64_t(layer) * layer_elems(d);
   const dim3 grid(T, d.num_kv_heads);
+  const int D = d.head_dim;
   if (d.cache_dtype == KV_F32) {
-    append_copy_kernel<float><<<grid, 128, 0, stream>>>(
+    append_copy_kernel<float><<<grid, D, 0, stream>>>(
         static_cast<float*>(p->k_cache) + lo, static_cast<float*>(p->v_cache) + lo,
         static_cast<const float*>(k_new), static_cast<const float*>(v_new), slots, d.num_kv_heads,
         d.head_dim);
   } else if (d.cache_dtype == KV_BF16) {
-    append_copy_kernel<uint16_t><<<grid, 128, 0, stream>>>(
+    append_copy_kernel<uint16_t><<<grid, D, 0, stream>>>(
         static_cast<uint16_t*>(p->k_cache) + lo, static_cast<uint16_t*>(p->v_cache) + lo,
         static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), slots,
         d.num_kv_heads, d.head_dim);
   } else {
     const int64_t so = int64_t(layer) * d.num_blocks * d.num_kv_heads;
-    append_fp8_kernel<<<grid, 128, 0, stream>>>(
-        static_cast<uint8_t*>(p->k_cache) + lo, static_cast<uint8_t*>(p->v_cache) + lo,
-        p->k_scale + so, p->v_scale + so, static_cast<const uint16_t*>(k_new),
-        static_cast<const uint16_t*>(v_new), slots, T, d.num_kv_heads, d.head_dim);
+    auto* kc8 = static_cast<uint8_t*>(p->k_cache) + lo;
+    auto* vc8 = static_cast<uint8_t*>(p->v_cache) + lo;
+    auto* kn = static_cast<const uint16_t*>(k_new);
+    auto* vn = static_cast<const uint16_t*>(v_new);
+    if (D == 128)
+      append_fp8_kernel<128><<<grid, 128, 0, stream>>>(kc8, vc8, p->k_scale + so, p->v_scale + so, kn, vn,
+                                                       slots, T, d.num_kv_heads);
+    else
+      append_fp8_kernel<64><<<grid, 64, 0, stream>>>(kc8, vc8, p->k_scale + so, p->v_scale + so, kn, vn,
+                                                     slots, T, d.num_kv_heads);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KV_E_HIP, "kv_append launch: %s", hipGetErrorString(e));

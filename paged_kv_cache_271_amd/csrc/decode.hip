@@ -412,7 +412,7 @@ stream_reduce_kernel(uint16_t* __restrict__ out, const float* __restrict__ ws_ml
                      int n_hgroups, int H, int HS, int workers, int chunk_fixed) {
   constexpr int DQ = D / 4;
   constexpr int PL = 256 / DQ;
-  __shared__ float s_red[256];
+  __shared__ float s_m[PL], s_l[PL];
   __shared__ __attribute__((aligned(16))) float s_a[PL][D];
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int64_t row = int64_t(b) * h_q + h;
@@ -435,38 +435,58 @@ stream_reduce_kernel(uint16_t* __restrict__ out, const float* __restrict__ ws_ml
   const int first_role = start > c0 * C ? 1 : 0;
   auto slot = [&](int k) -> int64_t { return ((c0 + k) * 2 + (k == 0 ? first_role : 0)) * HS + hh; };
 
-  float M = -INFINITY;
-  for (int k = tid; k < K; k += 256) M = fmaxf(M, ws_ml[slot(k) * 2]);
-  s_red[tid] = M;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (tid < o) s_red[tid] = fmaxf(s_red[tid], s_red[tid + o]);
-    __syncthreads();
-  }
-  M = s_red[0];
-  __syncthreads();
-
+  // each thread merges the pieces k = pl, pl + PL, ... in one pass, keeping a
+  // running maximum and rescaling its sums when it grows; four pieces' loads
+  // are in flight at a time
   const int pl = tid / DQ, dq = tid - pl * DQ;
+  float M = -INFINITY, L = 0.0f;
   f32x4 A = {0.f, 0.f, 0.f, 0.f};
-  float Lp = 0.0f;
-  for (int k = pl; k < K; k += PL) {
+  int k = pl;
+  for (; k + 3 * PL < K; k += 4 * PL) {
+    float m4[4], l4[4];
+    f32x4 a4[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t s = slot(k + u * PL);
+      m4[u] = ws_ml[s * 2];
+      l4[u] = ws_ml[s * 2 + 1];
+      a4[u] = *reinterpret_cast<const f32x4*>(ws_acc + s * D + 4 * dq);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float Mn = fmaxf(M, m4[u]);
+      const float eo = __builtin_amdgcn_exp2f(M - Mn), en = __builtin_amdgcn_exp2f(m4[u] - Mn);
+      L = L * eo + l4[u] * en;
+      A = A * eo + a4[u] * en;
+      M = Mn;
+    }
+  }
+  for (; k < K; k += PL) {
     const int64_t s = slot(k);
-    const float e = __builtin_amdgcn_exp2f(ws_ml[s * 2] - M);
-    if (dq == 0) Lp += e * ws_ml[s * 2 + 1];
-    A += e * *reinterpret_cast<const f32x4*>(ws_acc + s * D + 4 * dq);
+    const float mp = ws_ml[s * 2];
+    const float Mn = fmaxf(M, mp);
+    const float eo = __builtin_amdgcn_exp2f(M - Mn), en = __builtin_amdgcn_exp2f(mp - Mn);
+    L = L * eo + ws_ml[s * 2 + 1] * en;
+    A = A * eo + *reinterpret_cast<const f32x4*>(ws_acc + s * D + 4 * dq) * en;
+    M = Mn;
+  }
+  // merge the PL lanes of each dimension quad (lanes without pieces hold M = -inf)
+  if (dq == 0) {  // M and L are the same for every dq of a lane
+    s_m[pl] = M;
+    s_l[pl] = L;
   }
   *reinterpret_cast<f32x4*>(&s_a[pl][4 * dq]) = A;
-  s_red[tid] = Lp;
   __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (tid < o) s_red[tid] += s_red[tid + o];
-    __syncthreads();
-  }
-  const float L = s_red[0];
   if (tid < D) {
-    float a = 0.0f;
-    for (int k = 0; k < PL; ++k) a += s_a[k][tid];
-    out[row * D + tid] = uint16_t(f2bf_bits(a / L));
+    float Mx = -INFINITY;
+    for (int p = 0; p < PL; ++p) Mx = fmaxf(Mx, s_m[p]);
+    float a = 0.0f, l = 0.0f;
+    for (int p = 0; p < PL; ++p) {
+      const float e = s_m[p] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s_m[p] - Mx);
+      a += e * s_a[p][tid];
+      l += e * s_l[p];
+    }
+    out[row * D + tid] = uint16_t(f2bf_bits(a / l));
   }
 }
 
