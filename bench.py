@@ -5,8 +5,10 @@ Llama-3-8B-shaped decode batch -- h_q 32, h_kv 8, d_h 128, bf16, block size 16,
 64 requests with contexts uniform on [512, 4096].  A step is one pass of the
 whole hot path for one layer: the host allocator reserves blocks and maps the
 slot of every request's new token (once per model step, i.e. every `layers`
-steps), the table/length/slot arrays go to the device, kv_append writes the new
-token's K and V, and paged_attention_decode reads the whole cache.  The pool
+steps), the table/length/slot arrays go to the device, and one
+paged_attention_decode_append call writes the new token's K and V and reads
+the whole cache (for bf16 one kernel does both; --two-calls times
+kv_append + paged_attention_decode instead).  The pool
 holds `layers` layers (32, as in Llama-3-8B) and the steps walk them in order,
 so each step reads a layer whose K/V was last touched `layers - 1` steps
 earlier, far beyond the 256 MB last-level cache, as in a real decode step.
@@ -51,6 +53,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=-1, help="input seed (-1: workload default)")
     ap.add_argument("--partition", type=int, default=0,
                     help="tokens per piece (0: split the batch evenly over the decode waves)")
+    ap.add_argument("--two-calls", action="store_true",
+                    help="run the step as kv_append + paged_attention_decode instead of the "
+                         "single paged_attention_decode_append call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -179,15 +184,24 @@ def decode_workload(args, torch, synth, pk, dev):
         state["max_ctx"] = int(lens.max())
         state["kv"] = int(lens.astype(np.int64).sum()) * H * D * elem * 2
 
+    # fp8 pools have no fused kernel (the append re-quantises whole tiles), so
+    # their step is always the two calls, with the decode alone between events
+    two_calls = args.two_calls or dtype == "fp8"
+
     def step(i, ev=None):
         s, r = divmod(i, L)
         if r == 0:
             host_reserve()
-        pool.append(r, k_new[s, r], v_new[s, r], d_slots)
+        if two_calls:
+            pool.append(r, k_new[s, r], v_new[s, r], d_slots)
         if ev is not None:
             ev[0].record(stream)
-        pool.decode(r, q_all[s, r], d_table, d_lens, state["max_ctx"], scale, args.partition,
-                    out=out, workspace=ws)
+        if two_calls:
+            pool.decode(r, q_all[s, r], d_table, d_lens, state["max_ctx"], scale, args.partition,
+                        out=out, workspace=ws)
+        else:
+            pool.decode_append(r, q_all[s, r], k_new[s, r], v_new[s, r], d_slots, d_table, d_lens,
+                               state["max_ctx"], scale, args.partition, out=out, workspace=ws)
         if ev is not None:
             ev[1].record(stream)
         return state["kv"]
@@ -221,10 +235,12 @@ def decode_workload(args, torch, synth, pk, dev):
         "cache_dtype": dtype, "batch": B, "h_q": h_q, "h_kv": H, "head_dim": D, "block_size": 16,
         "contexts": (list(w["contexts"]) if "contexts" in w else {"uniform": list(w["ctx_range"])}),
         "layers_in_pool": L, "partition_tokens": args.partition,
+        "step": "kv_append + paged_attention_decode" if two_calls else "paged_attention_decode_append",
     }
     return dict(wall=wall, kv_total=float(sum(per_step_kv)), dec_ms=dec_ms, dec_kv=dec_kv,
                 config=config, cpu=cpu, dtype="bf16" if dtype != "fp8" else "fp8-e4m3 K/V, bf16 q",
-                kernel="paged_attention_decode (decode_stream_kernel + stream_reduce_kernel)")
+                kernel=("paged_attention_decode" if two_calls else "paged_attention_decode_append")
+                + " call (decode_stream_kernel + stream_reduce_kernel)")
 
 
 def churn_workload(args, torch, synth, pk, dev):

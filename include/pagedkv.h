@@ -228,6 +228,33 @@ int paged_attention_decode(kv_pool* pool, int32_t layer, void* out, const void* 
                            float scale, int32_t partition_tokens, void* workspace,
                            int64_t workspace_bytes, void* hip_stream);
 
+/* Device: one whole decode step of layer `layer`: the append of one new token
+ * per request followed by the attention over the context that includes it
+ * (the order of §1 of the askaiml page: the new token's K and V join the
+ * cache, then attention reads all of it).  Same result as
+ *   kv_append(pool, layer, k_new, v_new, slot_mapping, B, stream);
+ *   paged_attention_decode(pool, layer, out, q, ...);
+ * with these added arguments:
+ * k_new, v_new: device [B][num_kv_heads][head_dim] (bf16 for bf16 and fp8
+ * pools, float for f32 pools), the new token of each request; slot_mapping:
+ * device int32 [B], the slot of position context_lens[b] - 1 of request b
+ * (as kv_slot_mapping / kv_batch_reserve give it), or -1 when request b
+ * appends nothing this step.  The slot's block must be mapped by request b
+ * alone (kv_slot_mapping refuses shared blocks).
+ * bf16 pools run it as one kernel: the attention takes the last position from
+ * k_new / v_new while the same launch stores them into the slot, so the step
+ * costs no separate append launch (outputs agree with the two calls to the
+ * bf16 rounding of the weights).  f32 and fp8 pools launch the append kernel
+ * and then the decode (fp8 re-quantises the tile, which the attention must
+ * read).  Errors and workspace are those of paged_attention_decode, plus
+ * KV_E_INVALID for a NULL k_new, v_new or slot_mapping. */
+int paged_attention_decode_append(kv_pool* pool, int32_t layer, void* out, const void* q,
+                                  int32_t q_dtype, const void* k_new, const void* v_new,
+                                  const int32_t* slot_mapping, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t B,
+                                  int32_t h_q, int32_t max_ctx, float scale, int32_t partition_tokens,
+                                  void* workspace, int64_t workspace_bytes, void* hip_stream);
+
 /* -------------------------------------------------------------- errors -- */
 
 /* Static name of a status code. */

@@ -52,6 +52,9 @@ SIGNATURES = {
     "paged_attention_workspace_bytes": (_I64, [_P, _I32, _I32, _I32, _I32]),
     "paged_attention_decode": (ctypes.c_int, [_P, _I32, _P, _P, _I32, _P, _I32, _P, _I32, _I32,
                                               _I32, ctypes.c_float, _I32, _P, _I64, _P]),
+    "paged_attention_decode_append": (ctypes.c_int, [_P, _I32, _P, _P, _I32, _P, _P, _P, _P, _I32,
+                                                     _P, _I32, _I32, _I32, ctypes.c_float, _I32, _P,
+                                                     _I64, _P]),
     "kv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kv_last_error": (ctypes.c_char_p, []),
 }
@@ -275,6 +278,37 @@ def paged_attention_decode(h, desc, layer, out, q, block_tables, context_lens, m
                                        wb, _stream_ptr(stream)))
 
 
+def paged_attention_decode_append(h, desc, layer, out, q, k_new, v_new, slot_mapping,
+                                  block_tables, context_lens, max_ctx, scale, partition_tokens=0,
+                                  workspace=None, stream=None):
+    """paged_attention_decode with the step's append: k_new, v_new [B, h_kv, d_h]
+    (the pool's input dtype), slot_mapping int32 [B] (-1: no new token)."""
+    import torch
+    if q.dim() != 3 or q.shape[2] != desc.head_dim:
+        raise ValueError("q must be [B, h_q, head_dim]")
+    B, h_q, _ = q.shape
+    want = torch.float32 if desc.cache_dtype == KV_F32 else torch.bfloat16
+    qp = _dev_ptr(q, "q", want)
+    op = _dev_ptr(out, "out", want, q.numel())
+    n = B * desc.num_kv_heads * desc.head_dim
+    kp = _dev_ptr(k_new, "k_new", want, n)
+    vp = _dev_ptr(v_new, "v_new", want, n)
+    sp = _dev_ptr(slot_mapping, "slot_mapping", torch.int32, B)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B, max_blocks]")
+    tp = _dev_ptr(block_tables, "block_tables", torch.int32)
+    cp = _dev_ptr(context_lens, "context_lens", torch.int32, B)
+    wp, wb = None, 0
+    if workspace is not None:
+        wp = _dev_ptr(workspace, "workspace")
+        wb = workspace.numel() * workspace.element_size()
+    qd = KV_F32 if want == torch.float32 else KV_BF16
+    _check(_lib.paged_attention_decode_append(h, int(layer), op, qp, qd, kp, vp, sp, tp,
+                                              block_tables.shape[1], cp, B, h_q, int(max_ctx),
+                                              float(scale), int(partition_tokens), wp, wb,
+                                              _stream_ptr(stream)))
+
+
 def kv_status_string(status):
     load_library()
     return _lib.kv_status_string(status).decode()
@@ -365,4 +399,19 @@ class Pool:
                 workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
         paged_attention_decode(self.handle, self.desc, layer, out, q, block_tables, context_lens,
                                max_ctx, scale, partition_tokens, workspace, stream)
+        return out
+
+    def decode_append(self, layer, q, k_new, v_new, slot_mapping, block_tables, context_lens,
+                      max_ctx, scale, partition_tokens=0, out=None, workspace=None, stream=None):
+        """Append one token per request (slot_mapping[b], -1 = none), then decode."""
+        import torch
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            nbytes = self.workspace_bytes(q.shape[0], q.shape[1], max_ctx, partition_tokens)
+            if nbytes > 0:
+                workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+        paged_attention_decode_append(self.handle, self.desc, layer, out, q, k_new, v_new,
+                                      slot_mapping, block_tables, context_lens, max_ctx, scale,
+                                      partition_tokens, workspace, stream)
         return out

@@ -280,6 +280,37 @@ __device__ inline void run_segment(WaveState<D>& st, const uint8_t* __restrict__
   }
 }
 
+// Fold one more token, whose K and V rows (head_dim values each, this kv
+// head) are given directly, into the wave state: the score of head r is the
+// dot product of the lane group's quarter of q and of the key, summed over
+// the four lane groups; then the usual online-softmax update.  The weight is
+// counted once in l (lane group 0) since l is summed over lane groups later.
+template <int D>
+__device__ inline void add_token(WaveState<D>& st, const uint16_t* __restrict__ kn,
+                                 const uint16_t* __restrict__ vn, const bf16x8 (&qv)[D / 32],
+                                 float scale_log2, int grp) {
+  float s = 0.0f;
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+    const bf16x8 kx = __builtin_bit_cast(bf16x8, ld16(kn + 32 * kk + 8 * grp));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s = fmaf(float(qv[kk][e]), float(kx[e]), s);
+  }
+  s = wave_sum16(s) * scale_log2;
+  const float m_new = fmaxf(st.m, s);
+  const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+  const float p = __builtin_amdgcn_exp2f(s - m_new);
+  st.l = st.l * alpha + (grp == 0 ? p : 0.0f);
+  st.m = m_new;
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(vn + 16 * t + 4 * grp);
+    const f32x4 v = {__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u),
+                     __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xFFFF0000u)};
+    st.acc[t] = st.acc[t] * alpha + v * p;
+  }
+}
+
 // Exclusive prefix sums of blocks per request into s_pref[0..B] (256 threads).
 __device__ inline void block_prefix_blocks(int32_t* s_pref, int32_t* s_tmp, const int32_t* ctx_lens, int B,
                                            int max_ctx) {
@@ -308,20 +339,65 @@ __device__ inline void block_prefix_blocks(int32_t* s_pref, int32_t* s_tmp, cons
 }
 
 // grid = workers / 4 workgroups of 256 threads; chunk_fixed = 0 for balanced chunks.
-template <bool FP8, int D>
+//
+// APPEND (bf16 caches): request b also appends one token, k_new[b] / v_new[b]
+// ([H][D] each), at new_slots[b] (-1: none), which is the slot of its
+// position ctx - 1.  The attention then reads positions < ctx - 1 from the
+// cache and takes the last one from k_new / v_new (add_token, in the segment
+// that ends the request), so no wave reads the slot being written; threads of
+// the same launch store the token into the cache while the block counts are
+// summed.
+template <bool FP8, int D, bool APPEND>
 __global__ void __launch_bounds__(256, 3)
-decode_stream_kernel(const void* __restrict__ kc_, const void* __restrict__ vc_,
+decode_stream_kernel(void* __restrict__ kc_, void* __restrict__ vc_,
                      const float* __restrict__ kscale, const float* __restrict__ vscale,
                      const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
                      const int32_t* __restrict__ tables, int max_blocks,
                      const int32_t* __restrict__ ctx_lens, int B, int max_ctx, int H, int h_q,
                      int G, int n_hgroups, int HS, float scale_log2, int chunk_fixed,
                      float* __restrict__ ws_ml, float* __restrict__ ws_acc,
-                     int32_t* __restrict__ ws_pref) {
+                     int32_t* __restrict__ ws_pref, const uint16_t* __restrict__ k_new,
+                     const uint16_t* __restrict__ v_new, const int32_t* __restrict__ new_slots) {
   constexpr int T8 = D / 16;
   __shared__ int32_t s_pref[kMaxStreamB + 1];
   __shared__ int32_t s_tmp[4];
+  // APPEND: 16-byte pieces (8 dims) of the new rows; thread i of the grid
+  // takes piece i (and i + grid, ... on big batches).  The first piece's
+  // loads are issued before the block counts are summed, its stores after.
+  const int pieces = APPEND ? B * H * (D / 8) : 0;
+  const int gthreads = gridDim.x * 256;
+  int piece = blockIdx.x * 256 + threadIdx.x;
+  u32x4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
+  int32_t pslot = -1;
+  if (APPEND && piece < pieces) {
+    pslot = new_slots[piece / (H * (D / 8))];
+    kx = ld16(k_new + int64_t(piece) * 8);
+    vx = ld16(v_new + int64_t(piece) * 8);
+  }
   block_prefix_blocks(s_pref, s_tmp, ctx_lens, B, max_ctx);
+  if constexpr (APPEND) {
+    uint16_t* kw = static_cast<uint16_t*>(kc_);
+    uint16_t* vw = static_cast<uint16_t*>(vc_);
+    while (piece < pieces) {
+      if (pslot >= 0) {
+        const int hd = piece % (H * (D / 8));  // kv head and dim piece within the request
+        const int g = hd / (D / 8);
+        const int d0 = 8 * (hd - g * (D / 8));
+        const int64_t tile = (int64_t(pslot / kBS) * H + g) * kBS * D;
+        const int off = pslot % kBS;
+        *reinterpret_cast<u32x4*>(kw + tile + off * D + d0) = kx;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          vw[tile + int64_t(d0 + e) * kBS + off] = uint16_t(vx[e / 2] >> (16 * (e & 1)));
+      }
+      piece += gthreads;
+      if (piece < pieces) {
+        pslot = new_slots[piece / (H * (D / 8))];
+        kx = ld16(k_new + int64_t(piece) * 8);
+        vx = ld16(v_new + int64_t(piece) * 8);
+      }
+    }
+  }
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i <= B; i += 256) ws_pref[i] = s_pref[i];
 
@@ -365,8 +441,24 @@ decode_stream_kernel(const void* __restrict__ kc_, const void* __restrict__ vc_,
       WaveState<D> st;
 #pragma unroll
       for (int t = 0; t < T8; ++t) st.acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      run_segment<FP8, D>(st, kc, vc, kscale, vscale, tables + int64_t(b) * max_blocks,
-                          clamp_ctx(ctx_lens, b, max_ctx), H, g, j, j1, scale_log2, qv, r, grp);
+      const int ctx = clamp_ctx(ctx_lens, b, max_ctx);
+      if constexpr (APPEND) {
+        // the cache holds positions < ctx - 1; a segment cut down to nothing
+        // is the request's last block holding only the new token
+        const bool app = new_slots[b] >= 0;  // ctx > 0 here: b has blocks
+        const int ctx_c = ctx - (app ? 1 : 0);
+        const int jc1 = min(j1, (ctx_c + kBS - 1) / kBS);
+        if (j < jc1)
+          run_segment<FP8, D>(st, kc, vc, kscale, vscale, tables + int64_t(b) * max_blocks, ctx_c, H, g,
+                              j, jc1, scale_log2, qv, r, grp);
+        if (app && j1 == nb) {
+          const int64_t nrow = (int64_t(b) * H + g) * D;
+          add_token<D>(st, k_new + nrow, v_new + nrow, qv, scale_log2, grp);
+        }
+      } else {
+        run_segment<FP8, D>(st, kc, vc, kscale, vscale, tables + int64_t(b) * max_blocks, ctx, H, g, j, j1,
+                            scale_log2, qv, r, grp);
+      }
       const float l = wave_sum16(st.l);
       if (j == 0 && j1 == nb) {  // the whole (b, gh): finish here
         if (r < nh) {
@@ -692,20 +784,26 @@ int launch_decode_d(const DecodeArgs& a, hipStream_t s) {
     return ok();
   }
   const int64_t lb = lo * elem_bytes(d.cache_dtype);
-  const uint8_t* kc = static_cast<const uint8_t*>(a.pool->k_cache) + lb;
-  const uint8_t* vc = static_cast<const uint8_t*>(a.pool->v_cache) + lb;
+  uint8_t* kc = static_cast<uint8_t*>(a.pool->k_cache) + lb;
+  uint8_t* vc = static_cast<uint8_t*>(a.pool->v_cache) + lb;
   const int64_t so = int64_t(a.layer) * d.num_blocks * H;
   const dim3 grid(a.workers / 4);
   auto* q = static_cast<const uint16_t*>(a.q);
   auto* out = static_cast<uint16_t*>(a.out);
-  if (d.cache_dtype == KV_BF16)
-    decode_stream_kernel<false, D><<<grid, 256, 0, s>>>(
+  if (d.cache_dtype == KV_BF16 && a.new_slots)
+    decode_stream_kernel<false, D, true><<<grid, 256, 0, s>>>(
         kc, vc, nullptr, nullptr, q, out, a.tables, a.max_blocks, a.ctx, a.B, a.max_ctx, H, a.h_q, G, nhg,
-        a.hs, sl, a.chunk, a.ws_ml, a.ws_acc, a.ws_pref);
+        a.hs, sl, a.chunk, a.ws_ml, a.ws_acc, a.ws_pref, static_cast<const uint16_t*>(a.k_new),
+        static_cast<const uint16_t*>(a.v_new), a.new_slots);
+  else if (d.cache_dtype == KV_BF16)
+    decode_stream_kernel<false, D, false><<<grid, 256, 0, s>>>(
+        kc, vc, nullptr, nullptr, q, out, a.tables, a.max_blocks, a.ctx, a.B, a.max_ctx, H, a.h_q, G, nhg,
+        a.hs, sl, a.chunk, a.ws_ml, a.ws_acc, a.ws_pref, nullptr, nullptr, nullptr);
   else
-    decode_stream_kernel<true, D><<<grid, 256, 0, s>>>(
+    decode_stream_kernel<true, D, false><<<grid, 256, 0, s>>>(
         kc, vc, a.pool->k_scale + so, a.pool->v_scale + so, q, out, a.tables, a.max_blocks, a.ctx, a.B,
-        a.max_ctx, H, a.h_q, G, nhg, a.hs, sl, a.chunk, a.ws_ml, a.ws_acc, a.ws_pref);
+        a.max_ctx, H, a.h_q, G, nhg, a.hs, sl, a.chunk, a.ws_ml, a.ws_acc, a.ws_pref, nullptr, nullptr,
+        nullptr);
   e = hipGetLastError();
   if (e != hipSuccess) return fail(KV_E_HIP, "decode launch: %s", hipGetErrorString(e));
   stream_reduce_kernel<D><<<dim3(a.h_q, a.B), 256, 0, s>>>(out, a.ws_ml, a.ws_acc, a.ws_pref, a.ctx, a.B,

@@ -63,6 +63,11 @@ struct DecodeArgs {
   float* ws_ml;      // [slots][2]  (max in log2 units, sum)
   float* ws_acc;     // [slots][head_dim]
   int32_t* ws_pref;  // bf16/fp8: [B + 1] blocks before each request
+  // bf16 decode with the step's append fused in (all null otherwise): one
+  // token per request, [B][H][D] each, written at new_slots[b] (-1: none)
+  const void* k_new;
+  const void* v_new;
+  const int32_t* new_slots;
 };
 
 // Fills the plan for a decode of this shape (pointers excluded) and returns

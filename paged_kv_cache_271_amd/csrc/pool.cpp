@@ -288,15 +288,17 @@ int64_t paged_attention_workspace_bytes(const kv_pool* p, int32_t B, int32_t h_q
   return need < 0 ? -1 : need;
 }
 
-int paged_attention_decode(kv_pool* p, int32_t layer, void* out, const void* q, int32_t q_dtype,
-                           const int32_t* tables, int32_t max_blocks, const int32_t* ctx, int32_t B,
-                           int32_t h_q, int32_t max_ctx, float scale, int32_t part, void* ws,
-                           int64_t ws_bytes, void* stream) {
+namespace {
+
+// Checks shared by the decode entry points; fills the plan on success.
+int prepare_decode(kv_pool* p, int32_t layer, void* out, const void* q, int32_t q_dtype,
+                   const int32_t* tables, int32_t max_blocks, const int32_t* ctx, int32_t B, int32_t h_q,
+                   int32_t max_ctx, float scale, int32_t part, void* ws, int64_t ws_bytes, DecodeArgs* a) {
   if (!p) return fail(KV_E_INVALID, "NULL pool");
   const kv_pool_desc& d = p->desc;
   if (layer < 0 || layer >= d.num_layers) return fail(KV_E_INVALID, "layer %d out of range", layer);
   if (B < 0) return fail(KV_E_INVALID, "negative batch");
-  if (B == 0) return ok();
+  if (B == 0) return KV_OK;  // nothing to do; the caller returns before launching
   if (B > 65535) return fail(KV_E_UNSUPPORTED, "batch %d above 65535", B);
   if (!out || !q || !tables || !ctx) return fail(KV_E_INVALID, "NULL device array");
   const int32_t want_q = d.cache_dtype == KV_F32 ? KV_F32 : KV_BF16;
@@ -308,28 +310,64 @@ int paged_attention_decode(kv_pool* p, int32_t layer, void* out, const void* q, 
     return fail(KV_E_INVALID, "max_ctx %d outside [0, %d blocks * %d]", max_ctx, max_blocks, d.block_size);
   if (part < 0 || part % d.block_size != 0)
     return fail(KV_E_INVALID, "partition_tokens %d is not a multiple of %d", part, d.block_size);
-  DecodeArgs a{};
-  const int64_t need = plan_decode(d, B, h_q, max_ctx, part, &a);
+  const int64_t need = plan_decode(d, B, h_q, max_ctx, part, a);
   if (need < 0) return int(need);  // plan_decode recorded the message
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(KV_E_WORKSPACE, "workspace of %lld bytes, %lld needed", (long long)ws_bytes, (long long)need);
-  a.pool = p;
-  a.layer = layer;
-  a.out = out;
-  a.q = q;
-  a.tables = tables;
-  a.max_blocks = max_blocks;
-  a.ctx = ctx;
-  a.B = B;
-  a.h_q = h_q;
-  a.max_ctx = max_ctx;
-  a.scale = scale;
+  a->pool = p;
+  a->layer = layer;
+  a->out = out;
+  a->q = q;
+  a->tables = tables;
+  a->max_blocks = max_blocks;
+  a->ctx = ctx;
+  a->B = B;
+  a->h_q = h_q;
+  a->max_ctx = max_ctx;
+  a->scale = scale;
   if (need > 0) {
-    a.ws_ml = static_cast<float*>(ws);
-    a.ws_acc = a.ws_ml + a.slots * 2;
-    a.ws_pref = reinterpret_cast<int32_t*>(a.ws_acc + a.slots * d.head_dim);
+    a->ws_ml = static_cast<float*>(ws);
+    a->ws_acc = a->ws_ml + a->slots * 2;
+    a->ws_pref = reinterpret_cast<int32_t*>(a->ws_acc + a->slots * d.head_dim);
   }
+  return KV_OK;
+}
+
+}  // namespace
+
+int paged_attention_decode(kv_pool* p, int32_t layer, void* out, const void* q, int32_t q_dtype,
+                           const int32_t* tables, int32_t max_blocks, const int32_t* ctx, int32_t B,
+                           int32_t h_q, int32_t max_ctx, float scale, int32_t part, void* ws,
+                           int64_t ws_bytes, void* stream) {
+  DecodeArgs a{};
+  const int st = prepare_decode(p, layer, out, q, q_dtype, tables, max_blocks, ctx, B, h_q, max_ctx, scale,
+                                part, ws, ws_bytes, &a);
+  if (st != KV_OK) return st;
+  if (B == 0) return ok();
   return launch_decode(a, static_cast<hipStream_t>(stream));
+}
+
+int paged_attention_decode_append(kv_pool* p, int32_t layer, void* out, const void* q, int32_t q_dtype,
+                                  const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                                  const int32_t* tables, int32_t max_blocks, const int32_t* ctx, int32_t B,
+                                  int32_t h_q, int32_t max_ctx, float scale, int32_t part, void* ws,
+                                  int64_t ws_bytes, void* stream) {
+  DecodeArgs a{};
+  const int st = prepare_decode(p, layer, out, q, q_dtype, tables, max_blocks, ctx, B, h_q, max_ctx, scale,
+                                part, ws, ws_bytes, &a);
+  if (st != KV_OK) return st;
+  if (B == 0) return ok();
+  if (!k_new || !v_new || !slot_mapping) return fail(KV_E_INVALID, "NULL device array");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p->desc.cache_dtype != KV_BF16) {  // the append kernel, then the decode
+    const int e = launch_append(p, layer, k_new, v_new, slot_mapping, B, s);
+    if (e != KV_OK) return e;
+    return launch_decode(a, s);
+  }
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.new_slots = slot_mapping;
+  return launch_decode(a, s);
 }
 
 const char* kv_status_string(int s) {

@@ -163,6 +163,68 @@ class Case:
         self.lens_list = [n + 1 for n in self.lens_list]
         self.sync_tables()
 
+    def decode_append_step(self, seed, appends=None, partition_tokens=0):
+        """One fused step (paged_attention_decode_append): request b appends one
+        token when appends[b] (every request by default), then all decode.
+        Checks that the call wrote exactly the new rows into the cache (bf16 /
+        f32: the bits at the slots, everything else unchanged; fp8: the host
+        mirror's quantiser) and returns the decode output as float64; the case
+        then holds the grown requests."""
+        B = len(self.lens_list)
+        appends = np.ones(B, bool) if appends is None else np.asarray(appends, bool)
+        old = [self.seq_raw(b) for b in range(B)]
+        new_slots = self.pool.batch_reserve(self.table, self.lens, appends.astype(np.int32))
+        slots = np.full(B, -1, np.int32)
+        slots[appends] = new_slots
+        check_slots(slots, self.N)
+        rng = synth.streams(seed)
+        shape = (B, self.H, self.D)
+        if self.dtype == "f32":
+            k = synth.normal_f32(rng["append"], shape)
+            v = synth.normal_f32(rng["append"], shape)
+        else:
+            k = synth.normal_bf16_bits(rng["append"], shape)
+            v = synth.normal_bf16_bits(rng["append"], shape)
+        lens_after = [n + int(a) for n, a in zip(self.lens_list, appends)]
+        assert list(self.lens) == lens_after
+        self.sync_tables()
+        max_ctx = max(lens_after)
+        check_indices(self.table, self.lens, self.N, max_ctx)
+        for b in np.nonzero(appends)[0]:  # the slot is the last position's
+            pos = lens_after[b] - 1
+            assert slots[b] == self.table[b, pos // 16] * 16 + pos % 16
+        dk, dv = to_dev_bits(k, self.dtype), to_dev_bits(v, self.dtype)
+        kc_before = self.pool.k_cache.clone()
+        vc_before = self.pool.v_cache.clone()
+        q = self.dq if self.device_inputs else to_dev_bits(self.q, self.dtype)
+        d_slots = torch.from_numpy(slots).to(DEV)
+        out = self.pool.decode_append(0, q, dk, dv, d_slots, self.d_table, self.d_lens, max_ctx,
+                                      1.0 / math.sqrt(self.D), partition_tokens)
+        torch.cuda.synchronize()
+        if self.dtype == "fp8":
+            if self.ref_pool is not None:
+                self.ref_pool.append(0, k[appends], v[appends], new_slots)
+                assert np.array_equal(self.pool.k_cache.cpu().numpy(), self.ref_pool.K)
+                assert np.array_equal(self.pool.v_cache.cpu().numpy(), self.ref_pool.V)
+                assert np.array_equal(self.pool.k_scale.cpu().numpy(), self.ref_pool.Ks)
+                assert np.array_equal(self.pool.v_scale.cpu().numpy(), self.ref_pool.Vs)
+        else:
+            idx = np.nonzero(appends)[0]
+            blk = torch.from_numpy((slots[idx] // 16).astype(np.int64)).to(DEV)
+            off = torch.from_numpy((slots[idx] % 16).astype(np.int64)).to(DEV)
+            ti = torch.from_numpy(idx.astype(np.int64)).to(DEV)
+            kc_before[0, blk, :, off, :] = dk[ti]
+            vc_before[0, blk, :, :, off] = dv[ti]
+            bits = (lambda t: t.view(torch.int32)) if self.dtype == "f32" else (lambda t: t.view(torch.int16))
+            assert torch.equal(bits(self.pool.k_cache), bits(kc_before)), "K cache differs from the append"
+            assert torch.equal(bits(self.pool.v_cache), bits(vc_before)), "V cache differs from the append"
+        del kc_before, vc_before
+        self._seqs = [(np.concatenate([kb, k[b:b + 1]]), np.concatenate([vb, v[b:b + 1]])) if appends[b]
+                      else (kb, vb) for b, (kb, vb) in enumerate(old)]
+        self.lens_list = lens_after
+        o = from_dev_bits(out)
+        return o.astype(np.float64) if self.dtype == "f32" else oracle.bf16_bits_to_f64(o)
+
     def seq_raw(self, b):
         """Input bits of request b's tokens, [n, H, D]."""
         if self._seqs is not None:

@@ -1,9 +1,10 @@
-"""GPU parity at the full workload sizes, in the launch configuration the
-benchmark times (512-token partitions): the Llama-3-8B-shaped batch (every
-output), the Llama-3-70B-shaped long contexts (sampled heads), the fp8 batch
-with outliers (sampled requests; codes and scales bit-exact), and 32 layers x
-64 steps of prefix sharing with churn (allocator state every step, sampled
-outputs at checkpoints)."""
+"""GPU parity at the full workload sizes, in the launch configurations the
+benchmark times (the balanced split, and 512-token partitions): the
+Llama-3-8B-shaped batch (every output, with the step's append fused in and as
+two calls), the Llama-3-70B-shaped long contexts (sampled heads), the fp8
+batch with outliers (sampled requests; codes and scales bit-exact), and 32
+layers x 64 steps of prefix sharing with churn (allocator state every step,
+sampled outputs at checkpoints)."""
 
 import math
 
@@ -23,24 +24,34 @@ def _blocks(lens):
     return int(sum(oracle.blocks_for(int(n), 16) for n in lens))
 
 
+def _check_all(got, ref, what):
+    worst = 0.0
+    atol, rtol = TOL["bf16"]
+    for b in range(len(ref)):
+        err = np.abs(got[b] - ref[b])
+        assert np.all(err <= atol + rtol * np.abs(ref[b])), f"{what}, request {b}: {err.max():.3e}"
+        worst = max(worst, float(err.max()))
+    log(f"  {what}: all {len(ref)} requests within tolerance; max|err| {worst:.3e}")
+
+
 def test_llama3_8b_batch_all_outputs(gpu_lib):
+    """Prefill ctx - 1 tokens, then the fused step appends the last one and
+    decodes (the benchmark's step); the plain decode of the same cache in
+    both splits."""
     w = synth.WORKLOADS["llama3_8b"]
     rng = synth.streams(2)
     lens = synth.uniform_contexts(rng["contexts"], w["batch"], *w["ctx_range"])
     N = _blocks(lens)
     log(f"llama3_8b: B={len(lens)} ctx {lens.min()}..{lens.max()} sum {lens.sum()} blocks {N}")
-    c = Case("bf16", w["h_kv"], w["head_dim"], w["h_q"], lens, num_blocks=N,
+    c = Case("bf16", w["h_kv"], w["head_dim"], w["h_q"], lens - 1, num_blocks=N,
              order=synth.permutation(rng["free_order"], N), seed=2, device_inputs=True,
              max_blocks=256)
-    got = c.decode(partition_tokens=w["partition_tokens"])
+    got = c.decode_append_step(seed=21, partition_tokens=0)
+    assert c.lens_list == [int(x) for x in lens]
     ref = c.oracle()
-    worst = 0.0
-    for b in range(len(lens)):
-        err = np.abs(got[b] - ref[b])
-        atol, rtol = TOL["bf16"]
-        assert np.all(err <= atol + rtol * np.abs(ref[b])), f"request {b}: {err.max():.3e}"
-        worst = max(worst, float(err.max()))
-    log(f"  all {len(lens)}x{w['h_q']} outputs within tolerance; max|err| {worst:.3e}")
+    _check_all(got, ref, "fused append + balanced decode")
+    for part in (0, w["partition_tokens"]):
+        _check_all(c.decode(partition_tokens=part), ref, f"decode, partition_tokens {part}")
 
 
 def test_llama3_70b_long_context_sampled(gpu_lib):
@@ -52,12 +63,13 @@ def test_llama3_70b_long_context_sampled(gpu_lib):
     c = Case("bf16", w["h_kv"], w["head_dim"], w["h_q"], lens, num_blocks=N,
              order=synth.permutation(rng["free_order"], N), seed=3, device_inputs=True,
              max_blocks=8192)
-    got = c.decode(partition_tokens=w["partition_tokens"])
+    got = {part: c.decode(partition_tokens=part) for part in (0, w["partition_tokens"])}
     G = w["h_q"] // w["h_kv"]
     for b in range(len(lens)):
         heads = sorted(int(g * G + rng["q"].integers(0, G)) for g in rng["q"].choice(8, 3, replace=False))
         ref = c.oracle(batch=[b], heads=heads)[b]
-        assert_close(got[b][heads], ref, "bf16", f"ctx {lens[b]} heads {heads}")
+        for part, o in got.items():
+            assert_close(o[b][heads], ref, "bf16", f"ctx {lens[b]} heads {heads} partition {part}")
 
 
 def test_fp8_batch_sampled(gpu_lib):
@@ -69,7 +81,7 @@ def test_fp8_batch_sampled(gpu_lib):
     c = Case("fp8", w["h_kv"], w["head_dim"], w["h_q"], lens, num_blocks=N,
              order=synth.permutation(rng["free_order"], N), seed=5, device_inputs=True,
              max_blocks=512, outlier_p=w["outlier_p"], mirror=False)
-    got = c.decode(partition_tokens=w["partition_tokens"])
+    got = {part: c.decode(partition_tokens=part) for part in (0, w["partition_tokens"])}
     kc = c.pool.k_cache[0]
     vc = c.pool.v_cache[0]
     ks = c.pool.k_scale[0].cpu().numpy()
@@ -89,13 +101,14 @@ def test_fp8_batch_sampled(gpu_lib):
         assert np.array_equal(ks[phys], ref_pool.Ks[0]) and np.array_equal(vs[phys], ref_pool.Vs[0])
         Kq, Vq = ref_pool.gather_f64(0, np.arange(nb), n)
         ref_q = oracle.attention_fp64(q[b], Kq, Vq, scale)
-        assert_close(got[b], ref_q, "fp8", f"request {b} (ctx {n}) vs the cached values")
-        assert_close(got[b], ref_q, "fp8q", f"request {b} (ctx {n}) vs the cached values")
+        for part, o in got.items():
+            assert_close(o[b], ref_q, "fp8", f"request {b} (ctx {n}) partition {part} vs the cached values")
+            assert_close(o[b], ref_q, "fp8q", f"request {b} (ctx {n}) partition {part} vs the cached values")
         # diagnostic only: what E4M3 storage itself costs against the inputs
         K0, V0 = oracle.bf16_bits_to_f64(kraw), oracle.bf16_bits_to_f64(vraw)
         ref0 = oracle.attention_fp64(q[b], K0, V0, scale)
         log(f"  request {b}: quantisation effect max|oracle(codes) - oracle(inputs)| "
-            f"{np.max(np.abs(ref_q - ref0)):.3e}, kernel vs inputs {np.max(np.abs(got[b] - ref0)):.3e}")
+            f"{np.max(np.abs(ref_q - ref0)):.3e}, kernel vs inputs {np.max(np.abs(got[0][b] - ref0)):.3e}")
 
 
 def test_prefix_sharing_with_churn(gpu_lib):

@@ -33,7 +33,7 @@ def _declared_functions():
 
 def test_exports_every_declared_function(lib):
     names = _declared_functions()
-    assert len(names) == 19
+    assert len(names) == 20
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(pk.SIGNATURES) == names
@@ -144,6 +144,18 @@ def test_device_entry_argument_checks(lib):
         assert dec(mc=64, part=16, ws=FAKE, wb=need - 4) == -6
         assert dec(B=0) == 0                                 # empty batch is a no-op
         assert lib.paged_attention_workspace_bytes(h, 2, 3, 64, 0) == -1
+        # the fused step runs the same checks, then wants its three new arrays
+        fused = lambda **kw: lib.paged_attention_decode_append(
+            h, kw.get("layer", 0), FAKE, FAKE, kw.get("qd", qd), kw.get("kn", FAKE), FAKE,
+            kw.get("sl", FAKE), FAKE, 4, FAKE, kw.get("B", 2), kw.get("hq", 4), kw.get("mc", 64),
+            ctypes.c_float(0.1), kw.get("part", 0), kw.get("ws", None), kw.get("wb", 0), None)
+        assert fused(layer=1) == -1
+        assert fused(qd=pk.KV_F32 + pk.KV_BF16 - qd) == -2
+        assert fused(hq=3) == -1 and fused(mc=65) == -1 and fused(part=24) == -1
+        assert fused(mc=64, part=16) == -6
+        assert fused(B=0) == 0
+        assert fused(kn=None, part=16, ws=FAKE, wb=need) == -1
+        assert fused(sl=None, part=16, ws=FAKE, wb=need) == -1
         if dtype == pk.KV_F32:
             # partitions of 16 tokens: 2 x 4 heads x 4 partitions of (2 + 64) floats
             assert need == 2 * 4 * 4 * (2 + 64) * 4
