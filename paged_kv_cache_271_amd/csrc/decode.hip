@@ -106,7 +106,9 @@ __device__ inline uint16_t to_out<uint16_t>(float x) { return uint16_t(f2bf_bits
 // stream_reduce_kernel merges the pieces of each (b, gh) in chunk order.
 // C = ceil(units / workers) by default, so every wave gets the same number
 // of blocks whatever the context lengths; a caller-chosen chunk length forces
-// more pieces (each wave then takes every workers-th chunk).
+// more pieces (each wave then takes every workers-th chunk).  When the number
+// of kv-head groups is a multiple of four, a workgroup's four waves move
+// together over four adjacent groups (see the kernel).
 //
 // Inside a segment a wave takes NB = 2 blocks per step.  Lane group q (lanes
 // 16q..16q+15) owns tokens 8(q&1)..8(q&1)+7 of block q>>1 of the step:
@@ -402,8 +404,16 @@ decode_stream_kernel(void* __restrict__ kc_, void* __restrict__ vc_,
     for (int i = threadIdx.x; i <= B; i += 256) ws_pref[i] = s_pref[i];
 
   const int hge = H * n_hgroups;
-  const int64_t U = int64_t(hge) * s_pref[B];
-  const int W = gridDim.x * 4;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, uniform
+  // When the (kv-head, head-group) pairs come in fours, a unit is (b, set of
+  // four pairs, j) and a workgroup streams whole chunks, its wave wv taking
+  // pair 4 * set + wv of every block: the four waves read adjacent tiles of
+  // the same blocks (16 KiB runs for bf16, d 128) and share table entries and
+  // fp8 scales in one L2.  Otherwise every wave streams chunks of its own.
+  const bool coop = (hge & 3) == 0;
+  const int hsets = coop ? hge >> 2 : hge;
+  const int64_t U = int64_t(hsets) * s_pref[B];
+  const int W = coop ? gridDim.x : gridDim.x * 4;
   const int64_t C = chunk_fixed > 0 ? chunk_fixed : max<int64_t>(1, (U + W - 1) / W);
   const int64_t NC = (U + C - 1) / C;
   const int lane = threadIdx.x & 63;
@@ -412,11 +422,11 @@ decode_stream_kernel(void* __restrict__ kc_, void* __restrict__ vc_,
   const uint8_t* kc = static_cast<const uint8_t*>(kc_);
   const uint8_t* vc = static_cast<const uint8_t*>(vc_);
 
-  for (int64_t c = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6); c < NC; c += W) {
+  for (int64_t c = coop ? int64_t(blockIdx.x) : int64_t(blockIdx.x) * 4 + wv; c < NC; c += W) {
     int64_t u = c * C;
     const int64_t u_end = min(U, u + C);
-    // request holding unit u: the last b with hge * pref[b] <= u
-    const int64_t x = u / hge;
+    // request holding unit u: the last b with hsets * pref[b] <= u
+    const int64_t x = u / hsets;
     int lo = 0, hi = B - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -425,12 +435,13 @@ decode_stream_kernel(void* __restrict__ kc_, void* __restrict__ vc_,
     }
     int b = lo;
     int nb = s_pref[b + 1] - s_pref[b];
-    int64_t rem = u - int64_t(hge) * s_pref[b];
-    int gh = int(rem / nb);
-    int j = int(rem - int64_t(gh) * nb);
+    int64_t rem = u - int64_t(hsets) * s_pref[b];
+    int gs = int(rem / nb);
+    int j = int(rem - int64_t(gs) * nb);
     int role = 0;
     while (true) {
       const int j1 = int(min<int64_t>(nb, j + (u_end - u)));
+      const int gh = coop ? 4 * gs + wv : gs;
       const int g = gh / n_hgroups;
       const int hg = gh - g * n_hgroups;
       const int head0 = g * G + hg * 16;
@@ -471,7 +482,7 @@ decode_stream_kernel(void* __restrict__ kc_, void* __restrict__ vc_,
           }
         }
       } else if (r < nh) {
-        const int64_t slot = (c * 2 + role) * HS + r;
+        const int64_t slot = (coop ? (c * 2 + role) * 4 + wv : c * 2 + role) * HS + r;
         if (grp == 0) {
           ws_ml[slot * 2] = st.m;
           ws_ml[slot * 2 + 1] = l;
@@ -483,8 +494,8 @@ decode_stream_kernel(void* __restrict__ kc_, void* __restrict__ vc_,
       if (u >= u_end) break;
       role = 1;
       j = 0;
-      if (++gh == hge) {
-        gh = 0;
+      if (++gs == hsets) {
+        gs = 0;
         do {
           ++b;
         } while (s_pref[b + 1] == s_pref[b]);
@@ -513,19 +524,30 @@ stream_reduce_kernel(uint16_t* __restrict__ out, const float* __restrict__ ws_ml
     if (tid < D) out[row * D + tid] = 0;
     return;
   }
+  // the decode kernel's split: units (b, set, j), sets of four pairs when
+  // they divide evenly (one chunk stream per workgroup), else one pair
   const int hge = H * n_hgroups;
-  const int64_t U = int64_t(hge) * ws_pref[B];
-  const int64_t C = chunk_fixed > 0 ? chunk_fixed : max<int64_t>(1, (U + workers - 1) / workers);
+  const bool coop = (hge & 3) == 0;
+  const int hsets = coop ? hge >> 2 : hge;
+  const int streams = coop ? workers / 4 : workers;
+  const int64_t U = int64_t(hsets) * ws_pref[B];
+  const int64_t C = chunk_fixed > 0 ? chunk_fixed : max<int64_t>(1, (U + streams - 1) / streams);
   const int g = h / G;
   const int hg = (h - g * G) / 16;
   const int hh = (h - g * G) % 16;
-  const int64_t start = int64_t(hge) * ws_pref[b] + int64_t(g * n_hgroups + hg) * nb;
+  const int gh = g * n_hgroups + hg;
+  const int gs = coop ? gh >> 2 : gh;
+  const int wv = coop ? gh & 3 : 0;
+  const int64_t start = int64_t(hsets) * ws_pref[b] + int64_t(gs) * nb;
   const int64_t c0 = start / C;
   const int64_t c1 = (start + nb - 1) / C;
   if (c0 == c1) return;  // finished inside one chunk by the decode kernel
   const int K = int(c1 - c0 + 1);
   const int first_role = start > c0 * C ? 1 : 0;
-  auto slot = [&](int k) -> int64_t { return ((c0 + k) * 2 + (k == 0 ? first_role : 0)) * HS + hh; };
+  auto slot = [&](int k) -> int64_t {
+    const int64_t cr = (c0 + k) * 2 + (k == 0 ? first_role : 0);
+    return (coop ? cr * 4 + wv : cr) * HS + hh;
+  };
 
   // each thread merges the pieces k = pl, pl + PL, ... in one pass, keeping a
   // running maximum and rescaling its sums when it grows; four pieces' loads
@@ -836,7 +858,13 @@ int64_t plan_decode(const kv_pool_desc& d, int32_t B, int32_t h_q, int32_t max_c
   if (B > kMaxStreamB) return fail(KV_E_UNSUPPORTED, "batch %d above %d for bf16/fp8 caches", B, kMaxStreamB);
   const int32_t chunk = partition_tokens / kBS;  // 0: balanced
   const int64_t umax = int64_t(B) * hge * ((int64_t(max_ctx) + kBS - 1) / kBS);
-  const int64_t chunks = chunk > 0 ? std::max<int64_t>(1, (umax + chunk - 1) / chunk) : kStreamWorkers;
+  // wave states per role: one per wave chunk (sets of four pairs: four per
+  // workgroup chunk, kStreamWorkers / 4 of them when balanced)
+  const bool coop = hge % 4 == 0;
+  int64_t chunks = kStreamWorkers;
+  if (chunk > 0)
+    chunks = coop ? 4 * std::max<int64_t>(1, (umax / 4 + chunk - 1) / chunk)
+                  : std::max<int64_t>(1, (umax + chunk - 1) / chunk);
   a->chunk = chunk;
   a->workers = kStreamWorkers;
   a->hs = std::min(16, G);
