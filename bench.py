@@ -41,6 +41,25 @@ EVENT_EVERY = 8
 DEFAULT_LAYERS = {"llama3_8b": 32, "llama3_70b_long": 8, "fp8": 16}
 DEFAULT_SEED = {"llama3_8b": 2, "llama3_70b_long": 3, "fp8": 5, "prefix_churn": 4}
 
+# HBM bytes (read + written) per launch of decode_stream_kernel in the default
+# step of each workload, from the rocprofv3 FETCH_SIZE and WRITE_SIZE runs in
+# profiles/decode_stream_workloads_hbm_counters.md, scaled by the plain-copy
+# calibration there (fetch x2, write x1).  They hold for the kernel source they
+# were taken on, identified by its SHA-256; any other source reports null.
+TRAFFIC_SOURCE = "paged_kv_cache_271_amd/csrc/decode.hip"
+TRAFFIC_SHA256 = "b8985b2b7f4c54ef0970d0cafaff33f97a6f8920f617a39da44a74f488e28931"
+TRAFFIC_BYTES = {"llama3_8b": 594_014_515, "fp8": 1_235_903_898, "llama3_70b_long": 1_358_273_741}
+
+
+def measured_traffic(workload, two_calls):
+    import hashlib
+    if two_calls and workload != "fp8":
+        return None  # counters were taken on the fused kernel
+    with open(os.path.join(ROOT, TRAFFIC_SOURCE), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != TRAFFIC_SHA256:
+            return None
+    return TRAFFIC_BYTES.get(workload)
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -238,7 +257,7 @@ def decode_workload(args, torch, synth, pk, dev):
         "step": "kv_append + paged_attention_decode" if two_calls else "paged_attention_decode_append",
     }
     return dict(wall=wall, kv_total=float(sum(per_step_kv)), dec_ms=dec_ms, dec_kv=dec_kv,
-                config=config, cpu=cpu, dtype="bf16" if dtype != "fp8" else "fp8-e4m3 K/V, bf16 q",
+                config=config, cpu=cpu, traffic=measured_traffic(name, two_calls), dtype="bf16" if dtype != "fp8" else "fp8-e4m3 K/V, bf16 q",
                 kernel=("paged_attention_decode" if two_calls else "paged_attention_decode_append")
                 + " call (decode_stream_kernel + stream_reduce_kernel)")
 
@@ -313,7 +332,9 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": r.get("traffic"),
+            "traffic_note": "HBM bytes read + written per decode_stream_kernel launch (rocprofv3 "
+                            "FETCH_SIZE/WRITE_SIZE, copy-calibrated); null if the kernel source changed",
             "us_per_call": round(dec_mean_s * 1e6, 2),
             "calls_timed": int(len(r["dec_ms"])),
         }
