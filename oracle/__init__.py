@@ -33,6 +33,7 @@ from .fp8 import (E4M3_MAX, e4m3_decode, e4m3_encode, e4m3_value_table,
                   quantize_run)
 from .attention import (attention_fp64, attention_bruteforce, partitioned_fp64,
                         partition_states, combine_partitions, decode_batch_fp64)
+from .prefix_cache import RefPrefixCache, reserve_cow
 
 __all__ = [
     "kv_bytes_per_token", "kv_total_bytes", "kv_total_bytes_hidden",
@@ -43,4 +44,5 @@ __all__ = [
     "E4M3_MAX", "e4m3_decode", "e4m3_encode", "e4m3_value_table", "quantize_run",
     "attention_fp64", "attention_bruteforce", "partitioned_fp64",
     "partition_states", "combine_partitions", "decode_batch_fp64",
+    "RefPrefixCache", "reserve_cow",
 ]
