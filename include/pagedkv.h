@@ -170,6 +170,64 @@ int kv_slot_mapping(const kv_pool* pool, const int32_t* table_row, int32_t n_tab
 int kv_batch_reserve(kv_pool* pool, int32_t B, int32_t* table, int32_t max_blocks, int32_t* lens,
                      const int32_t* n_new, int32_t* slots_out);
 
+/* ---------------------------------------------------- prefix sharing -- */
+
+/* Host: the prefix cache ("KV cache and PagedAttention", askaiml §6 "Prefix
+ * caching": the engine hashes a prompt prefix, keeps its KV pages under that
+ * key and reuses them for a later request with the same prefix; the key
+ * carries the tenant so tenants never share).  Granularity is one whole page:
+ * page i of a prompt is keyed by (tenant, the entry of page i-1, its 16
+ * token ids), compared exactly (a 64-bit FNV-1a hash only locates keys), so a
+ * page is reused only after an identical prefix.  The cache holds one
+ * reference on every cached page.  Every match or insert touch stamps the
+ * entry with the next value of a counter.  All host functions, no device work.
+ *
+ * kv_prefix_match: walks the whole pages of tokens[0, n_tokens) from the
+ * start, stopping at the first page without an entry or after max_blocks;
+ * writes the cached pages to blocks_out (host [max_blocks]) and their number
+ * to *n_matched.  Each matched page gains one reference (the caller's table
+ * now maps it; kv_block_release it when the request ends). */
+int kv_prefix_match(kv_pool* pool, int64_t tenant, const int32_t* tokens, int32_t n_tokens,
+                    int32_t* blocks_out, int32_t max_blocks, int32_t* n_matched);
+
+/* kv_prefix_insert: once table_row's pages hold the KV of tokens[0, n_tokens),
+ * enters its whole pages: a page whose key is already cached keeps the
+ * existing entry (table_row's page stays private to its request); otherwise
+ * table_row[i] becomes the entry and gains one reference.  *n_added = new
+ * entries.  KV_E_INVALID if n_table < n_tokens / 16; KV_E_BAD_BLOCK (nothing
+ * changed) if any of those table entries is out of range or free. */
+int kv_prefix_insert(kv_pool* pool, int64_t tenant, const int32_t* tokens, int32_t n_tokens,
+                     const int32_t* table_row, int32_t n_table, int32_t* n_added);
+
+/* kv_prefix_evict: frees up to n_wanted cached pages, least recently touched
+ * first, among entries whose page no request maps (refcount 1) and that no
+ * other entry continues (removing one may make its parent eligible).  The
+ * freed pages go on the free stack in that order and, if blocks_freed is not
+ * NULL (host [n_wanted]), are listed there; *n_freed = how many. */
+int kv_prefix_evict(kv_pool* pool, int32_t n_wanted, int32_t* blocks_freed, int32_t* n_freed);
+
+/* Number of cache entries (cached pages). */
+int kv_prefix_num_entries(const kv_pool* pool, int32_t* n);
+
+/* Host: kv_batch_reserve with copy-on-write.  Same arguments and effect, except
+ * that a request about to write into its partly filled last page while that
+ * page is shared (refcount > 1, e.g. after a fork for parallel sampling or
+ * beam search: copy the table row and kv_block_retain_n its pages) gets a
+ * fresh page in its table instead.  The old page loses that reference and the
+ * pair is listed in copy_src / copy_dst (host, capacity B; *n_copies pairs)
+ * for kv_block_copy, which must run before the new tokens are appended.  Per
+ * request the copy's page is allocated before the request's new pages.  On
+ * error nothing changes (stack, counts, table, lens as before). */
+int kv_batch_reserve_cow(kv_pool* pool, int32_t B, int32_t* table, int32_t max_blocks, int32_t* lens,
+                         const int32_t* n_new, int32_t* slots_out, int32_t* copy_src, int32_t* copy_dst,
+                         int32_t* n_copies);
+
+/* Device: copy page src[i] to page dst[i] for i < n, every layer, K and V, and
+ * for fp8 pools both scales.  src, dst: device int32 [n]; pairs with an id out
+ * of [0, num_blocks), or src == dst, are skipped.  Destinations must be
+ * distinct and not also sources (the copies run concurrently). */
+int kv_block_copy(kv_pool* pool, const int32_t* src, const int32_t* dst, int32_t n, void* hip_stream);
+
 /* --------------------------------------------------------------- append -- */
 
 /* Device: write T new tokens into layer `layer` of the pool.

@@ -27,7 +27,8 @@ page ids, counts and order):
 * `insert` is called once the request's pages hold the prompt's KV: for each
   whole page of the prompt it keeps an existing entry with that key (the
   request's own page then stays private) or adds one for the request's page
-  and retains it.
+  and retains it.  Every page of the row must be allocated, else nothing
+  changes (BadBlock).
 * Every touch (match or insert) stamps the entry with the next value of a
   counter.  `evict` frees pages least recently touched first, among entries
   that no request maps (page refcount 1: the cache's own reference) and that
@@ -85,6 +86,9 @@ class RefPrefixCache:
         keys = self._keys(tenant, tokens)
         if len(keys) > len(table_row):
             raise ValueError("table row shorter than the prompt's whole pages")
+        for i in range(len(keys)):      # all or nothing: check before changing
+            if self.alloc.refcount(int(table_row[i])) == 0:
+                raise BadBlock(int(table_row[i]))
         added = 0
         for i, k in enumerate(keys):
             e = self.entries.get(k)

@@ -7,5 +7,7 @@ from .binding import (  # noqa: F401
     load_library, make_desc, kv_bytes_per_token, kv_blocks_for_tokens, kv_pool_buffer_bytes,
     kv_pool_create, kv_pool_destroy, kv_block_alloc, kv_block_retain, kv_block_release, kv_block_retain_n, kv_block_release_n,
     kv_block_refcount, kv_num_free_blocks, kv_slot_mapping, kv_batch_reserve, kv_append,
-    paged_attention_workspace_bytes, paged_attention_decode, kv_status_string, kv_last_error)
+    paged_attention_workspace_bytes, paged_attention_decode, paged_attention_decode_append,
+    kv_prefix_match, kv_prefix_insert, kv_prefix_evict, kv_prefix_num_entries, kv_batch_reserve_cow,
+    kv_block_copy, kv_status_string, kv_last_error)
 from .build import LIB_PATH, build as build_library  # noqa: F401

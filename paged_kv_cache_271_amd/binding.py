@@ -55,6 +55,13 @@ SIGNATURES = {
     "paged_attention_decode_append": (ctypes.c_int, [_P, _I32, _P, _P, _I32, _P, _P, _P, _P, _I32,
                                                      _P, _I32, _I32, _I32, ctypes.c_float, _I32, _P,
                                                      _I64, _P]),
+    "kv_prefix_match": (ctypes.c_int, [_P, _I64, _PI32, _I32, _PI32, _I32, _PI32]),
+    "kv_prefix_insert": (ctypes.c_int, [_P, _I64, _PI32, _I32, _PI32, _I32, _PI32]),
+    "kv_prefix_evict": (ctypes.c_int, [_P, _I32, _PI32, _PI32]),
+    "kv_prefix_num_entries": (ctypes.c_int, [_P, _PI32]),
+    "kv_batch_reserve_cow": (ctypes.c_int, [_P, _I32, _PI32, _I32, _PI32, _PI32, _PI32, _PI32, _PI32,
+                                            _PI32]),
+    "kv_block_copy": (ctypes.c_int, [_P, _P, _P, _I32, _P]),
     "kv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kv_last_error": (ctypes.c_char_p, []),
 }
@@ -235,7 +242,65 @@ def kv_batch_reserve(h, table, lens, n_new):
     return out
 
 
+def kv_prefix_match(h, tenant, tokens, max_blocks=None):
+    """Pages of the longest cached whole-page prefix of `tokens` (each retained)."""
+    t = _host_i32(tokens)
+    cap = t.size // 16 if max_blocks is None else int(max_blocks)
+    out = np.empty(max(cap, 1), dtype=np.int32)
+    n = ctypes.c_int32()
+    _check(_lib.kv_prefix_match(h, int(tenant), _i32p(t), t.size, _i32p(out), cap, ctypes.byref(n)))
+    return out[:n.value].copy()
+
+
+def kv_prefix_insert(h, tenant, tokens, table_row):
+    t = _host_i32(tokens)
+    r = _host_i32(table_row)
+    n = ctypes.c_int32()
+    _check(_lib.kv_prefix_insert(h, int(tenant), _i32p(t), t.size, _i32p(r), r.size, ctypes.byref(n)))
+    return n.value
+
+
+def kv_prefix_evict(h, n_wanted):
+    out = np.empty(max(int(n_wanted), 1), dtype=np.int32)
+    n = ctypes.c_int32()
+    _check(_lib.kv_prefix_evict(h, int(n_wanted), _i32p(out), ctypes.byref(n)))
+    return out[:n.value].copy()
+
+
+def kv_prefix_num_entries(h):
+    n = ctypes.c_int32()
+    _check(_lib.kv_prefix_num_entries(h, ctypes.byref(n)))
+    return n.value
+
+
+def kv_batch_reserve_cow(h, table, lens, n_new):
+    """kv_batch_reserve with copy-on-write; returns (slots, copy_src, copy_dst)."""
+    if table.dtype != np.int32 or not table.flags.c_contiguous or table.ndim != 2:
+        raise TypeError("table must be a C-contiguous int32 [B, max_blocks] array")
+    if lens.dtype != np.int32 or not lens.flags.c_contiguous or lens.size != table.shape[0]:
+        raise TypeError("lens must be a contiguous int32 [B] array")
+    nn = _host_i32(n_new)
+    if nn.size != lens.size:
+        raise ValueError("n_new must have B entries")
+    out = np.empty(int(nn.sum()), dtype=np.int32)
+    src = np.empty(max(lens.size, 1), dtype=np.int32)
+    dst = np.empty(max(lens.size, 1), dtype=np.int32)
+    nc = ctypes.c_int32()
+    _check(_lib.kv_batch_reserve_cow(h, lens.size, _i32p(table), table.shape[1], _i32p(lens),
+                                     _i32p(nn), _i32p(out), _i32p(src), _i32p(dst), ctypes.byref(nc)))
+    return out, src[:nc.value].copy(), dst[:nc.value].copy()
+
+
 # ------------------------------------------------------------ device ops ----
+def kv_block_copy(h, src, dst, stream=None):
+    """src, dst: int32 device tensors of page ids (same length)."""
+    import torch
+    n = src.numel()
+    sp = _dev_ptr(src, "src", torch.int32)
+    dp = _dev_ptr(dst, "dst", torch.int32, n)
+    _check(_lib.kv_block_copy(h, sp, dp, n, _stream_ptr(stream)))
+
+
 def kv_append(h, desc, layer, k_new, v_new, slot_mapping, stream=None):
     """k_new, v_new: [T, h_kv, d_h] (float32 for f32 pools, bfloat16 otherwise);
     slot_mapping: int32 [T] on the device."""
@@ -381,6 +446,24 @@ class Pool:
 
     def batch_reserve(self, table, lens, n_new):
         return kv_batch_reserve(self.handle, table, lens, n_new)
+
+    def prefix_match(self, tenant, tokens, max_blocks=None):
+        return kv_prefix_match(self.handle, tenant, tokens, max_blocks)
+
+    def prefix_insert(self, tenant, tokens, table_row):
+        return kv_prefix_insert(self.handle, tenant, tokens, table_row)
+
+    def prefix_evict(self, n_wanted):
+        return kv_prefix_evict(self.handle, n_wanted)
+
+    def prefix_num_entries(self):
+        return kv_prefix_num_entries(self.handle)
+
+    def batch_reserve_cow(self, table, lens, n_new):
+        return kv_batch_reserve_cow(self.handle, table, lens, n_new)
+
+    def block_copy(self, src, dst, stream=None):
+        kv_block_copy(self.handle, src, dst, stream)
 
     def append(self, layer, k_new, v_new, slot_mapping, stream=None):
         kv_append(self.handle, self.desc, layer, k_new, v_new, slot_mapping, stream)

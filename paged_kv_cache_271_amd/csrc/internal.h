@@ -2,13 +2,52 @@
 // libpagedkv.  Not part of the ABI.
 #pragma once
 
+#include <array>
 #include <cstdint>
+#include <set>
 #include <string>
+#include <unordered_map>
+#include <utility>
 #include <vector>
 
 #include <hip/hip_runtime.h>
 
 #include "pagedkv.h"
+
+namespace pagedkv {
+
+// Prefix-cache key of one whole page: tenant, the entry of the page before it
+// (-1 for the first page) and its 16 token ids.  Compared exactly; the hash
+// only locates it.
+struct PrefixKey {
+  int64_t tenant;
+  int32_t parent;
+  std::array<int32_t, 16> tokens;
+  bool operator==(const PrefixKey& o) const {
+    return tenant == o.tenant && parent == o.parent && tokens == o.tokens;
+  }
+};
+
+struct PrefixKeyHash {
+  size_t operator()(const PrefixKey& k) const;
+};
+
+struct PrefixEntry {
+  PrefixKey key;
+  int32_t block;
+  int64_t tick;      // last touch
+  int32_t children;  // entries whose parent this is
+};
+
+struct PrefixCache {
+  std::unordered_map<PrefixKey, int32_t, PrefixKeyHash> index;  // key -> entry
+  std::vector<PrefixEntry> entries;
+  std::vector<int32_t> free_entries;                // reusable entry slots
+  std::set<std::pair<int64_t, int32_t>> leaves;     // (tick, entry) with no children
+  int64_t clock = 0;
+};
+
+}  // namespace pagedkv
 
 struct kv_pool {
   kv_pool_desc desc;
@@ -18,6 +57,7 @@ struct kv_pool {
   float* v_scale;
   std::vector<int32_t> stack;  // free blocks; the back is the top
   std::vector<int32_t> rc;     // reference count per block, 0 = free
+  pagedkv::PrefixCache prefix;
 };
 
 namespace pagedkv {
@@ -39,6 +79,13 @@ inline int64_t layer_elems(const kv_pool_desc& d) {
 // Device launches (append.hip, decode.hip).  Arguments are already checked.
 int launch_append(const kv_pool* pool, int32_t layer, const void* k_new, const void* v_new,
                   const int32_t* slots, int32_t T, hipStream_t stream);
+int launch_block_copy(const kv_pool* pool, const int32_t* src, const int32_t* dst, int32_t n,
+                      hipStream_t stream);
+
+// Host allocator primitives shared by pool.cpp and prefix.cpp.
+inline bool block_live(const kv_pool* p, int32_t b) {
+  return b >= 0 && b < p->desc.num_blocks && p->rc[b] > 0;
+}
 
 // Launch plan of one decode.  fp32 caches use fixed partitions of `part`
 // tokens (num_part of them, states [B][h_q][num_part]); bf16 and fp8 caches

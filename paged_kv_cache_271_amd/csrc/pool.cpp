@@ -21,10 +21,6 @@ bool desc_valid(const kv_pool_desc* d) {
          d->num_kv_heads >= 1 && d->head_dim >= 1 && d->cache_dtype >= KV_F32 &&
          d->cache_dtype <= KV_FP8_E4M3;
 }
-
-bool block_live(const kv_pool* p, int32_t b) {
-  return b >= 0 && b < p->desc.num_blocks && p->rc[b] > 0;
-}
 }  // namespace
 
 namespace pagedkv {
