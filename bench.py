@@ -39,7 +39,7 @@ METRIC = "paged decode-attention KV GB/s (% of HBM peak) + µs/step, Llama-3-8B 
 HBM_PEAK_GBS = 8000.0
 EVENT_EVERY = 8
 DEFAULT_LAYERS = {"llama3_8b": 32, "llama3_70b_long": 8, "fp8": 16}
-DEFAULT_SEED = {"llama3_8b": 2, "llama3_70b_long": 3, "fp8": 5, "prefix_churn": 4}
+DEFAULT_SEED = {"llama3_8b": 2, "llama3_70b_long": 3, "fp8": 5, "prefix_churn": 4, "cow_fork": 6}
 
 # HBM bytes (read + written) per launch of decode_stream_kernel in the default
 # step of each workload, from the rocprofv3 FETCH_SIZE and WRITE_SIZE runs in
@@ -67,7 +67,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=1024)
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--workload", default="llama3_8b",
-                    choices=["llama3_8b", "llama3_70b_long", "fp8", "prefix_churn"])
+                    choices=["llama3_8b", "llama3_70b_long", "fp8", "prefix_churn", "cow_fork"])
     ap.add_argument("--layers", type=int, default=0, help="layers in the pool (0: workload default)")
     ap.add_argument("--seed", type=int, default=-1, help="input seed (-1: workload default)")
     ap.add_argument("--partition", type=int, default=0,
@@ -276,6 +276,7 @@ def churn_workload(args, torch, synth, pk, dev):
         run.step(s)
     torch.cuda.synchronize()
     logical, unique = [], []
+    run.admit_seconds = 0.0
     t0 = time.perf_counter()
     for s in range(args.steps):
         run.step(args.warmup + s)
@@ -287,9 +288,74 @@ def churn_workload(args, torch, synth, pk, dev):
               "prefix_tokens": w["prefix_tokens"], "suffix_range": list(w["suffix_range"]),
               "churn_per_step": w["churn"], "partition_tokens": 0,
               "unique_kv_bytes_per_step": int(np.mean(unique)),
-              "unique_kv_GBs": round(float(sum(unique)) / wall / 1e9, 1)}
+              "unique_kv_GBs": round(float(sum(unique)) / wall / 1e9, 1),
+              "admission": "kv_prefix_match of the 2000-token prefix (125 pages)",
+              "admission_host_us_per_request": round(run.admit_seconds / (args.steps * w["churn"]) * 1e6, 2)}
     return dict(wall=wall, kv_total=float(sum(logical)), dec_ms=None, dec_kv=None, config=config,
                 cpu=None, dtype="bf16", kernel=None)
+
+
+def cow_fork_workload(args, torch, synth, pk, dev):
+    """Copy-on-write forks (parallel sampling / beam search): every step forks
+    each of 256 parent requests (Llama-3-8B heads, 32 layers) whose only page
+    is partly filled; the children reserve one token each through
+    kv_batch_reserve_cow, one kv_block_copy call copies the 256 shared pages
+    in every layer, and the children are retired again (host).  value = bytes
+    the copy reads and writes per second of wall time."""
+    B, L, H, D = 256, 32, 8, 128
+    N = 2 * B + 8
+    rng = synth.streams(args.seed)
+    order = synth.permutation(rng["free_order"], N)
+    pool = pk.Pool(L, N, H, D, "bf16", dev, initial_free_order=order)
+    ptable = np.zeros((B, 1), np.int32)
+    plen = np.zeros(B, np.int32)
+    slots = pool.batch_reserve(ptable, plen, rng["contexts"].integers(1, 16, B).astype(np.int32))
+    d_slots = torch.from_numpy(slots).to(dev)
+    for layer in range(L):
+        k = synth.device_normal((len(slots), H, D), 3000 + 2 * layer, dev, torch.bfloat16)
+        v = synth.device_normal((len(slots), H, D), 3001 + 2 * layer, dev, torch.bfloat16)
+        pool.append(layer, k, v, d_slots)
+    page_bytes = H * 16 * D * 2
+    moved = 2 * B * L * 2 * page_bytes          # read + written, K and V
+    pinned = torch.empty(2 * B, dtype=torch.int32, pin_memory=True)
+    d_pairs = torch.empty(2 * B, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    ones = np.ones(B, np.int32)
+
+    def step(ev=None):
+        ctable, clen = ptable.copy(), plen.copy()
+        pool.retain_n(ctable.reshape(-1))           # the fork
+        _, src, dst = pool.batch_reserve_cow(ctable, clen, ones)
+        assert len(src) == B
+        pn = pinned.numpy()
+        pn[:B], pn[B:] = src, dst
+        d_pairs.copy_(pinned, non_blocking=True)
+        if ev is not None:
+            ev[0].record(stream)
+        pool.block_copy(d_pairs[:B], d_pairs[B:])
+        if ev is not None:
+            ev[1].record(stream)
+        pool.release_n(ctable.reshape(-1))          # the children retire
+        return moved
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [(TimingEvent(), TimingEvent()) if j % EVENT_EVERY == 0 else None for j in range(args.steps)]
+    t0 = time.perf_counter()
+    total = 0
+    for j in range(args.steps):
+        total += step(events[j])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec_ms = np.array([e[0].elapsed_ms(e[1]) for e in events if e is not None])
+    config = {"workload": "cow_fork_page_copy", "forks_per_step": B, "layers": L, "h_kv": H, "head_dim": D,
+              "cache_dtype": "bf16", "page_bytes_per_layer_kv": 2 * page_bytes,
+              "bytes_moved_per_step": moved}
+    return dict(wall=wall, kv_total=float(total), dec_ms=dec_ms, dec_kv=np.full(len(dec_ms), float(moved)),
+                config=config, cpu=None, traffic=None, dtype="bf16",
+                kernel="kv_block_copy call (block_copy_kernel), bytes read + written",
+                metric="kv_block_copy GB/s (read + written), copy-on-write forks")
 
 
 def main():
@@ -312,6 +378,8 @@ def main():
 
     if args.workload == "prefix_churn":
         r = churn_workload(args, torch, synth, pk, dev)
+    elif args.workload == "cow_fork":
+        r = cow_fork_workload(args, torch, synth, pk, dev)
     else:
         r = decode_workload(args, torch, synth, pk, dev)
     value = r["kv_total"] / r["wall"] / 1e9
@@ -343,7 +411,7 @@ def main():
     config["hbm_fraction"] = round(value / HBM_PEAK_GBS, 4)
     config["kv_bytes_per_step"] = int(mean_kv)
     res = {
-        "metric": METRIC,
+        "metric": r.get("metric", METRIC),
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,

@@ -177,9 +177,9 @@ int kv_batch_reserve(kv_pool* pool, int32_t B, int32_t* table, int32_t max_block
  * key and reuses them for a later request with the same prefix; the key
  * carries the tenant so tenants never share).  Granularity is one whole page:
  * page i of a prompt is keyed by (tenant, the entry of page i-1, its 16
- * token ids), compared exactly (a 64-bit FNV-1a hash only locates keys), so a
- * page is reused only after an identical prefix.  The cache holds one
- * reference on every cached page.  Every match or insert touch stamps the
+ * token ids), compared exactly (a 64-bit FNV-1a-style hash over the key's
+ * 32-bit words only locates keys), so a page is reused only after an
+ * identical prefix.  The cache holds one reference on every cached page.  Every match or insert touch stamps the
  * entry with the next value of a counter.  All host functions, no device work.
  *
  * kv_prefix_match: walks the whole pages of tokens[0, n_tokens) from the

@@ -11,8 +11,8 @@
 //
 // A page's key is (tenant, entry of the page before it, its 16 tokens), so a
 // page is reused only when everything before it matches as well.  Keys are
-// compared exactly; FNV-1a (64-bit) over the key's bytes only picks the hash
-// bucket.  The cache holds one reference on each cached page; every match or
+// compared exactly; an FNV-1a style hash over the key's 32-bit words only
+// picks the hash bucket.  The cache holds one reference on each cached page; every match or
 // insert touch stamps the entry with a counter, and eviction frees, least
 // recently touched first, entries that no request maps (refcount 1) and that
 // no other entry continues.
@@ -25,18 +25,18 @@
 namespace pagedkv {
 
 size_t PrefixKeyHash::operator()(const PrefixKey& k) const {
-  uint64_t h = 0xcbf29ce484222325ull;  // FNV-1a offset basis
-  auto mix = [&h](const void* p, size_t n) {
-    const auto* c = static_cast<const unsigned char*>(p);
-    for (size_t i = 0; i < n; ++i) {
-      h ^= c[i];
-      h *= 0x100000001b3ull;  // FNV prime
-    }
+  // FNV-1a's xor-then-multiply step with its 64-bit offset basis and prime,
+  // taken over 32-bit words instead of bytes (19 steps per key, not 76)
+  uint64_t h = 0xcbf29ce484222325ull;
+  auto step = [&h](uint32_t w) {
+    h ^= w;
+    h *= 0x100000001b3ull;
   };
-  mix(&k.tenant, sizeof k.tenant);
-  mix(&k.parent, sizeof k.parent);
-  mix(k.tokens.data(), sizeof(int32_t) * k.tokens.size());
-  return size_t(h);
+  step(uint32_t(uint64_t(k.tenant)));
+  step(uint32_t(uint64_t(k.tenant) >> 32));
+  step(uint32_t(k.parent));
+  for (const int32_t t : k.tokens) step(uint32_t(t));
+  return size_t(h ^ (h >> 32));
 }
 
 namespace {

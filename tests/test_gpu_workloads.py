@@ -120,7 +120,8 @@ def test_prefix_sharing_with_churn(gpu_lib):
     run = workloads.PrefixChurn(DEV, layers=w["num_layers"], batch=w["batch"],
                                 prefix=w["prefix_tokens"], suffix=w["suffix_range"],
                                 steps=w["steps"], churn=w["churn"], seed=4,
-                                record_layers=layers, record_slots=slots, mirror=ref_alloc)
+                                record_layers=layers, record_slots=slots, mirror=ref_alloc,
+                                mirror_cache=oracle.RefPrefixCache(ref_alloc))
     pb = w["prefix_tokens"] // 16
     scale = 1.0 / math.sqrt(128)
     for s in range(w["steps"]):
@@ -148,8 +149,11 @@ def test_prefix_sharing_with_churn(gpu_lib):
         if s % 8 == 0:
             log(f"step {s}: free {run.pool.num_free()}, logical {run.logical_kv_bytes() / 1e9:.2f} GB, "
                 f"unique {run.unique_kv_bytes() / 1e9:.3f} GB per layer")
-    # retire everything and drop the prefix entry: the pool is whole again
+    # retire everything and evict the cached prefix: the pool is whole again
     for b in range(w["batch"]):
         run._retire(b)
-    run.pool.release_n(run.prefix_blocks)
-    assert run.pool.num_free() == run.N
+    assert run.pool.prefix_num_entries() == pb
+    freed = run.pool.prefix_evict(pb + 10)
+    # a chain: only its last page is a leaf, so the pages go last to first
+    assert list(freed) == [int(x) for x in run.prefix_blocks[::-1]]
+    assert run.pool.num_free() == run.N and run.pool.prefix_num_entries() == 0

@@ -4,13 +4,15 @@ from `synth`; they hold no attention arithmetic.
 
 PrefixChurn -- continuous batching over a shared prefix ("KV cache and
 PagedAttention", askaiml.pages.dev, §4 "PagedAttention" page sharing, §5
-"Continuous batching", §6 "Prefix caching"): `batch` live requests map the
-same prefix blocks (reference count 1 for the prefix entry plus one per live
-request) followed by private suffix blocks.  Each step retires `churn`
-requests (their blocks released: the prefix count drops, suffix blocks return
-to the free list), admits as many new ones with fresh suffixes, and then, for
-every layer, one kv_append call writes the new suffixes and one new token of
-every other live request, and paged_attention_decode reads all of them.
+"Continuous batching", §6 "Prefix caching"): the prefix is computed once and
+entered in the library's prefix cache; every admitted request finds its
+blocks with kv_prefix_match (reference count 1 for the cache plus one per
+live request) and follows them with private suffix blocks.  Each step retires
+`churn` requests (their blocks released: the prefix count drops, suffix
+blocks return to the free list), admits as many new ones with fresh suffixes,
+and then, for every layer, one kv_append call writes the new suffixes and one
+new token of every other live request, and paged_attention_decode reads all
+of them.
 """
 
 import math
@@ -25,7 +27,7 @@ H, D, HQ = 8, 128, 32
 class PrefixChurn:
     def __init__(self, dev, layers=32, batch=256, prefix=2000, suffix=(5, 500), steps=64,
                  churn=26, seed=4, record_layers=(), record_slots=(), mirror=None,
-                 reuse_inputs=False):
+                 mirror_cache=None, reuse_inputs=False):
         import torch
         import paged_kv_cache_271_amd as pk
         self.torch, self.pk, self.dev = torch, pk, dev
@@ -40,9 +42,14 @@ class PrefixChurn:
         self.N = self.pb + batch * max_suffix_blocks + 16
         order = synth.permutation(self.rng["free_order"], self.N)
         self.pool = pk.Pool(layers, self.N, H, D, "bf16", dev, initial_free_order=order)
-        self.mirror = mirror           # optional reference allocator driven in lockstep
+        # optional reference allocator and prefix cache (over that allocator)
+        # driven in lockstep with the library
+        self.mirror, self.mirror_cache = mirror, mirror_cache
+        assert (mirror is None) == (mirror_cache is None)
         if mirror is not None:
             mirror.__init__(self.N, order)
+        self.prefix_tokens = np.arange(prefix, dtype=np.int32) + 1_000_000
+        self.admit_seconds = 0.0
         self.record_layers = tuple(record_layers)
         self.record_slots = tuple(record_slots)
         self.scale = 1.0 / math.sqrt(D)
@@ -69,6 +76,13 @@ class PrefixChurn:
             self.pool.append(layer, k, v, d_slots)
             if layer in self.record_layers:
                 self.prefix_bits[layer] = (_bits(k), _bits(v))
+        # the cache takes its own reference; the prefill's is dropped
+        assert self.pool.prefix_insert(0, self.prefix_tokens, ptab[0]) == self.pb
+        self.pool.release_n(ptab[0])
+        if mirror is not None:
+            assert mirror_cache.insert(0, self.prefix_tokens, list(ptab[0])) == self.pb
+            for blk in ptab[0]:
+                mirror.release(int(blk))
 
         self.table = np.zeros((batch, self.MB), np.int32)
         self.lens = np.zeros(batch, np.int32)
@@ -104,11 +118,14 @@ class PrefixChurn:
                 assert got == table[b, j], (b, j, got, table[b, j])
 
     def _admit(self, b):
-        self.table[b, :self.pb] = self.prefix_blocks
-        self.pool.retain_n(self.prefix_blocks)
+        import time
+        t0 = time.perf_counter()
+        hit = self.pool.prefix_match(0, self.prefix_tokens)
+        self.admit_seconds += time.perf_counter() - t0
+        assert len(hit) == self.pb
+        self.table[b, :self.pb] = hit
         if self.mirror is not None:
-            for blk in self.prefix_blocks:
-                self.mirror.retain(int(blk))
+            assert list(hit) == self.mirror_cache.match(0, self.prefix_tokens)
         self.lens[b] = self.prefix_len
         for l in self.record_layers:
             if (l, b) in self.history:
