@@ -15,7 +15,7 @@ Sources (the pages this follows; section names as printed on each page):
 * "KV cache and PagedAttention" (askaiml.pages.dev) -- §1 "The setup",
   §2 "Memory cost" (formula and worked examples), §3 "Naive implementation",
   §4 "PagedAttention", §6 "Prefix caching", §7 "KV cache quantisation",
-  §9 "The big picture".
+  §8 "Sliding-window cache and attention sinks", §9 "The big picture".
 * "KV Cache" glossary (inferensys.com) -- cache-size calculation, PagedAttention
   block management, GQA and MQA entries.
 * "Memoizing Context via KV Caching" (blog.sanjeevnode.in) -- the attention
@@ -34,6 +34,7 @@ from .fp8 import (E4M3_MAX, e4m3_decode, e4m3_encode, e4m3_value_table,
 from .attention import (attention_fp64, attention_bruteforce, partitioned_fp64,
                         partition_states, combine_partitions, decode_batch_fp64)
 from .prefix_cache import RefPrefixCache, reserve_cow
+from .window import window_positions, attention_window_fp64, dead_pages, window_cache_bytes
 
 __all__ = [
     "kv_bytes_per_token", "kv_total_bytes", "kv_total_bytes_hidden",
@@ -45,4 +46,5 @@ __all__ = [
     "attention_fp64", "attention_bruteforce", "partitioned_fp64",
     "partition_states", "combine_partitions", "decode_batch_fp64",
     "RefPrefixCache", "reserve_cow",
+    "window_positions", "attention_window_fp64", "dead_pages", "window_cache_bytes",
 ]
