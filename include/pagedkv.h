@@ -313,6 +313,37 @@ int paged_attention_decode_append(kv_pool* pool, int32_t layer, void* out, const
                                   int32_t h_q, int32_t max_ctx, float scale, int32_t partition_tokens,
                                   void* workspace, int64_t workspace_bytes, void* hip_stream);
 
+/* ------------------------------------------------------ sliding window -- */
+
+/* Device: paged_attention_decode for a model with sliding-window attention
+ * and attention sinks ("KV cache and PagedAttention", askaiml §8: only the
+ * last W tokens are needed, and keeping the first few tokens as well steadies
+ * long generations).  For a request of n = context_lens[b] tokens the output
+ * is the attention over positions t < sink_tokens and n - window_tokens <= t
+ * < n, positions keeping their index.  Only pages holding such positions are
+ * read, so their table entries must be valid and the others may be -1 or
+ * released (kv_window_release).  sink_tokens >= 0, window_tokens >= 1, bf16
+ * and fp8 pools (KV_E_UNSUPPORTED for f32).  All other arguments, the
+ * workspace and errors are those of paged_attention_decode. */
+int paged_attention_decode_window(kv_pool* pool, int32_t layer, void* out, const void* q, int32_t q_dtype,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t B, int32_t h_q, int32_t max_ctx,
+                                  float scale, int32_t sink_tokens, int32_t window_tokens,
+                                  int32_t partition_tokens, void* workspace, int64_t workspace_bytes,
+                                  void* hip_stream);
+
+/* Host: give back the pages no later windowed decode of these requests reads.
+ * The window only moves forward, so logical page j of a request of lens[b]
+ * tokens is dead when 16 j >= sink_tokens and 16 (j + 1) <= lens[b] -
+ * window_tokens.  Each dead page's table entry loses its reference (pushed on
+ * the free stack at zero, request by request, page by page) and becomes -1;
+ * entries already -1 are skipped.  table: host [B][max_blocks], edited;
+ * lens: host [B].  *n_released = pages dropped.  KV_E_INVALID for bad sizes,
+ * KV_E_BAD_BLOCK if a dead entry is free, out of range or dropped more often
+ * than it is mapped; nothing changes on an error. */
+int kv_window_release(kv_pool* pool, int32_t B, int32_t* table, int32_t max_blocks, const int32_t* lens,
+                      int32_t sink_tokens, int32_t window_tokens, int32_t* n_released);
+
 /* -------------------------------------------------------------- errors -- */
 
 /* Static name of a status code. */

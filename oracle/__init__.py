@@ -34,7 +34,8 @@ from .fp8 import (E4M3_MAX, e4m3_decode, e4m3_encode, e4m3_value_table,
 from .attention import (attention_fp64, attention_bruteforce, partitioned_fp64,
                         partition_states, combine_partitions, decode_batch_fp64)
 from .prefix_cache import RefPrefixCache, reserve_cow
-from .window import window_positions, attention_window_fp64, dead_pages, window_cache_bytes
+from .window import (window_positions, attention_window_fp64, dead_pages, window_cache_bytes,
+                     window_release)
 
 __all__ = [
     "kv_bytes_per_token", "kv_total_bytes", "kv_total_bytes_hidden",
@@ -46,5 +47,5 @@ __all__ = [
     "attention_fp64", "attention_bruteforce", "partitioned_fp64",
     "partition_states", "combine_partitions", "decode_batch_fp64",
     "RefPrefixCache", "reserve_cow",
-    "window_positions", "attention_window_fp64", "dead_pages", "window_cache_bytes",
+    "window_positions", "attention_window_fp64", "dead_pages", "window_cache_bytes", "window_release",
 ]

@@ -16,7 +16,9 @@ Readings taken where the page is silent:
 * A page can go back to the pool once none of its positions can be read again:
   the window only moves forward as the request grows, so page p (positions
   16p .. 16p + 15) is dead for a request of n tokens when all its positions
-  are at or past S and before n - W.
+  are at or past S and before n - W.  `window_release` drops the request's
+  reference on each dead page, request by request and page by page, and marks
+  the table entry -1 (a free page is never read again by that request).
 """
 
 import numpy as np
@@ -56,3 +58,29 @@ def window_cache_bytes(window, sink, num_layers, kv_width, dtype_bytes):
     before rounding to pages): the page's formula 2 * W * L * d_kv * b with
     the sink tokens added to W."""
     return 2 * (window + sink) * num_layers * kv_width * dtype_bytes
+
+
+def window_release(alloc, table, lens, sink, window, block_size=16):
+    """Give back every dead page of each request (request order, then page
+    order), marking its table entry -1; entries already -1 are skipped.
+    table: per-request page lists (edited in place).  Returns the number
+    released.  Nothing changes if a page is not allocated (BadBlock)."""
+    from .allocator import BadBlock
+    drops = {}
+    for b, row in enumerate(table):
+        for p in dead_pages(lens[b], sink, window, block_size):
+            blk = row[p]
+            if blk == -1:
+                continue
+            drops[blk] = drops.get(blk, 0) + 1
+            if alloc.refcount(blk) < drops[blk]:
+                raise BadBlock(blk)
+    n = 0
+    for b, row in enumerate(table):
+        for p in dead_pages(lens[b], sink, window, block_size):
+            if row[p] == -1:
+                continue
+            alloc.release(row[p])
+            row[p] = -1
+            n += 1
+    return n

@@ -62,6 +62,10 @@ SIGNATURES = {
     "kv_batch_reserve_cow": (ctypes.c_int, [_P, _I32, _PI32, _I32, _PI32, _PI32, _PI32, _PI32, _PI32,
                                             _PI32]),
     "kv_block_copy": (ctypes.c_int, [_P, _P, _P, _I32, _P]),
+    "paged_attention_decode_window": (ctypes.c_int, [_P, _I32, _P, _P, _I32, _P, _I32, _P, _I32, _I32,
+                                                     _I32, ctypes.c_float, _I32, _I32, _I32, _P, _I64,
+                                                     _P]),
+    "kv_window_release": (ctypes.c_int, [_P, _I32, _PI32, _I32, _PI32, _I32, _I32, _PI32]),
     "kv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kv_last_error": (ctypes.c_char_p, []),
 }
@@ -374,6 +378,46 @@ def paged_attention_decode_append(h, desc, layer, out, q, k_new, v_new, slot_map
                                               _stream_ptr(stream)))
 
 
+def paged_attention_decode_window(h, desc, layer, out, q, block_tables, context_lens, max_ctx, scale,
+                                  sink_tokens, window_tokens, partition_tokens=0, workspace=None,
+                                  stream=None):
+    """paged_attention_decode over positions < sink_tokens and the last window_tokens."""
+    import torch
+    if q.dim() != 3 or q.shape[2] != desc.head_dim:
+        raise ValueError("q must be [B, h_q, head_dim]")
+    B, h_q, _ = q.shape
+    want = torch.float32 if desc.cache_dtype == KV_F32 else torch.bfloat16
+    qp = _dev_ptr(q, "q", want)
+    op = _dev_ptr(out, "out", want, q.numel())
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B, max_blocks]")
+    tp = _dev_ptr(block_tables, "block_tables", torch.int32)
+    cp = _dev_ptr(context_lens, "context_lens", torch.int32, B)
+    wp, wb = None, 0
+    if workspace is not None:
+        wp = _dev_ptr(workspace, "workspace")
+        wb = workspace.numel() * workspace.element_size()
+    qd = KV_F32 if want == torch.float32 else KV_BF16
+    _check(_lib.paged_attention_decode_window(h, int(layer), op, qp, qd, tp, block_tables.shape[1], cp, B,
+                                              h_q, int(max_ctx), float(scale), int(sink_tokens),
+                                              int(window_tokens), int(partition_tokens), wp, wb,
+                                              _stream_ptr(stream)))
+
+
+def kv_window_release(h, table, lens, sink_tokens, window_tokens):
+    """Drop the dead pages of every request (table edited in place, -1 marks
+    them); returns how many."""
+    if table.dtype != np.int32 or not table.flags.c_contiguous or table.ndim != 2:
+        raise TypeError("table must be a C-contiguous int32 [B, max_blocks] array")
+    ln = _host_i32(lens)
+    if ln.size != table.shape[0]:
+        raise ValueError("lens must have B entries")
+    n = ctypes.c_int32()
+    _check(_lib.kv_window_release(h, ln.size, _i32p(table), table.shape[1], _i32p(ln), int(sink_tokens),
+                                  int(window_tokens), ctypes.byref(n)))
+    return n.value
+
+
 def kv_status_string(status):
     load_library()
     return _lib.kv_status_string(status).decode()
@@ -483,6 +527,23 @@ class Pool:
         paged_attention_decode(self.handle, self.desc, layer, out, q, block_tables, context_lens,
                                max_ctx, scale, partition_tokens, workspace, stream)
         return out
+
+    def decode_window(self, layer, q, block_tables, context_lens, max_ctx, scale, sink_tokens,
+                      window_tokens, partition_tokens=0, out=None, workspace=None, stream=None):
+        import torch
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            nbytes = self.workspace_bytes(q.shape[0], q.shape[1], max_ctx, partition_tokens)
+            if nbytes > 0:
+                workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+        paged_attention_decode_window(self.handle, self.desc, layer, out, q, block_tables, context_lens,
+                                      max_ctx, scale, sink_tokens, window_tokens, partition_tokens,
+                                      workspace, stream)
+        return out
+
+    def window_release(self, table, lens, sink_tokens, window_tokens):
+        return kv_window_release(self.handle, table, lens, sink_tokens, window_tokens)
 
     def decode_append(self, layer, q, k_new, v_new, slot_mapping, block_tables, context_lens,
                       max_ctx, scale, partition_tokens=0, out=None, workspace=None, stream=None):

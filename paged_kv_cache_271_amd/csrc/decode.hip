@@ -140,13 +140,27 @@ __device__ inline void load_q(bf16x8 (&qv)[D / 32], const uint16_t* q, int64_t r
   }
 }
 
+// Zero the 16-bit elements e of an 8-element vector whose bit e of `keep` is clear.
+__device__ inline u32x4 mask_bits(u32x4 v, uint32_t keep) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t lo = (keep >> (2 * w)) & 1u ? 0x0000FFFFu : 0u;
+    const uint32_t hi = (keep >> (2 * w + 1)) & 1u ? 0xFFFF0000u : 0u;
+    v[w] &= lo | hi;
+  }
+  return v;
+}
+
 // Stream blocks [j0, j1) of one (request, kv-head) into the wave state.
-template <bool FP8, int D>
+// Positions at or past ctx are masked.  WIN: so are positions in
+// [sink, win_lo) (a sliding window with attention sinks).
+template <bool FP8, int D, bool WIN = false>
 __device__ inline void run_segment(WaveState<D>& st, const uint8_t* __restrict__ kc,
                                    const uint8_t* __restrict__ vc, const float* __restrict__ kscale,
                                    const float* __restrict__ vscale, const int32_t* __restrict__ trow,
                                    int ctx, int H, int g, int j0, int j1, float scale_log2,
-                                   const bf16x8 (&qv)[D / 32], int r, int grp) {
+                                   const bf16x8 (&qv)[D / 32], int r, int grp, int sink = 0,
+                                   int win_lo = 0) {
   constexpr int NB = kStreamNB;
   constexpr int KK = D / 32;
   constexpr int T8 = D / 16;
@@ -234,12 +248,22 @@ __device__ inline void run_segment(WaveState<D>& st, const uint8_t* __restrict__
       }
     }
     const int valid = vV ? min(kBS, ctx - bV * kBS) - vtok : 0;  // valid among the lane's 8
+    uint32_t keep = 0;  // WIN: bit e set when token vtok + e of block bV is read
+    if constexpr (WIN) {
+      const int p0 = bV * kBS + vtok;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int p = p0 + e;
+        keep |= uint32_t(vV && p < ctx && (p < sink || p >= win_lo)) << e;
+      }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float s = (4 * j + i < valid) ? S[j][i] * kfac : -INFINITY;
+        const bool ok = WIN ? ((keep >> (4 * j + i)) & 1u) != 0 : 4 * j + i < valid;
+        const float s = ok ? S[j][i] * kfac : -INFINITY;
         S[j][i] = s;
         mx = fmaxf(mx, s);
       }
@@ -276,7 +300,11 @@ __device__ inline void run_segment(WaveState<D>& st, const uint8_t* __restrict__
       } else {
         v = vraw[t];
       }
-      if (vh < 8) v = mask_tail(v, vh);  // stale or poisoned slots past the context
+      if constexpr (WIN) {
+        if (keep != 0xFFu) v = mask_bits(v, keep);  // stale slots, or outside the window
+      } else {
+        if (vh < 8) v = mask_tail(v, vh);  // stale or poisoned slots past the context
+      }
       st.acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), pop, st.acc[t], 0, 0, 0);
     }
   }
@@ -313,14 +341,39 @@ __device__ inline void add_token(WaveState<D>& st, const uint16_t* __restrict__ 
   }
 }
 
-// Exclusive prefix sums of blocks per request into s_pref[0..B] (256 threads).
+// Pages a decode reads for a request of n tokens: logical pages [0, a) and
+// [c, nb), nb = ceil(n / 16).  Without a window a = c = nb.  With `sink`
+// sink tokens and a window of `window` tokens, c is the page of position
+// max(0, n - window) and a = min(pages holding the sinks, c) (a == c: the two
+// ranges meet and every page is read).  Every page read holds at least one
+// position that is read.
+struct VisitedPages {
+  int a, c, nb;
+  __device__ int count() const { return a + nb - c; }
+};
+
+template <bool WIN>
+__device__ inline VisitedPages visited_pages(int n, int sink, int window) {
+  const int nb = (n + kBS - 1) / kBS;
+  if constexpr (!WIN) {
+    return {nb, nb, nb};
+  } else {
+    const int c = max(0, n - window) / kBS;
+    const int a = min((min(sink, n) + kBS - 1) / kBS, c);
+    return {a, c, nb};
+  }
+}
+
+// Exclusive prefix sums of the pages each request reads into s_pref[0..B]
+// (256 threads).
+template <bool WIN>
 __device__ inline void block_prefix_blocks(int32_t* s_pref, int32_t* s_tmp, const int32_t* ctx_lens, int B,
-                                           int max_ctx) {
+                                           int max_ctx, int sink, int window) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int32_t carry = 0;
   for (int base = 0; base < B; base += 256) {
     const int b = base + tid;
-    const int32_t v = b < B ? (clamp_ctx(ctx_lens, b, max_ctx) + kBS - 1) / kBS : 0;
+    const int32_t v = b < B ? visited_pages<WIN>(clamp_ctx(ctx_lens, b, max_ctx), sink, window).count() : 0;
     int32_t x = v;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -349,7 +402,11 @@ __device__ inline void block_prefix_blocks(int32_t* s_pref, int32_t* s_tmp, cons
 // that ends the request), so no wave reads the slot being written; threads of
 // the same launch store the token into the cache while the block counts are
 // summed.
-template <bool FP8, int D, bool APPEND>
+//
+// WIN: a sliding window of `window` tokens plus `sink` sink tokens; units
+// run over the pages each request reads (visited_pages), so pages outside
+// are never touched and may be free.
+template <bool FP8, int D, bool APPEND, bool WIN>
 __global__ void __launch_bounds__(256, 3)
 decode_stream_kernel(void* __restrict__ kc_, void* __restrict__ vc_,
                      const float* __restrict__ kscale, const float* __restrict__ vscale,
@@ -359,7 +416,8 @@ decode_stream_kernel(void* __restrict__ kc_, void* __restrict__ vc_,
                      int G, int n_hgroups, int HS, float scale_log2, int chunk_fixed,
                      float* __restrict__ ws_ml, float* __restrict__ ws_acc,
                      int32_t* __restrict__ ws_pref, const uint16_t* __restrict__ k_new,
-                     const uint16_t* __restrict__ v_new, const int32_t* __restrict__ new_slots) {
+                     const uint16_t* __restrict__ v_new, const int32_t* __restrict__ new_slots, int sink,
+                     int window) {
   constexpr int T8 = D / 16;
   __shared__ int32_t s_pref[kMaxStreamB + 1];
   __shared__ int32_t s_tmp[4];
@@ -376,7 +434,7 @@ decode_stream_kernel(void* __restrict__ kc_, void* __restrict__ vc_,
     kx = ld16(k_new + int64_t(piece) * 8);
     vx = ld16(v_new + int64_t(piece) * 8);
   }
-  block_prefix_blocks(s_pref, s_tmp, ctx_lens, B, max_ctx);
+  block_prefix_blocks<WIN>(s_pref, s_tmp, ctx_lens, B, max_ctx, sink, window);
   if constexpr (APPEND) {
     uint16_t* kw = static_cast<uint16_t*>(kc_);
     uint16_t* vw = static_cast<uint16_t*>(vc_);
@@ -453,7 +511,21 @@ decode_stream_kernel(void* __restrict__ kc_, void* __restrict__ vc_,
 #pragma unroll
       for (int t = 0; t < T8; ++t) st.acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int ctx = clamp_ctx(ctx_lens, b, max_ctx);
-      if constexpr (APPEND) {
+      if constexpr (WIN) {
+        // read positions [0, sink) and [ctx - window, ctx); visited pages
+        // [j, j1) map to logical [0, a) then [c, nb)
+        const VisitedPages vp = visited_pages<true>(ctx, sink, window);
+        const int win_lo = max(0, ctx - window);
+#pragma clang loop unroll(disable)
+        for (int part = 0; part < 2; ++part) {
+          const int lo = part == 0 ? j : max(j, vp.a);
+          const int hi = part == 0 ? min(j1, vp.a) : j1;
+          const int off = part == 0 ? 0 : vp.c - vp.a;
+          if (lo < hi)
+            run_segment<FP8, D, true>(st, kc, vc, kscale, vscale, tables + int64_t(b) * max_blocks, ctx, H, g,
+                                      lo + off, hi + off, scale_log2, qv, r, grp, sink, win_lo);
+        }
+      } else if constexpr (APPEND) {
         // the cache holds positions < ctx - 1; a segment cut down to nothing
         // is the request's last block holding only the new token
         const bool app = new_slots[b] >= 0;  // ctx > 0 here: b has blocks
@@ -507,19 +579,19 @@ decode_stream_kernel(void* __restrict__ kc_, void* __restrict__ vc_,
 
 // Merge the pieces of one (request, query head) left by decode_stream_kernel.
 // grid (h_q, B), 256 threads = (256 / (D/4)) piece lanes x D/4 dimension quads.
-template <int D>
+template <int D, bool WIN>
 __global__ void __launch_bounds__(256)
 stream_reduce_kernel(uint16_t* __restrict__ out, const float* __restrict__ ws_ml,
                      const float* __restrict__ ws_acc, const int32_t* __restrict__ ws_pref,
                      const int32_t* __restrict__ ctx_lens, int B, int max_ctx, int h_q, int G,
-                     int n_hgroups, int H, int HS, int workers, int chunk_fixed) {
+                     int n_hgroups, int H, int HS, int workers, int chunk_fixed, int sink, int window) {
   constexpr int DQ = D / 4;
   constexpr int PL = 256 / DQ;
   __shared__ float s_m[PL], s_l[PL];
   __shared__ __attribute__((aligned(16))) float s_a[PL][D];
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int64_t row = int64_t(b) * h_q + h;
-  const int nb = (clamp_ctx(ctx_lens, b, max_ctx) + kBS - 1) / kBS;
+  const int nb = visited_pages<WIN>(clamp_ctx(ctx_lens, b, max_ctx), sink, window).count();
   if (nb == 0) {
     if (tid < D) out[row * D + tid] = 0;
     return;
@@ -812,25 +884,40 @@ int launch_decode_d(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(a.workers / 4);
   auto* q = static_cast<const uint16_t*>(a.q);
   auto* out = static_cast<uint16_t*>(a.out);
+  const float* ks = d.cache_dtype == KV_FP8_E4M3 ? a.pool->k_scale + so : nullptr;
+  const float* vs = d.cache_dtype == KV_FP8_E4M3 ? a.pool->v_scale + so : nullptr;
+  const bool win = a.window > 0;
   if (d.cache_dtype == KV_BF16 && a.new_slots)
-    decode_stream_kernel<false, D, true><<<grid, 256, 0, s>>>(
+    decode_stream_kernel<false, D, true, false><<<grid, 256, 0, s>>>(
         kc, vc, nullptr, nullptr, q, out, a.tables, a.max_blocks, a.ctx, a.B, a.max_ctx, H, a.h_q, G, nhg,
         a.hs, sl, a.chunk, a.ws_ml, a.ws_acc, a.ws_pref, static_cast<const uint16_t*>(a.k_new),
-        static_cast<const uint16_t*>(a.v_new), a.new_slots);
-  else if (d.cache_dtype == KV_BF16)
-    decode_stream_kernel<false, D, false><<<grid, 256, 0, s>>>(
+        static_cast<const uint16_t*>(a.v_new), a.new_slots, 0, 0);
+  else if (d.cache_dtype == KV_BF16 && win)
+    decode_stream_kernel<false, D, false, true><<<grid, 256, 0, s>>>(
         kc, vc, nullptr, nullptr, q, out, a.tables, a.max_blocks, a.ctx, a.B, a.max_ctx, H, a.h_q, G, nhg,
-        a.hs, sl, a.chunk, a.ws_ml, a.ws_acc, a.ws_pref, nullptr, nullptr, nullptr);
+        a.hs, sl, a.chunk, a.ws_ml, a.ws_acc, a.ws_pref, nullptr, nullptr, nullptr, a.sink, a.window);
+  else if (d.cache_dtype == KV_BF16)
+    decode_stream_kernel<false, D, false, false><<<grid, 256, 0, s>>>(
+        kc, vc, nullptr, nullptr, q, out, a.tables, a.max_blocks, a.ctx, a.B, a.max_ctx, H, a.h_q, G, nhg,
+        a.hs, sl, a.chunk, a.ws_ml, a.ws_acc, a.ws_pref, nullptr, nullptr, nullptr, 0, 0);
+  else if (win)
+    decode_stream_kernel<true, D, false, true><<<grid, 256, 0, s>>>(
+        kc, vc, ks, vs, q, out, a.tables, a.max_blocks, a.ctx, a.B, a.max_ctx, H, a.h_q, G, nhg, a.hs, sl,
+        a.chunk, a.ws_ml, a.ws_acc, a.ws_pref, nullptr, nullptr, nullptr, a.sink, a.window);
   else
-    decode_stream_kernel<true, D, false><<<grid, 256, 0, s>>>(
-        kc, vc, a.pool->k_scale + so, a.pool->v_scale + so, q, out, a.tables, a.max_blocks, a.ctx, a.B,
-        a.max_ctx, H, a.h_q, G, nhg, a.hs, sl, a.chunk, a.ws_ml, a.ws_acc, a.ws_pref, nullptr, nullptr,
-        nullptr);
+    decode_stream_kernel<true, D, false, false><<<grid, 256, 0, s>>>(
+        kc, vc, ks, vs, q, out, a.tables, a.max_blocks, a.ctx, a.B, a.max_ctx, H, a.h_q, G, nhg, a.hs, sl,
+        a.chunk, a.ws_ml, a.ws_acc, a.ws_pref, nullptr, nullptr, nullptr, 0, 0);
   e = hipGetLastError();
   if (e != hipSuccess) return fail(KV_E_HIP, "decode launch: %s", hipGetErrorString(e));
-  stream_reduce_kernel<D><<<dim3(a.h_q, a.B), 256, 0, s>>>(out, a.ws_ml, a.ws_acc, a.ws_pref, a.ctx, a.B,
-                                                           a.max_ctx, a.h_q, G, nhg, H, a.hs, a.workers,
-                                                           a.chunk);
+  if (win)
+    stream_reduce_kernel<D, true><<<dim3(a.h_q, a.B), 256, 0, s>>>(
+        out, a.ws_ml, a.ws_acc, a.ws_pref, a.ctx, a.B, a.max_ctx, a.h_q, G, nhg, H, a.hs, a.workers, a.chunk,
+        a.sink, a.window);
+  else
+    stream_reduce_kernel<D, false><<<dim3(a.h_q, a.B), 256, 0, s>>>(
+        out, a.ws_ml, a.ws_acc, a.ws_pref, a.ctx, a.B, a.max_ctx, a.h_q, G, nhg, H, a.hs, a.workers, a.chunk,
+        0, 0);
   e = hipGetLastError();
   if (e != hipSuccess) return fail(KV_E_HIP, "decode reduce launch: %s", hipGetErrorString(e));
   return ok();

@@ -115,6 +115,10 @@ struct DecodeArgs {
   const void* k_new;
   const void* v_new;
   const int32_t* new_slots;
+  // bf16/fp8 sliding-window decode: positions [0, sink) and the last `window`
+  // are read (window 0: every position)
+  int32_t sink;
+  int32_t window;
 };
 
 // Fills the plan for a decode of this shape (pointers excluded) and returns

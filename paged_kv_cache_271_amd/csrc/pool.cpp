@@ -366,6 +366,65 @@ int paged_attention_decode_append(kv_pool* p, int32_t layer, void* out, const vo
   return launch_decode(a, s);
 }
 
+int paged_attention_decode_window(kv_pool* p, int32_t layer, void* out, const void* q, int32_t q_dtype,
+                                  const int32_t* tables, int32_t max_blocks, const int32_t* ctx, int32_t B,
+                                  int32_t h_q, int32_t max_ctx, float scale, int32_t sink, int32_t window,
+                                  int32_t part, void* ws, int64_t ws_bytes, void* stream) {
+  if (p && p->desc.cache_dtype == KV_F32)
+    return fail(KV_E_UNSUPPORTED, "sliding-window decode is built for bf16 and fp8 pools");
+  if (sink < 0 || window < 1)
+    return fail(KV_E_INVALID, "sink %d must be >= 0 and window %d >= 1", sink, window);
+  DecodeArgs a{};
+  const int st = prepare_decode(p, layer, out, q, q_dtype, tables, max_blocks, ctx, B, h_q, max_ctx, scale,
+                                part, ws, ws_bytes, &a);
+  if (st != KV_OK) return st;
+  if (B == 0) return ok();
+  a.sink = sink;
+  a.window = window;
+  return launch_decode(a, static_cast<hipStream_t>(stream));
+}
+
+int kv_window_release(kv_pool* p, int32_t B, int32_t* table, int32_t max_blocks, const int32_t* lens,
+                      int32_t sink, int32_t window, int32_t* n_released) {
+  if (!p || !n_released) return fail(KV_E_INVALID, "NULL argument");
+  if (B < 0 || max_blocks < 0) return fail(KV_E_INVALID, "negative size");
+  if (sink < 0 || window < 1)
+    return fail(KV_E_INVALID, "sink %d must be >= 0 and window %d >= 1", sink, window);
+  *n_released = 0;
+  if (B == 0) return ok();
+  if (!table || !lens) return fail(KV_E_INVALID, "NULL array");
+  const int32_t bs = p->desc.block_size;
+  // check everything first (a block may be dropped by several tables, at most
+  // as often as it is mapped): nothing changes on an error
+  std::unordered_map<int32_t, int32_t> drops;
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t n = lens[b];
+    if (n < 0 || kv_blocks_for_tokens(n, bs) > max_blocks)
+      return fail(KV_E_INVALID, "request %d: length %d outside a table of %d blocks", b, n, max_blocks);
+    const int32_t* row = table + int64_t(b) * max_blocks;
+    for (int32_t j = 0; int64_t(j + 1) * bs <= int64_t(n) - window; ++j) {
+      if (int64_t(j) * bs < sink || row[j] == -1) continue;
+      if (!block_live(p, row[j]) || ++drops[row[j]] > p->rc[row[j]])
+        return fail(KV_E_BAD_BLOCK, "request %d: block %d (page %d) out of range, free or over-released", b,
+                    row[j], j);
+    }
+  }
+  int32_t released = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    int32_t* row = table + int64_t(b) * max_blocks;
+    // dead pages: every position at or past the sinks and before n - window
+    for (int32_t j = 0; int64_t(j + 1) * bs <= int64_t(lens[b]) - window; ++j) {
+      if (int64_t(j) * bs < sink || row[j] == -1) continue;
+      const int32_t blk = row[j];
+      if (--p->rc[blk] == 0) p->stack.push_back(blk);
+      row[j] = -1;
+      ++released;
+    }
+  }
+  *n_released = released;
+  return ok();
+}
+
 const char* kv_status_string(int s) {
   switch (s) {
     case KV_OK: return "KV_OK";

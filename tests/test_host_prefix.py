@@ -177,3 +177,75 @@ def test_reserve_cow_bit_exact(seed):
             assert pk.kv_block_alloc(h) == alloc.alloc()
     finally:
         pk.kv_pool_destroy(h)
+
+
+# ------------------------------------------------------------ window release --
+@settings(max_examples=60, deadline=None)
+@given(seed=st.integers(0, 2 ** 31 - 1))
+def test_window_release_bit_exact(seed):
+    """Requests (some sharing their first pages) of random lengths drop their
+    dead pages; table edits, counts, released totals and the free stack match
+    the oracle, over two rounds of growth."""
+    lib = pk.load_library()
+    rng = np.random.default_rng(seed)
+    n = 60
+    order = rng.permutation(n)
+    h = make_pool(lib, n, order)
+    alloc = oracle.RefAllocator(n, order)
+    try:
+        B, MB = int(rng.integers(1, 5)), 12
+        sink, win = int(rng.integers(0, 40)), int(rng.integers(1, 80))
+        table = np.full((B, MB), -1, np.int32)
+        rows = [[] for _ in range(B)]
+        lens = np.zeros(B, np.int32)
+        shared = []
+        for _ in range(int(rng.integers(0, 3))):       # a shared first part
+            b = alloc.alloc()
+            assert pk.kv_block_alloc(h) == b
+            shared.append(b)
+        for r in range(B):
+            rows[r] = list(shared)
+            if r:
+                for b in shared:
+                    alloc.retain(b)
+                    pk.kv_block_retain(h, b)
+        for rnd in range(2):
+            for r in range(B):
+                # grow past the shared pages by 0..59 tokens
+                t = min(MB * 16, max(int(lens[r]), 16 * len(shared)) + int(rng.integers(0, 60)))
+                while 16 * len(rows[r]) < t:
+                    b = alloc.alloc()
+                    assert pk.kv_block_alloc(h) == b
+                    rows[r].append(b)
+                lens[r] = t
+                table[r, :len(rows[r])] = rows[r]
+            want = oracle.window_release(alloc, rows, [int(x) for x in lens], sink, win)
+            got = pk.kv_window_release(h, table, lens, sink, win)
+            assert got == want
+            for r in range(B):
+                assert list(table[r, :len(rows[r])]) == rows[r]
+            same_state(h, alloc, n)
+        while alloc.num_free():
+            assert pk.kv_block_alloc(h) == alloc.alloc()
+    finally:
+        pk.kv_pool_destroy(h)
+
+
+def test_window_release_errors_change_nothing(lib):
+    h = make_pool(lib, 8, range(8))
+    try:
+        a, b = pk.kv_block_alloc(h), pk.kv_block_alloc(h)
+        # one block listed by two tables but mapped once: over-release
+        table = np.array([[a, b, -1], [a, b, -1]], np.int32)
+        lens = np.array([40, 40], np.int32)
+        with pytest.raises(pk.KVError, match="BAD_BLOCK"):
+            pk.kv_window_release(h, table, lens, 0, 8)
+        assert pk.kv_block_refcount(h, a) == 1 and table[0, 0] == a and table[1, 0] == a
+        with pytest.raises(pk.KVError, match="INVALID"):
+            pk.kv_window_release(h, table, lens, 0, 0)          # window must be >= 1
+        with pytest.raises(pk.KVError, match="INVALID"):
+            pk.kv_window_release(h, table[:, :2].copy(), lens, 0, 8)   # 40 tokens need 3 pages
+        # sinks keep page 0; the window keeps the last 8 of 40: page 1 (16..31) is dead
+        assert pk.kv_window_release(h, table[:1].copy(), lens[:1], 4, 8) == 1
+    finally:
+        pk.kv_pool_destroy(h)
