@@ -38,8 +38,9 @@ sys.path.insert(0, ROOT)
 METRIC = "paged decode-attention KV GB/s (% of HBM peak) + µs/step, Llama-3-8B shape"
 HBM_PEAK_GBS = 8000.0
 EVENT_EVERY = 8
-DEFAULT_LAYERS = {"llama3_8b": 32, "llama3_70b_long": 8, "fp8": 16}
-DEFAULT_SEED = {"llama3_8b": 2, "llama3_70b_long": 3, "fp8": 5, "prefix_churn": 4, "cow_fork": 6}
+DEFAULT_LAYERS = {"llama3_8b": 32, "llama3_70b_long": 8, "fp8": 16, "llama3_8b_window": 4}
+DEFAULT_SEED = {"llama3_8b": 2, "llama3_70b_long": 3, "fp8": 5, "prefix_churn": 4, "cow_fork": 6,
+                "llama3_8b_window": 7}
 
 # HBM bytes (read + written) per launch of decode_stream_kernel in the default
 # step of each workload, from the rocprofv3 FETCH_SIZE and WRITE_SIZE runs in
@@ -67,7 +68,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=1024)
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--workload", default="llama3_8b",
-                    choices=["llama3_8b", "llama3_70b_long", "fp8", "prefix_churn", "cow_fork"])
+                    choices=["llama3_8b", "llama3_70b_long", "fp8", "prefix_churn", "cow_fork",
+                             "llama3_8b_window"])
     ap.add_argument("--layers", type=int, default=0, help="layers in the pool (0: workload default)")
     ap.add_argument("--seed", type=int, default=-1, help="input seed (-1: workload default)")
     ap.add_argument("--partition", type=int, default=0,
@@ -174,6 +176,14 @@ def decode_workload(args, torch, synth, pk, dev):
         del k, v
     torch.cuda.synchronize()
     log("prefill done")
+    sink, window = w.get("sink", 0), w.get("window", 0)
+    if window:   # pages no windowed decode reads go back to the pool
+        freed = pool.window_release(table, lens, sink, window)
+        log(f"window {window} + {sink} sinks: {freed} pages released, {pool.num_free()} free")
+
+    def read_tokens(n):
+        n = n.astype(np.int64)
+        return n if not window else np.minimum(n, np.minimum(n, sink) + window)
 
     # per (model step, layer) new-token K/V and queries, resident before timing
     k_new = synth.device_normal((model_steps, L, B, H, D), 7, dev, in_dt, outlier, 8.0)
@@ -191,6 +201,8 @@ def decode_workload(args, torch, synth, pk, dev):
 
     def host_reserve():
         slots = pool.batch_reserve(table, lens, np.ones(B, np.int32))
+        if window:
+            pool.window_release(table, lens, sink, window)
         pinned = torch.empty(B * MB + 2 * B, dtype=torch.int32, pin_memory=True)
         pn = pinned.numpy()
         pn[:B * MB] = table.reshape(-1)
@@ -201,11 +213,11 @@ def decode_workload(args, torch, synth, pk, dev):
         d_lens.copy_(dev_buf[B * MB:B * MB + B])
         d_slots.copy_(dev_buf[B * MB + B:])
         state["max_ctx"] = int(lens.max())
-        state["kv"] = int(lens.astype(np.int64).sum()) * H * D * elem * 2
+        state["kv"] = int(read_tokens(lens).sum()) * H * D * elem * 2
 
     # fp8 pools have no fused kernel (the append re-quantises whole tiles), so
     # their step is always the two calls, with the decode alone between events
-    two_calls = args.two_calls or dtype == "fp8"
+    two_calls = args.two_calls or dtype == "fp8" or bool(window)
 
     def step(i, ev=None):
         s, r = divmod(i, L)
@@ -215,7 +227,10 @@ def decode_workload(args, torch, synth, pk, dev):
             pool.append(r, k_new[s, r], v_new[s, r], d_slots)
         if ev is not None:
             ev[0].record(stream)
-        if two_calls:
+        if window:
+            pool.decode_window(r, q_all[s, r], d_table, d_lens, state["max_ctx"], scale, sink, window,
+                               args.partition, out=out, workspace=ws)
+        elif two_calls:
             pool.decode(r, q_all[s, r], d_table, d_lens, state["max_ctx"], scale, args.partition,
                         out=out, workspace=ws)
         else:
@@ -254,11 +269,13 @@ def decode_workload(args, torch, synth, pk, dev):
         "cache_dtype": dtype, "batch": B, "h_q": h_q, "h_kv": H, "head_dim": D, "block_size": 16,
         "contexts": (list(w["contexts"]) if "contexts" in w else {"uniform": list(w["ctx_range"])}),
         "layers_in_pool": L, "partition_tokens": args.partition,
+        **({"sink_tokens": sink, "window_tokens": window} if window else {}),
         "step": "kv_append + paged_attention_decode" if two_calls else "paged_attention_decode_append",
     }
     return dict(wall=wall, kv_total=float(sum(per_step_kv)), dec_ms=dec_ms, dec_kv=dec_kv,
                 config=config, cpu=cpu, traffic=measured_traffic(name, two_calls), dtype="bf16" if dtype != "fp8" else "fp8-e4m3 K/V, bf16 q",
-                kernel=("paged_attention_decode" if two_calls else "paged_attention_decode_append")
+                kernel=("paged_attention_decode_window" if window else
+                        "paged_attention_decode" if two_calls else "paged_attention_decode_append")
                 + " call (decode_stream_kernel + stream_reduce_kernel)")
 
 

@@ -47,6 +47,9 @@ WORKLOADS = {
     "prefix_churn": dict(dtype="bf16", num_layers=32, h_q=32, h_kv=8, head_dim=128,
                          batch=256, prefix_tokens=2000, suffix_range=(5, 500),
                          steps=64, churn=26, partition_tokens=512),
+    "llama3_8b_window": dict(dtype="bf16", num_layers=1, h_q=32, h_kv=8, head_dim=128,
+                             batch=64, ctx_range=(8192, 16384), sink=4, window=4096,
+                             partition_tokens=512),
     "fp8": dict(dtype="fp8", num_layers=1, h_q=32, h_kv=8, head_dim=128,
                 batch=128, ctx_range=(1024, 8192), outlier_p=0.01,
                 outlier_mul=8.0, partition_tokens=512),
