@@ -33,6 +33,7 @@ from .fp8 import (E4M3_MAX, e4m3_decode, e4m3_encode, e4m3_value_table,
                   quantize_run)
 from .attention import (attention_fp64, attention_bruteforce, partitioned_fp64,
                         partition_states, combine_partitions, decode_batch_fp64)
+from .int8 import INT8_MAX, int8_encode, int8_decode, quantize_run_int8
 from .prefix_cache import RefPrefixCache, reserve_cow
 from .window import (window_positions, attention_window_fp64, dead_pages, window_cache_bytes,
                      window_release)
@@ -46,6 +47,7 @@ __all__ = [
     "E4M3_MAX", "e4m3_decode", "e4m3_encode", "e4m3_value_table", "quantize_run",
     "attention_fp64", "attention_bruteforce", "partitioned_fp64",
     "partition_states", "combine_partitions", "decode_batch_fp64",
+    "INT8_MAX", "int8_encode", "int8_decode", "quantize_run_int8",
     "RefPrefixCache", "reserve_cow",
     "window_positions", "attention_window_fp64", "dead_pages", "window_cache_bytes", "window_release",
 ]

@@ -22,7 +22,8 @@ Readings taken where the pages are silent:
       K: [num_blocks][num_kv_heads][block_size][head_dim]   (token-major tile)
       V: [num_blocks][num_kv_heads][head_dim][block_size]   (dim-major tile)
   so each (block, kv-head) tile of K and of V is one contiguous run of bytes.
-  fp8 pools also hold one fp32 scale per (block, kv-head) for K and for V.
+  fp8 and int8 pools also hold one fp32 scale per (block, kv-head) for K and
+  for V.
 * Writing a token into a page mapped by more than one table is refused (the
   library answers KV_E_SHARED); the slot mapping raises SharedBlockWrite.
 * A slot of -1 means "skip this token".
@@ -31,6 +32,7 @@ Readings taken where the pages are silent:
 import numpy as np
 
 from .fp8 import e4m3_decode, quantize_run
+from .int8 import int8_decode, quantize_run_int8
 from .allocator import BadBlock
 
 
@@ -113,7 +115,8 @@ class RefPool:
     """Byte-level model of the device pool (all layers).
 
     dtype: "f32" (inputs float32), "bf16" (inputs bf16 bits),
-           "fp8" (inputs bf16 bits, stored as E4M3 codes plus scales).
+           "fp8" (inputs bf16 bits, stored as E4M3 codes plus scales),
+           "int8" (inputs bf16 bits, stored as symmetric int8 codes plus scales).
     """
 
     def __init__(self, num_layers, num_blocks, num_kv_heads, head_dim,
@@ -122,12 +125,12 @@ class RefPool:
         self.L, self.N, self.H, self.D, self.bs = (num_layers, num_blocks,
                                                    num_kv_heads, head_dim, block_size)
         self.dtype = dtype
-        np_t = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[dtype]
+        np_t = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8, "int8": np.int8}[dtype]
         kshape = (num_layers, num_blocks, num_kv_heads, block_size, head_dim)
         vshape = (num_layers, num_blocks, num_kv_heads, head_dim, block_size)
         self.K = np.zeros(kshape, np_t) if k_init is None else np.array(k_init, np_t).reshape(kshape)
         self.V = np.zeros(vshape, np_t) if v_init is None else np.array(v_init, np_t).reshape(vshape)
-        if dtype == "fp8":
+        if dtype in ("fp8", "int8"):
             sshape = (num_layers, num_blocks, num_kv_heads)
             self.Ks = np.zeros(sshape, np.float32) if k_scale_init is None \
                 else np.array(k_scale_init, np.float32).reshape(sshape)
@@ -142,7 +145,7 @@ class RefPool:
         slots = [int(s) for s in slots]
         k_new = np.asarray(k_new)
         v_new = np.asarray(v_new)
-        if self.dtype != "fp8":
+        if self.dtype not in ("fp8", "int8"):
             for t, s in enumerate(slots):
                 if s < 0:
                     continue
@@ -150,7 +153,8 @@ class RefPool:
                 self.K[layer, blk, :, off, :] = k_new[t]
                 self.V[layer, blk, :, :, off] = v_new[t]
             return
-        # fp8: group consecutive tokens that land in the same block into runs
+        # fp8 / int8: group consecutive tokens that land in the same block into runs
+        qrun = quantize_run if self.dtype == "fp8" else quantize_run_int8
         t = 0
         T = len(slots)
         while t < T:
@@ -168,14 +172,14 @@ class RefPool:
             vx = _raw_to_f32(v_new[run], "bf16")
             for g in range(self.H):
                 # K tile [bs][D]
-                codes, tile, s1 = quantize_run(kx[:, g, :], self.K[layer, blk, g],
+                codes, tile, s1 = qrun(kx[:, g, :], self.K[layer, blk, g],
                                                self.Ks[layer, blk, g], first)
                 tile[offs] = codes
                 self.K[layer, blk, g] = tile
                 self.Ks[layer, blk, g] = s1
                 # V tile is stored [D][bs]; quantise in [bs][D] view
                 vt = self.V[layer, blk, g].T.copy()
-                codes, vt, s1 = quantize_run(vx[:, g, :], vt, self.Vs[layer, blk, g], first)
+                codes, vt, s1 = qrun(vx[:, g, :], vt, self.Vs[layer, blk, g], first)
                 vt[offs] = codes
                 self.V[layer, blk, g] = vt.T
                 self.Vs[layer, blk, g] = s1
@@ -197,10 +201,11 @@ class RefPool:
     def gather_f64(self, layer, table_row, n):
         """Values the attention reads for the first n positions, float64."""
         kr, vr = self.gather_raw(layer, table_row, n)
-        if self.dtype != "fp8":
+        if self.dtype not in ("fp8", "int8"):
             return raw_to_f64(kr, self.dtype), raw_to_f64(vr, self.dtype)
         ksc = np.array([self.Ks[layer, int(table_row[p // self.bs])] for p in range(n)],
                        dtype=np.float64).reshape(n, self.H, 1)
         vsc = np.array([self.Vs[layer, int(table_row[p // self.bs])] for p in range(n)],
                        dtype=np.float64).reshape(n, self.H, 1)
-        return e4m3_decode(kr) * ksc, e4m3_decode(vr) * vsc
+        dec = e4m3_decode if self.dtype == "fp8" else int8_decode
+        return dec(kr) * ksc, dec(vr) * vsc
