@@ -14,10 +14,13 @@ so each step reads a layer whose K/V was last touched `layers - 1` steps
 earlier, far beyond the 256 MB last-level cache, as in a real decode step.
 
 Other workloads (--workload) are measured the same way: llama3_70b_long
-(h_q 64, 4 requests of 32k-128k tokens), fp8 (E4M3 cache, 128 requests of
-1k-8k tokens with x8 outliers) and prefix_churn (32 layers x 256 requests
-sharing a 2000-token prefix, 26 retired and admitted per step; a step there
-is one model step over all 32 layers).
+(h_q 64, 4 requests of 32k-128k tokens), fp8 and int8 (8-bit caches, 128
+requests of 1k-8k tokens with x8 outliers), llama3_8b_window (64 requests of
+8k-16k tokens read through a 4096-token window plus 4 sink tokens, dead
+pages released), prefix_churn (32 layers x 256 requests sharing a
+2000-token prefix found in the prefix cache, 26 retired and admitted per
+step; a step there is one model step over all 32 layers) and cow_fork
+(copy-on-write page copies of 256 forks over 32 layers).
 
 Prints one JSON line.  `value` is KV GB/s: K+V bytes of the valid tokens read
 by the decodes of the timed steps over their wall time.
@@ -38,8 +41,8 @@ sys.path.insert(0, ROOT)
 METRIC = "paged decode-attention KV GB/s (% of HBM peak) + µs/step, Llama-3-8B shape"
 HBM_PEAK_GBS = 8000.0
 EVENT_EVERY = 8
-DEFAULT_LAYERS = {"llama3_8b": 32, "llama3_70b_long": 8, "fp8": 16, "llama3_8b_window": 4}
-DEFAULT_SEED = {"llama3_8b": 2, "llama3_70b_long": 3, "fp8": 5, "prefix_churn": 4, "cow_fork": 6,
+DEFAULT_LAYERS = {"llama3_8b": 32, "llama3_70b_long": 8, "fp8": 16, "int8": 16, "llama3_8b_window": 4}
+DEFAULT_SEED = {"llama3_8b": 2, "llama3_70b_long": 3, "fp8": 5, "int8": 5, "prefix_churn": 4, "cow_fork": 6,
                 "llama3_8b_window": 7}
 
 # HBM bytes (read + written) per launch of decode_stream_kernel in the default
@@ -68,7 +71,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=1024)
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--workload", default="llama3_8b",
-                    choices=["llama3_8b", "llama3_70b_long", "fp8", "prefix_churn", "cow_fork",
+                    choices=["llama3_8b", "llama3_70b_long", "fp8", "int8", "prefix_churn", "cow_fork",
                              "llama3_8b_window"])
     ap.add_argument("--layers", type=int, default=0, help="layers in the pool (0: workload default)")
     ap.add_argument("--seed", type=int, default=-1, help="input seed (-1: workload default)")
@@ -145,7 +148,7 @@ def decode_workload(args, torch, synth, pk, dev):
     dtype = w["dtype"]
     B, H, h_q, D = w["batch"], w["h_kv"], w["h_q"], w["head_dim"]
     L = args.layers or DEFAULT_LAYERS[name]
-    elem = 1 if dtype == "fp8" else 2
+    elem = 1 if dtype in ("fp8", "int8") else 2
     outlier = w.get("outlier_p", 0.0)
     total = args.warmup + args.steps
     model_steps = (total + L - 1) // L
@@ -215,9 +218,10 @@ def decode_workload(args, torch, synth, pk, dev):
         state["max_ctx"] = int(lens.max())
         state["kv"] = int(read_tokens(lens).sum()) * H * D * elem * 2
 
-    # fp8 pools have no fused kernel (the append re-quantises whole tiles), so
-    # their step is always the two calls, with the decode alone between events
-    two_calls = args.two_calls or dtype == "fp8" or bool(window)
+    # fp8 and int8 pools have no fused kernel (the append re-quantises whole
+    # tiles), nor has the windowed decode, so their step is always the two
+    # calls, with the decode alone between events
+    two_calls = args.two_calls or dtype in ("fp8", "int8") or bool(window)
 
     def step(i, ev=None):
         s, r = divmod(i, L)
@@ -273,7 +277,7 @@ def decode_workload(args, torch, synth, pk, dev):
         "step": "kv_append + paged_attention_decode" if two_calls else "paged_attention_decode_append",
     }
     return dict(wall=wall, kv_total=float(sum(per_step_kv)), dec_ms=dec_ms, dec_kv=dec_kv,
-                config=config, cpu=cpu, traffic=measured_traffic(name, two_calls), dtype="bf16" if dtype != "fp8" else "fp8-e4m3 K/V, bf16 q",
+                config=config, cpu=cpu, traffic=measured_traffic(name, two_calls), dtype={"fp8": "fp8-e4m3 K/V, bf16 q", "int8": "int8 K/V, bf16 q"}.get(dtype, "bf16"),
                 kernel=("paged_attention_decode_window" if window else
                         "paged_attention_decode" if two_calls else "paged_attention_decode_append")
                 + " call (decode_stream_kernel + stream_reduce_kernel)")

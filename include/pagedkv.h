@@ -15,7 +15,7 @@
  *    inferensys.com, PagedAttention block management).
  *  - Several query heads may share one KV head (GQA; MQA when there is a single
  *    KV head) ("KV Cache" glossary, GQA and MQA entries).
- *  - The cache may be held in fp8 E4M3 to halve its bytes (askaiml page, §7
+ *  - The cache may be held in fp8 E4M3 or INT8 to halve its bytes (askaiml page, §7
  *    "KV cache quantisation").
  *
  * Conventions for every function:
@@ -39,9 +39,10 @@
  * Pool layout in device memory, one array for K and one for V, each indexed
  *   K: [num_layers][num_blocks][num_kv_heads][block_size][head_dim]  token-major
  *   V: [num_layers][num_blocks][num_kv_heads][head_dim][block_size]  dim-major
- * Element type: float (KV_F32), bfloat16 (KV_BF16) or E4M3 code bytes
- * (KV_FP8_E4M3).  Each (block, kv-head) tile of K and of V is contiguous.
- * fp8 pools also take two fp32 scale arrays [num_layers][num_blocks][num_kv_heads],
+ * Element type: float (KV_F32), bfloat16 (KV_BF16), E4M3 code bytes
+ * (KV_FP8_E4M3) or symmetric int8 codes (KV_INT8).  Each (block, kv-head) tile
+ * of K and of V is contiguous.
+ * fp8 and int8 pools also take two fp32 scale arrays [num_layers][num_blocks][num_kv_heads],
  * one for K and one for V; a stored element means decode(code) * scale.
  * Supported: block_size 16, head_dim 64 or 128.
  */
@@ -56,7 +57,7 @@ extern "C" {
 
 typedef struct kv_pool kv_pool; /* opaque; holds host allocator state only */
 
-typedef enum { KV_F32 = 0, KV_BF16 = 1, KV_FP8_E4M3 = 2 } kv_dtype;
+typedef enum { KV_F32 = 0, KV_BF16 = 1, KV_FP8_E4M3 = 2, KV_INT8 = 3 } kv_dtype;
 
 typedef enum {
   KV_OK = 0,
@@ -81,7 +82,7 @@ typedef struct {
 /* ---------------------------------------------------------------- sizes -- */
 
 /* Bytes of K plus V one token occupies across all layers:
- * 2 * num_layers * num_kv_heads * head_dim * element bytes (fp8 scales not
+ * 2 * num_layers * num_kv_heads * head_dim * element bytes (fp8 / int8 scales not
  * included) -- the per-token memory formula of the askaiml page, §2
  * "Memory cost".  Returns -1 for an invalid descriptor. */
 int64_t kv_bytes_per_token(const kv_pool_desc* desc);
@@ -92,14 +93,14 @@ int64_t kv_bytes_per_token(const kv_pool_desc* desc);
 int32_t kv_blocks_for_tokens(int32_t n, int32_t block_size);
 
 /* Bytes the caller must allocate for the K array (the V array is the same
- * size) and for each fp8 scale array (0 for non-fp8 pools).  Either output
+ * size) and for each scale array (fp8 and int8 pools; 0 otherwise).  Either output
  * pointer may be NULL. */
 int kv_pool_buffer_bytes(const kv_pool_desc* desc, int64_t* cache_bytes, int64_t* scale_bytes);
 
 /* ----------------------------------------------------------------- pool -- */
 
 /* Create a pool over caller-owned device arrays (layout above).  k_scale and
- * v_scale are device fp32 arrays for fp8 pools and must be NULL otherwise.
+ * v_scale are device fp32 arrays for fp8 and int8 pools and must be NULL otherwise.
  * initial_free_order: host array of num_blocks distinct ids (a permutation of
  * 0..num_blocks-1) giving the order in which a fresh pool hands blocks out
  * (first kv_block_alloc returns initial_free_order[0]); NULL means 0,1,2,...
@@ -223,7 +224,7 @@ int kv_batch_reserve_cow(kv_pool* pool, int32_t B, int32_t* table, int32_t max_b
                          int32_t* n_copies);
 
 /* Device: copy page src[i] to page dst[i] for i < n, every layer, K and V, and
- * for fp8 pools both scales.  src, dst: device int32 [n]; pairs with an id out
+ * for fp8 and int8 pools both scales.  src, dst: device int32 [n]; pairs with an id out
  * of [0, num_blocks), or src == dst, are skipped.  Destinations must be
  * distinct and not also sources (the copies run concurrently). */
 int kv_block_copy(kv_pool* pool, const int32_t* src, const int32_t* dst, int32_t n, void* hip_stream);
@@ -232,17 +233,19 @@ int kv_block_copy(kv_pool* pool, const int32_t* src, const int32_t* dst, int32_t
 
 /* Device: write T new tokens into layer `layer` of the pool.
  * k_new, v_new: device [T][num_kv_heads][head_dim], float for KV_F32 pools and
- * bfloat16 for KV_BF16 and KV_FP8_E4M3 pools.  slot_mapping: device int32 [T];
+ * bfloat16 for KV_BF16, KV_FP8_E4M3 and KV_INT8 pools.  slot_mapping: device int32 [T];
  * token t goes to block slot/block_size, offset slot%block_size; -1 skips it.
- * f32 and bf16 pools store the bits unchanged.  fp8 pools quantise per
+ * f32 and bf16 pools store the bits unchanged.  fp8 and int8 pools quantise per
  * (block, kv-head) tile, separately for K and V: the tokens of one call that
  * land in one tile (which must be consecutive tokens of the call, at
  * increasing offsets) form a run; a run starting at offset 0 starts a fresh
  * tile (old scale ignored), otherwise s0 is the stored scale; the new scale is
- * s1 = max(s0, max|x| / 448) in fp32; when s1 != s0 the codes already below
- * the run's first offset are re-encoded from decode(code)*s0; each new code is
- * the E4M3 encoding (round to nearest even, saturating at 448) of
- * x * (1/s1), all code 0 when s1 == 0.
+ * s1 = max(s0, max|x| / M) in fp32 (M = 448 for fp8, 127 for int8); when
+ * s1 != s0 the codes already below the run's first offset are re-encoded from
+ * decode(code)*s0; each new code encodes x * (1/s1): fp8, the E4M3 encoding
+ * (round to nearest even, saturating at 448); int8, round half to even then
+ * clamp to [-127, 127] (askaiml §7 names INT8 next to fp8 with no details;
+ * this symmetric form reuses the fp8 tile rule).  All codes 0 when s1 == 0.
  * Two tokens of one call must not share a slot.  T == 0 is a no-op. */
 int kv_append(kv_pool* pool, int32_t layer, const void* k_new, const void* v_new,
               const int32_t* slot_mapping, int32_t T, void* hip_stream);
@@ -251,7 +254,7 @@ int kv_append(kv_pool* pool, int32_t layer, const void* k_new, const void* v_new
 
 /* Workspace bytes paged_attention_decode needs for this batch shape, -1 on
  * invalid arguments.  fp32 caches: 0 when one partition covers max_ctx.
- * bf16 and fp8 caches: always > 0 (split states plus B + 1 integers). */
+ * bf16, fp8 and int8 caches: always > 0 (split states plus B + 1 integers). */
 int64_t paged_attention_workspace_bytes(const kv_pool* pool, int32_t B, int32_t h_q,
                                         int32_t max_ctx, int32_t partition_tokens);
 
@@ -263,7 +266,7 @@ int64_t paged_attention_workspace_bytes(const kv_pool* pool, int32_t B, int32_t 
  * (the attention step of "Memoizing Context via KV Caching" and of the askaiml
  * page, §1, over the paged layout of its §4).
  * q: device [B][h_q][head_dim] of q_dtype (KV_F32 with f32 pools, KV_BF16 with
- * bf16 and fp8 pools); out: device, same shape and dtype as q.
+ * bf16, fp8 and int8 pools); out: device, same shape and dtype as q.
  * block_tables: device int32 [B][max_blocks_per_seq]; context_lens: device
  * int32 [B]; max_ctx: host bound, <= max_blocks_per_seq * block_size.  Each
  * context length is clamped to [0, max_ctx] before use, so a length beyond
@@ -273,7 +276,7 @@ int64_t paged_attention_workspace_bytes(const kv_pool* pool, int32_t B, int32_t 
  *  - fp32 caches: partitions of partition_tokens tokens (0 = 512) per request
  *    and kv-head; with more than one, their (max, sum, weighted sum) states go
  *    to the workspace and a second kernel merges them.
- *  - bf16 and fp8 caches (B <= 8192): 0 splits the blocks of the whole batch
+ *  - bf16, fp8 and int8 caches (B <= 8192): 0 splits the blocks of the whole batch
  *    evenly over the kernel's waves; otherwise each piece covers at most
  *    partition_tokens tokens.  Pieces that do not cover a whole request leave
  *    states in the workspace, merged by a second kernel in piece order.
@@ -293,7 +296,7 @@ int paged_attention_decode(kv_pool* pool, int32_t layer, void* out, const void* 
  *   kv_append(pool, layer, k_new, v_new, slot_mapping, B, stream);
  *   paged_attention_decode(pool, layer, out, q, ...);
  * with these added arguments:
- * k_new, v_new: device [B][num_kv_heads][head_dim] (bf16 for bf16 and fp8
+ * k_new, v_new: device [B][num_kv_heads][head_dim] (bf16 for bf16, fp8 and int8
  * pools, float for f32 pools), the new token of each request; slot_mapping:
  * device int32 [B], the slot of position context_lens[b] - 1 of request b
  * (as kv_slot_mapping / kv_batch_reserve give it), or -1 when request b
@@ -302,8 +305,8 @@ int paged_attention_decode(kv_pool* pool, int32_t layer, void* out, const void* 
  * bf16 pools run it as one kernel: the attention takes the last position from
  * k_new / v_new while the same launch stores them into the slot, so the step
  * costs no separate append launch (outputs agree with the two calls to the
- * bf16 rounding of the weights).  f32 and fp8 pools launch the append kernel
- * and then the decode (fp8 re-quantises the tile, which the attention must
+ * bf16 rounding of the weights).  f32, fp8 and int8 pools launch the append
+ * kernel and then the decode (fp8 and int8 re-quantise the tile, which the attention must
  * read).  Errors and workspace are those of paged_attention_decode, plus
  * KV_E_INVALID for a NULL k_new, v_new or slot_mapping. */
 int paged_attention_decode_append(kv_pool* pool, int32_t layer, void* out, const void* q,
@@ -322,8 +325,8 @@ int paged_attention_decode_append(kv_pool* pool, int32_t layer, void* out, const
  * is the attention over positions t < sink_tokens and n - window_tokens <= t
  * < n, positions keeping their index.  Only pages holding such positions are
  * read, so their table entries must be valid and the others may be -1 or
- * released (kv_window_release).  sink_tokens >= 0, window_tokens >= 1, bf16
- * and fp8 pools (KV_E_UNSUPPORTED for f32).  All other arguments, the
+ * released (kv_window_release).  sink_tokens >= 0, window_tokens >= 1; bf16,
+ * fp8 and int8 pools (KV_E_UNSUPPORTED for f32).  All other arguments, the
  * workspace and errors are those of paged_attention_decode. */
 int paged_attention_decode_window(kv_pool* pool, int32_t layer, void* out, const void* q, int32_t q_dtype,
                                   const int32_t* block_tables, int32_t max_blocks_per_seq,

@@ -3,7 +3,7 @@ cache, a slot-mapped append, and a refcounted O(1) block allocator, as a C-ABI
 HIP library (libpagedkv.so) with a thin ctypes binding."""
 
 from .binding import (  # noqa: F401
-    KV_F32, KV_BF16, KV_FP8_E4M3, BLOCK_SIZE, STATUS, SIGNATURES, KVError, KvPoolDesc, Pool,
+    KV_F32, KV_BF16, KV_FP8_E4M3, KV_INT8, BLOCK_SIZE, STATUS, SIGNATURES, KVError, KvPoolDesc, Pool,
     load_library, make_desc, kv_bytes_per_token, kv_blocks_for_tokens, kv_pool_buffer_bytes,
     kv_pool_create, kv_pool_destroy, kv_block_alloc, kv_block_retain, kv_block_release, kv_block_retain_n, kv_block_release_n,
     kv_block_refcount, kv_num_free_blocks, kv_slot_mapping, kv_batch_reserve, kv_append,

@@ -13,10 +13,10 @@ import numpy as np
 
 from .build import LIB_PATH
 
-KV_F32, KV_BF16, KV_FP8_E4M3 = 0, 1, 2
+KV_F32, KV_BF16, KV_FP8_E4M3, KV_INT8 = 0, 1, 2, 3
 STATUS = {0: "KV_OK", -1: "KV_E_INVALID", -2: "KV_E_UNSUPPORTED", -3: "KV_E_NO_BLOCKS",
           -4: "KV_E_BAD_BLOCK", -5: "KV_E_SHARED", -6: "KV_E_WORKSPACE", -7: "KV_E_HIP"}
-DTYPE_NAMES = {"f32": KV_F32, "bf16": KV_BF16, "fp8": KV_FP8_E4M3}
+DTYPE_NAMES = {"f32": KV_F32, "bf16": KV_BF16, "fp8": KV_FP8_E4M3, "int8": KV_INT8}
 BLOCK_SIZE = 16
 
 # every function pagedkv.h declares: name -> (restype, argtypes)
@@ -442,12 +442,12 @@ class Pool:
         load_library()
         self.desc = make_desc(num_layers, num_blocks, num_kv_heads, head_dim, dtype)
         self.dtype = dtype
-        tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[dtype]
+        tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8, "int8": torch.int8}[dtype]
         L, N, H, D, bs = num_layers, num_blocks, num_kv_heads, head_dim, BLOCK_SIZE
         self.k_cache = torch.zeros((L, N, H, bs, D), dtype=tdt, device=device)
         self.v_cache = torch.zeros((L, N, H, D, bs), dtype=tdt, device=device)
         self.k_scale = self.v_scale = None
-        if dtype == "fp8":
+        if dtype in ("fp8", "int8"):
             self.k_scale = torch.zeros((L, N, H), dtype=torch.float32, device=device)
             self.v_scale = torch.zeros((L, N, H), dtype=torch.float32, device=device)
         self.handle = kv_pool_create(self.desc, self.k_cache, self.v_cache, self.k_scale,

@@ -4,12 +4,12 @@
 // decode step appends the new token's K and V to the cache; §4
 // "PagedAttention": position p of a request lives in page table[p / 16] at
 // offset p % 16 (the slot the caller computed).  §7 "KV cache quantisation":
-// the cache may be held as fp8 E4M3.
+// the cache may be held as fp8 E4M3 or as INT8.
 //
 // Layout per layer: K [block][kv_head][16][head_dim], V [block][kv_head][head_dim][16].
-// f32 and bf16 pools copy bits.  fp8 pools quantise one (block, kv-head) tile
-// per workgroup with one fp32 scale per tile; the rule is spelled out in
-// pagedkv.h at kv_append.
+// f32 and bf16 pools copy bits.  fp8 and int8 pools quantise one (block,
+// kv-head) tile per workgroup with one fp32 scale per tile; the rule is
+// spelled out in pagedkv.h at kv_append.
 
 #include <cstdint>
 
@@ -82,6 +82,21 @@ __device__ inline uint32_t float_to_e4m3(float y) {
   return code | sign;
 }
 
+// Symmetric int8: round half to even, clamp to +-127 (never -128).
+__device__ inline uint32_t float_to_int8(float y) {
+  const float r = fminf(fmaxf(rintf(y), -127.0f), 127.0f);
+  return uint32_t(int32_t(r)) & 0xFFu;
+}
+__device__ inline float int8_to_float(uint32_t c) { return float(int8_t(uint8_t(c))); }
+
+// The 8-bit codec of a cache type: largest code magnitude, encode, decode.
+template <bool INT8>
+struct Codec8 {
+  static constexpr float kMax = INT8 ? 127.0f : 448.0f;
+  __device__ static uint32_t encode(float y) { return INT8 ? float_to_int8(y) : float_to_e4m3(y); }
+  __device__ static float decode(uint32_t c) { return INT8 ? int8_to_float(c) : e4m3_to_float(c); }
+};
+
 __device__ inline float bf16_bits_to_float(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
 // Max over the workgroup (one or two waves).
@@ -94,14 +109,15 @@ __device__ inline float block_max(float v, float* red) {
   return blockDim.x > 64 ? fmaxf(red[0], red[1]) : red[0];
 }
 
+// fp8 E4M3 and int8 caches share the kernel; only the codec differs.
 // One workgroup per (token t, kv-head g); only the first token of a run (the
 // consecutive tokens of this call landing in one block) does the work, for
 // the whole run.  The run's K tile ([16][D] codes) and V tile ([D][16]) are
 // staged in LDS with one 16-byte load per thread, re-encoded and written
 // there, and the changed bytes go back with 16-byte stores.
 // blockDim.x = D (64 or 128); thread d owns dimension d.
-template <int D>
-__global__ void __launch_bounds__(D) append_fp8_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
+template <int D, bool INT8>
+__global__ void __launch_bounds__(D) append_q8_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
                                                        float* __restrict__ ks, float* __restrict__ vs,
                                                        const uint16_t* __restrict__ k_new,
                                                        const uint16_t* __restrict__ v_new,
@@ -146,7 +162,7 @@ __global__ void __launch_bounds__(D) append_fp8_kernel(uint8_t* __restrict__ kc,
     for (int r = t; r <= u; ++r)
       amax = fmaxf(amax, fabsf(bf16_bits_to_float(src[(int64_t(r) * H + g) * D + d])));
     amax = block_max(amax, red);
-    const float s1 = fmaxf(s0, amax / 448.0f);
+    const float s1 = fmaxf(s0, amax / Codec8<INT8>::kMax);
     reenc[which] = s1 != s0 && first_off > 0;
     uint8_t* st = s_tile[which];
     if (s1 == 0.0f) {
@@ -155,12 +171,12 @@ __global__ void __launch_bounds__(D) append_fp8_kernel(uint8_t* __restrict__ kc,
       const float inv = 1.0f / s1;
       if (reenc[which])
         for (int o = 0; o < first_off; ++o) {
-          const float x = e4m3_to_float(st[pos(which, o)]) * s0;
-          st[pos(which, o)] = uint8_t(float_to_e4m3(x * inv));
+          const float x = Codec8<INT8>::decode(st[pos(which, o)]) * s0;
+          st[pos(which, o)] = uint8_t(Codec8<INT8>::encode(x * inv));
         }
       for (int r = t; r <= u; ++r) {
         const float x = bf16_bits_to_float(src[(int64_t(r) * H + g) * D + d]);
-        st[pos(which, slots[r] % kBS)] = uint8_t(float_to_e4m3(x * inv));
+        st[pos(which, slots[r] % kBS)] = uint8_t(Codec8<INT8>::encode(x * inv));
       }
     }
     if (d == 0) (which == 0 ? ks : vs)[sidx] = s1;
@@ -202,12 +218,16 @@ int launch_append(const kv_pool* p, int32_t layer, const void* k_new, const void
     auto* vc8 = static_cast<uint8_t*>(p->v_cache) + lo;
     auto* kn = static_cast<const uint16_t*>(k_new);
     auto* vn = static_cast<const uint16_t*>(v_new);
-    if (D == 128)
-      append_fp8_kernel<128><<<grid, 128, 0, stream>>>(kc8, vc8, p->k_scale + so, p->v_scale + so, kn, vn,
-                                                       slots, T, d.num_kv_heads);
-    else
-      append_fp8_kernel<64><<<grid, 64, 0, stream>>>(kc8, vc8, p->k_scale + so, p->v_scale + so, kn, vn,
-                                                     slots, T, d.num_kv_heads);
+    float* ks = p->k_scale + so;
+    float* vs = p->v_scale + so;
+    const int H = d.num_kv_heads;
+    if (d.cache_dtype == KV_FP8_E4M3) {
+      if (D == 128) append_q8_kernel<128, false><<<grid, 128, 0, stream>>>(kc8, vc8, ks, vs, kn, vn, slots, T, H);
+      else append_q8_kernel<64, false><<<grid, 64, 0, stream>>>(kc8, vc8, ks, vs, kn, vn, slots, T, H);
+    } else {
+      if (D == 128) append_q8_kernel<128, true><<<grid, 128, 0, stream>>>(kc8, vc8, ks, vs, kn, vn, slots, T, H);
+      else append_q8_kernel<64, true><<<grid, 64, 0, stream>>>(kc8, vc8, ks, vs, kn, vn, slots, T, H);
+    }
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KV_E_HIP, "kv_append launch: %s", hipGetErrorString(e));

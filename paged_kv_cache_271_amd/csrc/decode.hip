@@ -27,6 +27,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -37,6 +38,8 @@ constexpr int kBS = kBlockSize;
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef _Float16 f16x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
+typedef _Float16 f16x2 __attribute__((__vector_size__(2 * sizeof(_Float16))));
 typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
@@ -59,6 +62,56 @@ __device__ inline u32x2 fp8x4_to_bf16x4(uint32_t w) {
   r[0] = __builtin_bit_cast(uint32_t, lo);
   r[1] = __builtin_bit_cast(uint32_t, hi);
   return r;
+}
+
+// Cache element types of the balanced decode.  bf16 and fp8 caches feed the
+// MFMAs bf16 operands; int8 caches feed them fp16 operands, which hold every
+// int8 code exactly and come from the codes in one permute and one packed
+// subtract per pair (below), where bf16 would need a convert per code.
+constexpr int kQBf16 = 0, kQFp8 = 1, kQInt8 = 2;
+
+// Four symmetric int8 codes (one dword) -> four fp16 (two dwords), exact:
+// with the sign bit flipped a code c is the byte u = c + 128, 0x6400 | u is
+// the fp16 1024 + u, and subtracting 1152 leaves c.
+__device__ inline u32x2 int8x4_to_f16x4(uint32_t w) {
+  const uint32_t u = w ^ 0x80808080u;
+  const uint32_t lo = 0x64006400u | (u & 0xFFu) | ((u & 0xFF00u) << 8);
+  const uint32_t hi = 0x64006400u | ((u >> 16) & 0xFFu) | ((u >> 8) & 0xFF0000u);
+  const f16x2 bias = {static_cast<_Float16>(-1152.0f), static_cast<_Float16>(-1152.0f)};
+  u32x2 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, lo) + bias);
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, hi) + bias);
+  return r;
+}
+
+// Four 8-bit codes of cache type QT -> four MFMA operand elements.
+template <int QT>
+__device__ inline u32x2 q8x4_to_op(uint32_t w) {
+  if constexpr (QT == kQFp8) return fp8x4_to_bf16x4(w);
+  else return int8x4_to_f16x4(w);
+}
+
+// Two fp32 values -> one dword of two MFMA operand elements (bf16, or fp16
+// for int8 caches), round to nearest even.
+template <int QT>
+__device__ inline uint32_t pack_op(float lo, float hi) {
+  if constexpr (QT == kQInt8) {
+    const f16x2 h = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
+    return __builtin_bit_cast(uint32_t, h);
+  } else {
+    return pack_bf16(lo, hi);
+  }
+}
+
+// c += a * b on one 16x16x32 MFMA tile of the cache type's operands.
+template <int QT>
+__device__ inline f32x4 mfma_op(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (QT == kQInt8)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                  0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                   c, 0, 0, 0);
 }
 
 // Zero the 16-bit elements e >= valid (0 <= valid <= 8) of an 8-element vector.
@@ -129,14 +182,21 @@ struct WaveState {
   f32x4 acc[D / 16];    // lane (r, q): head r, dims 16t + 4q + i
 };
 
-template <bool FP8, int D>
-__device__ inline void load_q(bf16x8 (&qv)[D / 32], const uint16_t* q, int64_t row0, int r, int grp, int nh) {
+// The lane's share of the query row as MFMA operands (bf16 bits; for int8
+// caches converted to fp16, exact for magnitudes in fp16's normal range).
+template <int QT, int D>
+__device__ inline void load_q(u32x4 (&qv)[D / 32], const uint16_t* q, int64_t row0, int r, int grp, int nh) {
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk) {
-    const int dim0 = FP8 ? (D / 4) * grp + 8 * kk : 32 * kk + 8 * grp;
+    const int dim0 = QT != kQBf16 ? (D / 4) * grp + 8 * kk : 32 * kk + 8 * grp;
     u32x4 v = {0, 0, 0, 0};
     if (r < nh) v = ld16(q + (row0 + r) * D + dim0);
-    qv[kk] = __builtin_bit_cast(bf16x8, v);
+    if constexpr (QT == kQInt8) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        v[w] = pack_op<QT>(__uint_as_float(v[w] << 16), __uint_as_float(v[w] & 0xFFFF0000u));
+    }
+    qv[kk] = v;
   }
 }
 
@@ -154,17 +214,18 @@ __device__ inline u32x4 mask_bits(u32x4 v, uint32_t keep) {
 // Stream blocks [j0, j1) of one (request, kv-head) into the wave state.
 // Positions at or past ctx are masked.  WIN: so are positions in
 // [sink, win_lo) (a sliding window with attention sinks).
-template <bool FP8, int D, bool WIN = false>
+template <int QT, int D, bool WIN = false>
 __device__ inline void run_segment(WaveState<D>& st, const uint8_t* __restrict__ kc,
                                    const uint8_t* __restrict__ vc, const float* __restrict__ kscale,
                                    const float* __restrict__ vscale, const int32_t* __restrict__ trow,
                                    int ctx, int H, int g, int j0, int j1, float scale_log2,
-                                   const bf16x8 (&qv)[D / 32], int r, int grp, int sink = 0,
+                                   const u32x4 (&qv)[D / 32], int r, int grp, int sink = 0,
                                    int win_lo = 0) {
   constexpr int NB = kStreamNB;
   constexpr int KK = D / 32;
   constexpr int T8 = D / 16;
-  constexpr int EB = FP8 ? 1 : 2;
+  constexpr bool Q8 = QT != kQBf16;  // 8-bit codes with per-tile scales
+  constexpr int EB = Q8 ? 1 : 2;
   const int64_t tile_bytes = int64_t(kBS) * D * EB;
   const int kb_rel = r >> 3;    // block (of the step) feeding this lane's K row
   const int vb_rel = grp >> 1;  // block whose scores / V this lane owns
@@ -186,17 +247,17 @@ __device__ inline void run_segment(WaveState<D>& st, const uint8_t* __restrict__
     const uint8_t* vtile = vc + (pV * H + g) * tile_bytes;
 
     // ---- loads: K rows for the score MFMAs, this lane's V slice
-    bf16x8 kop[NB][KK];
+    u32x4 kop[NB][KK];
     u32x4 vraw[T8];
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       const int ktok = 8 * ((r >> 2) & 1) + 4 * j + (r & 3);
-      if constexpr (!FP8) {
+      if constexpr (!Q8) {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           u32x4 v = {0, 0, 0, 0};
           if (vK) v = ld16(ktile + (ktok * D + 32 * kk + 8 * grp) * 2);
-          kop[j][kk] = __builtin_bit_cast(bf16x8, v);
+          kop[j][kk] = v;
         }
       } else {
         constexpr int NSEG = D / 64;  // 16-byte pieces of a lane's D/4 codes
@@ -209,15 +270,15 @@ __device__ inline void run_segment(WaveState<D>& st, const uint8_t* __restrict__
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           const u32x4& sv = seg[kk / 2];
-          const u32x2 a = fp8x4_to_bf16x4(sv[(kk % 2) * 2 + 0]);
-          const u32x2 bq = fp8x4_to_bf16x4(sv[(kk % 2) * 2 + 1]);
-          kop[j][kk] = __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], bq[0], bq[1]});
+          const u32x2 a = q8x4_to_op<QT>(sv[(kk % 2) * 2 + 0]);
+          const u32x2 bq = q8x4_to_op<QT>(sv[(kk % 2) * 2 + 1]);
+          kop[j][kk] = u32x4{a[0], a[1], bq[0], bq[1]};
         }
       }
     }
 #pragma unroll
     for (int t = 0; t < T8; ++t) {
-      if constexpr (!FP8) {
+      if constexpr (!Q8) {
         u32x4 v = {0, 0, 0, 0};
         if (vV) v = ld16(vtile + ((16 * t + r) * kBS + vtok) * 2);
         vraw[t] = v;
@@ -235,13 +296,13 @@ __device__ inline void run_segment(WaveState<D>& st, const uint8_t* __restrict__
       S[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
-        S[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[j][kk], qv[kk], S[j], 0, 0, 0);
+        S[j] = mfma_op<QT>(kop[j][kk], qv[kk], S[j]);
     }
 
     // ---- online softmax over the step's 32 tokens
     float kfac = scale_log2;
     float vfac = 1.0f;
-    if constexpr (FP8) {
+    if constexpr (Q8) {
       if (vV) {
         kfac *= kscale[pV * H + g];
         vfac = vscale[pV * H + g];
@@ -286,16 +347,15 @@ __device__ inline void run_segment(WaveState<D>& st, const uint8_t* __restrict__
 
     // ---- weighted sum of V: k-slot e is token vtok + e of block bV
     const f32x4 lo = S[0] * vfac, hi = S[1] * vfac;
-    const u32x4 pw = {pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3]), pack_bf16(hi[0], hi[1]),
-                      pack_bf16(hi[2], hi[3])};
-    const bf16x8 pop = __builtin_bit_cast(bf16x8, pw);
+    const u32x4 pop = {pack_op<QT>(lo[0], lo[1]), pack_op<QT>(lo[2], lo[3]), pack_op<QT>(hi[0], hi[1]),
+                       pack_op<QT>(hi[2], hi[3])};
     const int vh = min(max(valid, 0), 8);
 #pragma unroll
     for (int t = 0; t < T8; ++t) {
       u32x4 v;
-      if constexpr (FP8) {
-        const u32x2 a = fp8x4_to_bf16x4(vraw[t][0]);
-        const u32x2 c2 = fp8x4_to_bf16x4(vraw[t][1]);
+      if constexpr (Q8) {
+        const u32x2 a = q8x4_to_op<QT>(vraw[t][0]);
+        const u32x2 c2 = q8x4_to_op<QT>(vraw[t][1]);
         v = u32x4{a[0], a[1], c2[0], c2[1]};
       } else {
         v = vraw[t];
@@ -305,7 +365,7 @@ __device__ inline void run_segment(WaveState<D>& st, const uint8_t* __restrict__
       } else {
         if (vh < 8) v = mask_tail(v, vh);  // stale or poisoned slots past the context
       }
-      st.acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), pop, st.acc[t], 0, 0, 0);
+      st.acc[t] = mfma_op<QT>(v, pop, st.acc[t]);
     }
   }
 }
@@ -317,14 +377,15 @@ __device__ inline void run_segment(WaveState<D>& st, const uint8_t* __restrict__
 // counted once in l (lane group 0) since l is summed over lane groups later.
 template <int D>
 __device__ inline void add_token(WaveState<D>& st, const uint16_t* __restrict__ kn,
-                                 const uint16_t* __restrict__ vn, const bf16x8 (&qv)[D / 32],
+                                 const uint16_t* __restrict__ vn, const u32x4 (&qv)[D / 32],
                                  float scale_log2, int grp) {
   float s = 0.0f;
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk) {
     const bf16x8 kx = __builtin_bit_cast(bf16x8, ld16(kn + 32 * kk + 8 * grp));
+    const bf16x8 qx = __builtin_bit_cast(bf16x8, qv[kk]);  // bf16 caches only
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s = fmaf(float(qv[kk][e]), float(kx[e]), s);
+    for (int e = 0; e < 8; ++e) s = fmaf(float(qx[e]), float(kx[e]), s);
   }
   s = wave_sum16(s) * scale_log2;
   const float m_new = fmaxf(st.m, s);
@@ -406,7 +467,7 @@ __device__ inline void block_prefix_blocks(int32_t* s_pref, int32_t* s_tmp, cons
 // WIN: a sliding window of `window` tokens plus `sink` sink tokens; units
 // run over the pages each request reads (visited_pages), so pages outside
 // are never touched and may be free.
-template <bool FP8, int D, bool APPEND, bool WIN>
+template <int QT, int D, bool APPEND, bool WIN>
 __global__ void __launch_bounds__(256, 3)
 decode_stream_kernel(void* __restrict__ kc_, void* __restrict__ vc_,
                      const float* __restrict__ kscale, const float* __restrict__ vscale,
@@ -505,8 +566,8 @@ decode_stream_kernel(void* __restrict__ kc_, void* __restrict__ vc_,
       const int head0 = g * G + hg * 16;
       const int nh = min(16, G - hg * 16);
       const int64_t row0 = int64_t(b) * h_q + head0;
-      bf16x8 qv[D / 32];
-      load_q<FP8, D>(qv, q, row0, r, grp, nh);
+      u32x4 qv[D / 32];
+      load_q<QT, D>(qv, q, row0, r, grp, nh);
       WaveState<D> st;
 #pragma unroll
       for (int t = 0; t < T8; ++t) st.acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -522,7 +583,7 @@ decode_stream_kernel(void* __restrict__ kc_, void* __restrict__ vc_,
           const int hi = part == 0 ? min(j1, vp.a) : j1;
           const int off = part == 0 ? 0 : vp.c - vp.a;
           if (lo < hi)
-            run_segment<FP8, D, true>(st, kc, vc, kscale, vscale, tables + int64_t(b) * max_blocks, ctx, H, g,
+            run_segment<QT, D, true>(st, kc, vc, kscale, vscale, tables + int64_t(b) * max_blocks, ctx, H, g,
                                       lo + off, hi + off, scale_log2, qv, r, grp, sink, win_lo);
         }
       } else if constexpr (APPEND) {
@@ -532,14 +593,14 @@ decode_stream_kernel(void* __restrict__ kc_, void* __restrict__ vc_,
         const int ctx_c = ctx - (app ? 1 : 0);
         const int jc1 = min(j1, (ctx_c + kBS - 1) / kBS);
         if (j < jc1)
-          run_segment<FP8, D>(st, kc, vc, kscale, vscale, tables + int64_t(b) * max_blocks, ctx_c, H, g,
+          run_segment<QT, D>(st, kc, vc, kscale, vscale, tables + int64_t(b) * max_blocks, ctx_c, H, g,
                               j, jc1, scale_log2, qv, r, grp);
         if (app && j1 == nb) {
           const int64_t nrow = (int64_t(b) * H + g) * D;
           add_token<D>(st, k_new + nrow, v_new + nrow, qv, scale_log2, grp);
         }
       } else {
-        run_segment<FP8, D>(st, kc, vc, kscale, vscale, tables + int64_t(b) * max_blocks, ctx, H, g, j, j1,
+        run_segment<QT, D>(st, kc, vc, kscale, vscale, tables + int64_t(b) * max_blocks, ctx, H, g, j, j1,
                             scale_log2, qv, r, grp);
       }
       const float l = wave_sum16(st.l);
@@ -884,30 +945,34 @@ int launch_decode_d(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(a.workers / 4);
   auto* q = static_cast<const uint16_t*>(a.q);
   auto* out = static_cast<uint16_t*>(a.out);
-  const float* ks = d.cache_dtype == KV_FP8_E4M3 ? a.pool->k_scale + so : nullptr;
-  const float* vs = d.cache_dtype == KV_FP8_E4M3 ? a.pool->v_scale + so : nullptr;
+  const bool q8 = d.cache_dtype == KV_FP8_E4M3 || d.cache_dtype == KV_INT8;
+  const float* ks = q8 ? a.pool->k_scale + so : nullptr;
+  const float* vs = q8 ? a.pool->v_scale + so : nullptr;
   const bool win = a.window > 0;
-  if (d.cache_dtype == KV_BF16 && a.new_slots)
-    decode_stream_kernel<false, D, true, false><<<grid, 256, 0, s>>>(
-        kc, vc, nullptr, nullptr, q, out, a.tables, a.max_blocks, a.ctx, a.B, a.max_ctx, H, a.h_q, G, nhg,
-        a.hs, sl, a.chunk, a.ws_ml, a.ws_acc, a.ws_pref, static_cast<const uint16_t*>(a.k_new),
-        static_cast<const uint16_t*>(a.v_new), a.new_slots, 0, 0);
-  else if (d.cache_dtype == KV_BF16 && win)
-    decode_stream_kernel<false, D, false, true><<<grid, 256, 0, s>>>(
-        kc, vc, nullptr, nullptr, q, out, a.tables, a.max_blocks, a.ctx, a.B, a.max_ctx, H, a.h_q, G, nhg,
-        a.hs, sl, a.chunk, a.ws_ml, a.ws_acc, a.ws_pref, nullptr, nullptr, nullptr, a.sink, a.window);
-  else if (d.cache_dtype == KV_BF16)
-    decode_stream_kernel<false, D, false, false><<<grid, 256, 0, s>>>(
-        kc, vc, nullptr, nullptr, q, out, a.tables, a.max_blocks, a.ctx, a.B, a.max_ctx, H, a.h_q, G, nhg,
-        a.hs, sl, a.chunk, a.ws_ml, a.ws_acc, a.ws_pref, nullptr, nullptr, nullptr, 0, 0);
-  else if (win)
-    decode_stream_kernel<true, D, false, true><<<grid, 256, 0, s>>>(
+  auto go = [&](auto qt, auto append, auto window) {
+    constexpr int QT = decltype(qt)::value;
+    constexpr bool AP = decltype(append)::value, WN = decltype(window)::value;
+    decode_stream_kernel<QT, D, AP, WN><<<grid, 256, 0, s>>>(
         kc, vc, ks, vs, q, out, a.tables, a.max_blocks, a.ctx, a.B, a.max_ctx, H, a.h_q, G, nhg, a.hs, sl,
-        a.chunk, a.ws_ml, a.ws_acc, a.ws_pref, nullptr, nullptr, nullptr, a.sink, a.window);
-  else
-    decode_stream_kernel<true, D, false, false><<<grid, 256, 0, s>>>(
-        kc, vc, ks, vs, q, out, a.tables, a.max_blocks, a.ctx, a.B, a.max_ctx, H, a.h_q, G, nhg, a.hs, sl,
-        a.chunk, a.ws_ml, a.ws_acc, a.ws_pref, nullptr, nullptr, nullptr, 0, 0);
+        a.chunk, a.ws_ml, a.ws_acc, a.ws_pref, static_cast<const uint16_t*>(a.k_new),
+        static_cast<const uint16_t*>(a.v_new), a.new_slots, a.sink, a.window);
+  };
+  using F = std::false_type;
+  using T = std::true_type;
+  using QB = std::integral_constant<int, kQBf16>;
+  using QF = std::integral_constant<int, kQFp8>;
+  using QI = std::integral_constant<int, kQInt8>;
+  if (d.cache_dtype == KV_BF16) {
+    if (a.new_slots) go(QB{}, T{}, F{});  // fused append (plain decode only)
+    else if (win) go(QB{}, F{}, T{});
+    else go(QB{}, F{}, F{});
+  } else if (d.cache_dtype == KV_FP8_E4M3) {
+    if (win) go(QF{}, F{}, T{});
+    else go(QF{}, F{}, F{});
+  } else {
+    if (win) go(QI{}, F{}, T{});
+    else go(QI{}, F{}, F{});
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return fail(KV_E_HIP, "decode launch: %s", hipGetErrorString(e));
   if (win)

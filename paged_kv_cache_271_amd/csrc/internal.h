@@ -71,6 +71,9 @@ int ok();
 
 inline int elem_bytes(int dtype) { return dtype == KV_F32 ? 4 : dtype == KV_BF16 ? 2 : 1; }
 
+// Caches of 8-bit codes with one fp32 scale per (layer, block, kv-head).
+inline bool scaled_dtype(int dtype) { return dtype == KV_FP8_E4M3 || dtype == KV_INT8; }
+
 // Elements of one layer of the K (or V) array.
 inline int64_t layer_elems(const kv_pool_desc& d) {
   return int64_t(d.num_blocks) * d.num_kv_heads * d.block_size * d.head_dim;

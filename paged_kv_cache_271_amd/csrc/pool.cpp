@@ -19,7 +19,7 @@ thread_local std::string g_last_error;
 bool desc_valid(const kv_pool_desc* d) {
   return d && d->num_layers >= 1 && d->num_blocks >= 1 && d->block_size >= 1 &&
          d->num_kv_heads >= 1 && d->head_dim >= 1 && d->cache_dtype >= KV_F32 &&
-         d->cache_dtype <= KV_FP8_E4M3;
+         d->cache_dtype <= KV_INT8;
 }
 }  // namespace
 
@@ -56,7 +56,7 @@ int32_t kv_blocks_for_tokens(int32_t n, int32_t block_size) {
 int kv_pool_buffer_bytes(const kv_pool_desc* d, int64_t* cache_bytes, int64_t* scale_bytes) {
   if (!desc_valid(d)) return fail(KV_E_INVALID, "invalid pool descriptor");
   const int64_t cb = int64_t(d->num_layers) * layer_elems(*d) * elem_bytes(d->cache_dtype);
-  const int64_t sb = d->cache_dtype == KV_FP8_E4M3
+  const int64_t sb = scaled_dtype(d->cache_dtype)
                          ? int64_t(d->num_layers) * d->num_blocks * d->num_kv_heads * 4
                          : 0;
   if (cache_bytes) *cache_bytes = cb;
@@ -74,11 +74,11 @@ int kv_pool_create(const kv_pool_desc* d, void* k_cache, void* v_cache, float* k
   if (d->head_dim != 64 && d->head_dim != 128)
     return fail(KV_E_UNSUPPORTED, "head_dim %d not supported (64 or 128)", d->head_dim);
   if (!k_cache || !v_cache) return fail(KV_E_INVALID, "k_cache and v_cache are required");
-  const bool fp8 = d->cache_dtype == KV_FP8_E4M3;
-  if (fp8 && (!k_scale || !v_scale))
-    return fail(KV_E_INVALID, "fp8 pools need k_scale and v_scale");
-  if (!fp8 && (k_scale || v_scale))
-    return fail(KV_E_INVALID, "scale arrays are only for fp8 pools");
+  const bool scaled = scaled_dtype(d->cache_dtype);
+  if (scaled && (!k_scale || !v_scale))
+    return fail(KV_E_INVALID, "fp8 and int8 pools need k_scale and v_scale");
+  if (!scaled && (k_scale || v_scale))
+    return fail(KV_E_INVALID, "scale arrays are only for fp8 and int8 pools");
   const int32_t n = d->num_blocks;
   std::vector<int32_t> seen(n, 0);
   auto* p = new (std::nothrow) kv_pool();

@@ -53,6 +53,10 @@ WORKLOADS = {
     "fp8": dict(dtype="fp8", num_layers=1, h_q=32, h_kv=8, head_dim=128,
                 batch=128, ctx_range=(1024, 8192), outlier_p=0.01,
                 outlier_mul=8.0, partition_tokens=512),
+    # the fp8 batch stored as symmetric int8 codes
+    "int8": dict(dtype="int8", num_layers=1, h_q=32, h_kv=8, head_dim=128,
+                 batch=128, ctx_range=(1024, 8192), outlier_p=0.01,
+                 outlier_mul=8.0, partition_tokens=512),
 }
 
 # sub-stream order of SeedSequence(seed).spawn(...)

@@ -12,7 +12,7 @@ import synth
 import paged_kv_cache_271_amd as pk
 
 DEV = "cuda:0"
-NAN_BITS = {"bf16": 0x7FC0, "fp8": 0x7F}
+NAN_BITS = {"bf16": 0x7FC0, "fp8": 0x7F, "int8": -128}   # int8: a code never written
 # (atol, rtol) against the fp64 oracle
 TOL = {
     "f32": (1e-5, 0.0),
@@ -21,6 +21,9 @@ TOL = {
     # dequantised codes, produced bit-exactly by the oracle's own quantiser)
     "fp8": (6e-2, 0.0),
     "fp8q": (2e-2, 2e-2),    # a tighter bound the kernel also meets
+    # int8 caches: against the oracle on the dequantised codes (the oracle's
+    # own quantiser produces them bit for bit), the bf16 bound
+    "int8": (2e-2, 2e-2),
 }
 
 
@@ -85,8 +88,8 @@ class Case:
         shape = (T, H, D)
         self.device_inputs = device_inputs
         if mirror is None:
-            mirror = dtype == "fp8" and T * H * D <= 4_000_000
-        self.ref_pool = oracle.RefPool(1, self.N, H, D, 16, "fp8") if mirror else None
+            mirror = dtype in ("fp8", "int8") and T * H * D <= 4_000_000
+        self.ref_pool = oracle.RefPool(1, self.N, H, D, 16, dtype) if mirror else None
         if device_inputs:
             tdt = torch.float32 if dtype == "f32" else torch.bfloat16
             self.dk = synth.device_normal(shape, seed * 16 + 1, DEV, tdt, outlier_p, 8.0)
@@ -118,8 +121,8 @@ class Case:
             self.pool.k_cache.view(torch.int16).fill_(NAN_BITS["bf16"])
             self.pool.v_cache.view(torch.int16).fill_(NAN_BITS["bf16"])
         else:
-            self.pool.k_cache.fill_(NAN_BITS["fp8"])
-            self.pool.v_cache.fill_(NAN_BITS["fp8"])
+            self.pool.k_cache.fill_(NAN_BITS[self.dtype])
+            self.pool.v_cache.fill_(NAN_BITS[self.dtype])
             self.pool.k_scale.fill_(float("nan"))
             self.pool.v_scale.fill_(float("nan"))
 
@@ -201,7 +204,7 @@ class Case:
         out = self.pool.decode_append(0, q, dk, dv, d_slots, self.d_table, self.d_lens, max_ctx,
                                       1.0 / math.sqrt(self.D), partition_tokens)
         torch.cuda.synchronize()
-        if self.dtype == "fp8":
+        if self.dtype in ("fp8", "int8"):
             if self.ref_pool is not None:
                 self.ref_pool.append(0, k[appends], v[appends], new_slots)
                 assert np.array_equal(self.pool.k_cache.cpu().numpy(), self.ref_pool.K)
@@ -237,8 +240,8 @@ class Case:
     def seq_f64(self, b, dequant=True):
         """Values attention should read: the stored values (dequantised codes
         for fp8 when dequant=True), else the inputs before quantisation."""
-        if self.dtype == "fp8" and dequant:
-            assert self.ref_pool is not None, "no host mirror of the fp8 pool"
+        if self.dtype in ("fp8", "int8") and dequant:
+            assert self.ref_pool is not None, "no host mirror of the quantised pool"
             return self.ref_pool.gather_f64(0, self.table[b], self.lens_list[b])
         k, v = self.seq_raw(b)
         if self.dtype == "f32":

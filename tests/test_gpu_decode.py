@@ -55,12 +55,13 @@ def test_append_copy_bit_exact(gpu_lib, dtype, D):
     assert np.array_equal(pool.v_cache.view(torch.uint8).cpu().numpy().reshape(-1), ref.V.reshape(-1).view(np.uint8))
 
 
-def test_append_fp8_bit_exact(gpu_lib):
-    log("append fp8")
+@pytest.mark.parametrize("dtype", ["fp8", "int8"])
+def test_append_quantised_bit_exact(gpu_lib, dtype):
+    log(f"append {dtype}")
     H, D, N = 3, 128, 10
     rng = np.random.default_rng(2)
-    pool = pk.Pool(1, N, H, D, "fp8", DEV, initial_free_order=rng.permutation(N))
-    ref = oracle.RefPool(1, N, H, D, 16, "fp8")
+    pool = pk.Pool(1, N, H, D, dtype, DEV, initial_free_order=rng.permutation(N))
+    ref = oracle.RefPool(1, N, H, D, 16, dtype)
     table = np.zeros((3, 4), np.int32)
     lens = np.zeros(3, np.int32)
     # bulk fills, single tokens growing the scale, and mixed run lengths
@@ -73,7 +74,7 @@ def test_append_fp8_bit_exact(gpu_lib):
         # single tokens larger than before force re-encoding of earlier slots
         k = synth.f32_to_bf16_bits(oracle.bf16_bits_to_f64(k).astype(np.float32) * np.float32(rng.uniform(0.5, 3)))
         check_slots(slots, N)
-        pool.append(0, to_dev_bits(k, "fp8"), to_dev_bits(v, "fp8"), torch.from_numpy(slots).to(DEV))
+        pool.append(0, to_dev_bits(k, dtype), to_dev_bits(v, dtype), torch.from_numpy(slots).to(DEV))
         ref.append(0, k, v, slots)
         torch.cuda.synchronize()
         assert np.array_equal(pool.k_scale.cpu().numpy(), ref.Ks)
@@ -103,7 +104,7 @@ def test_tiny_f32_two_steps(gpu_lib):
             c.grow(seed=11)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8", "int8"])
 def test_block_boundaries_and_split(gpu_lib, dtype):
     """Contexts at and around block edges, growing across them; forced small
     partitions agree with one partition."""
@@ -137,7 +138,7 @@ def test_identical_keys_give_mean_of_values(gpu_lib, dtype):
         assert_close(got[b], want, c.tol_key, f"mean of V, request {b}")
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8", "int8"])
 def test_one_token_and_empty(gpu_lib, dtype):
     c = Case(dtype, 2, 128, 4, [1, 0, 1, 0], num_blocks=4, seed=5)
     got = c.decode()
@@ -163,7 +164,7 @@ def test_group_sizes_mqa_mha(gpu_lib, H, h_q):
 
 
 # ------------------------------------------------ invariance / poison -------
-@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8", "int8"])
 def test_poisoned_slots_do_not_leak(gpu_lib, dtype):
     lens = [17, 40, 3, 130]
     clean = Case(dtype, 2, 128, 8, lens, num_blocks=30, seed=8, order=np.arange(30))
@@ -175,7 +176,7 @@ def test_poisoned_slots_do_not_leak(gpu_lib, dtype):
     assert np.all(np.isfinite(b)) and np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "f32", "int8"])
 def test_physical_permutation_bit_identical(gpu_lib, dtype):
     lens = [300, 17, 1000, 64]
     N = sum(oracle.blocks_for(n, 16) for n in lens) + 7
@@ -187,7 +188,7 @@ def test_physical_permutation_bit_identical(gpu_lib, dtype):
         assert np.array_equal(a.decode(partition_tokens=part), b.decode(partition_tokens=part))
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "int8"])
 def test_shared_prefix_equals_duplicated(gpu_lib, dtype):
     """Requests mapping one set of prefix blocks give the same bits as
     requests holding private copies."""

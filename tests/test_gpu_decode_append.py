@@ -30,7 +30,7 @@ def _case(dtype, H, D, h_q, seed, poison=False):
     return c, appends
 
 
-@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 64), ("fp8", 128)])
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 64), ("fp8", 128), ("int8", 128)])
 def test_decode_append_matches_oracle(gpu_lib, dtype, D):
     c, appends = _case(dtype, 2, D, 8, seed=31)
     for step, part in enumerate((0, 32)):

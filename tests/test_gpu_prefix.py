@@ -28,7 +28,7 @@ def pool_bytes(pool):
 
 def ref_bytes(ref):
     out = [ref.K.reshape(-1).view(np.uint8), ref.V.reshape(-1).view(np.uint8)]
-    if ref.dtype == "fp8":
+    if ref.dtype in ("fp8", "int8"):
         out += [ref.Ks, ref.Vs]
     return out
 
@@ -43,10 +43,10 @@ def same(pool, ref):
 def draw(rng, dtype, shape):
     if dtype == "f32":
         return synth.normal_f32(rng, shape)
-    return synth.normal_bf16_bits(rng, shape, 0.05 if dtype == "fp8" else 0.0, 8.0)
+    return synth.normal_bf16_bits(rng, shape, 0.05 if dtype in ("fp8", "int8") else 0.0, 8.0)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "f32", "int8"])
 def test_block_copy_bit_exact(gpu_lib, dtype):
     L, N, H, D = 3, 20, 2, 128 if dtype != "f32" else 64
     rng = np.random.default_rng(41)
@@ -59,7 +59,7 @@ def test_block_copy_bit_exact(gpu_lib, dtype):
     pool.v_cache.view(torch.uint8).copy_(torch.from_numpy(vb))
     ref.K = kb.reshape(-1).view(ref.K.dtype).reshape(ref.K.shape).copy()
     ref.V = vb.reshape(-1).view(ref.V.dtype).reshape(ref.V.shape).copy()
-    if dtype == "fp8":
+    if dtype in ("fp8", "int8"):
         ks = rng.random((L, N, H), dtype=np.float32)
         vs = rng.random((L, N, H), dtype=np.float32)
         pool.k_scale.copy_(torch.from_numpy(ks))
@@ -73,13 +73,13 @@ def test_block_copy_bit_exact(gpu_lib, dtype):
         if 0 <= s < N and 0 <= d < N and s != d:
             ref.K[:, d] = ref.K[:, s]
             ref.V[:, d] = ref.V[:, s]
-            if dtype == "fp8":
+            if dtype in ("fp8", "int8"):
                 ref.Ks[:, d] = ref.Ks[:, s]
                 ref.Vs[:, d] = ref.Vs[:, s]
     same(pool, ref)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "f32", "int8"])
 def test_fork_copy_on_write_decode(gpu_lib, dtype):
     """A parent of 37 tokens forked into three children; every request then
     appends its own tokens for three steps through copy-on-write.  The pool
@@ -129,7 +129,7 @@ def test_fork_copy_on_write_decode(gpu_lib, dtype):
             for a, b in zip(src, dst):
                 ref.K[:, b] = ref.K[:, a]
                 ref.V[:, b] = ref.V[:, a]
-                if dtype == "fp8":
+                if dtype in ("fp8", "int8"):
                     ref.Ks[:, b] = ref.Ks[:, a]
                     ref.Vs[:, b] = ref.Vs[:, a]
         T = int(n_new.sum())
@@ -154,7 +154,7 @@ def test_fork_copy_on_write_decode(gpu_lib, dtype):
         qf = q.astype(np.float64) if dtype == "f32" else oracle.bf16_bits_to_f64(q)
         for r in range(B):
             K, V = ref.gather_f64(0, table[r], int(lens[r]))
-            if dtype != "fp8":   # the stored values are the request's own inputs
+            if dtype in ("bf16", "f32"):   # the stored values are the request's own inputs
                 K0 = kseq[r].astype(np.float64) if dtype == "f32" else oracle.bf16_bits_to_f64(kseq[r])
                 assert np.array_equal(K, K0)
             ref_o = oracle.attention_fp64(qf[r], K, V, scale)

@@ -29,8 +29,8 @@ def poison_pages(pool, pages, dtype):
         pool.k_cache.view(torch.int16)[0, idx] = NAN_BITS["bf16"]
         pool.v_cache.view(torch.int16)[0, idx] = NAN_BITS["bf16"]
     else:
-        pool.k_cache[0, idx] = NAN_BITS["fp8"]
-        pool.v_cache[0, idx] = NAN_BITS["fp8"]
+        pool.k_cache[0, idx] = NAN_BITS[dtype]
+        pool.v_cache[0, idx] = NAN_BITS[dtype]
         pool.k_scale[0, idx] = float("nan")
         pool.v_scale[0, idx] = float("nan")
 
@@ -84,7 +84,7 @@ def synth_to_dev(c):
 LENS = [1, 15, 16, 17, 40, 100, 333, 1000, 0]
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "int8"])
 @pytest.mark.parametrize("sink,win", [(0, 1), (4, 16), (4, 100), (17, 33), (0, 5000), (40, 7), (16, 16)])
 def test_window_decode_matches_oracle(gpu_lib, dtype, sink, win):
     log(f"window decode {dtype} sink {sink} window {win}")

@@ -2,9 +2,9 @@
 benchmark times (the balanced split, and 512-token partitions): the
 Llama-3-8B-shaped batch (every output, with the step's append fused in and as
 two calls), the Llama-3-70B-shaped long contexts (sampled heads), the fp8
-batch with outliers (sampled requests; codes and scales bit-exact), and 32
-layers x 64 steps of prefix sharing with churn (allocator state every step,
-sampled outputs at checkpoints)."""
+batch with outliers stored as fp8 and as int8 (sampled requests; codes and
+scales bit-exact), and 32 layers x 64 steps of prefix sharing with churn
+(allocator state every step, sampled outputs at checkpoints)."""
 
 import math
 
@@ -72,13 +72,16 @@ def test_llama3_70b_long_context_sampled(gpu_lib):
             assert_close(o[b][heads], ref, "bf16", f"ctx {lens[b]} heads {heads} partition {part}")
 
 
-def test_fp8_batch_sampled(gpu_lib):
+@pytest.mark.parametrize("dtype", ["fp8", "int8"])
+def test_quantised_batch_sampled(gpu_lib, dtype):
+    """The fp8 workload's batch (128 requests of 1k-8k tokens, 1% x8
+    outliers), stored as fp8 E4M3 or as int8."""
     w = synth.WORKLOADS["fp8"]
     rng = synth.streams(5)
     lens = synth.uniform_contexts(rng["contexts"], w["batch"], *w["ctx_range"])
     N = _blocks(lens)
-    log(f"fp8: B={len(lens)} ctx {lens.min()}..{lens.max()} blocks {N}")
-    c = Case("fp8", w["h_kv"], w["head_dim"], w["h_q"], lens, num_blocks=N,
+    log(f"{dtype}: B={len(lens)} ctx {lens.min()}..{lens.max()} blocks {N}")
+    c = Case(dtype, w["h_kv"], w["head_dim"], w["h_q"], lens, num_blocks=N,
              order=synth.permutation(rng["free_order"], N), seed=5, device_inputs=True,
              max_blocks=512, outlier_p=w["outlier_p"], mirror=False)
     got = {part: c.decode(partition_tokens=part) for part in (0, w["partition_tokens"])}
@@ -92,7 +95,7 @@ def test_fp8_batch_sampled(gpu_lib):
         n = int(lens[b])
         nb = oracle.blocks_for(n, 16)
         kraw, vraw = c.seq_raw(b)
-        ref_pool = oracle.RefPool(1, nb, w["h_kv"], w["head_dim"], 16, "fp8")
+        ref_pool = oracle.RefPool(1, nb, w["h_kv"], w["head_dim"], 16, dtype)
         ref_pool.append(0, kraw, vraw, np.arange(n))
         phys = c.table[b, :nb].astype(np.int64)
         idx = torch.from_numpy(phys).to(DEV)
@@ -102,9 +105,9 @@ def test_fp8_batch_sampled(gpu_lib):
         Kq, Vq = ref_pool.gather_f64(0, np.arange(nb), n)
         ref_q = oracle.attention_fp64(q[b], Kq, Vq, scale)
         for part, o in got.items():
-            assert_close(o[b], ref_q, "fp8", f"request {b} (ctx {n}) partition {part} vs the cached values")
-            assert_close(o[b], ref_q, "fp8q", f"request {b} (ctx {n}) partition {part} vs the cached values")
-        # diagnostic only: what E4M3 storage itself costs against the inputs
+            for key in (("fp8", "fp8q") if dtype == "fp8" else ("int8",)):
+                assert_close(o[b], ref_q, key, f"request {b} (ctx {n}) partition {part} vs the cached values")
+        # diagnostic only: what the 8-bit storage itself costs against the inputs
         K0, V0 = oracle.bf16_bits_to_f64(kraw), oracle.bf16_bits_to_f64(vraw)
         ref0 = oracle.attention_fp64(q[b], K0, V0, scale)
         log(f"  request {b}: quantisation effect max|oracle(codes) - oracle(inputs)| "
