@@ -35,6 +35,7 @@ from .attention import (attention_fp64, attention_bruteforce, partitioned_fp64,
                         partition_states, combine_partitions, decode_batch_fp64)
 from .int8 import INT8_MAX, int8_encode, int8_decode, quantize_run_int8
 from .prefix_cache import RefPrefixCache, reserve_cow
+from .prefill import prefill_attention_fp64, prefill_flops
 from .window import (window_positions, attention_window_fp64, dead_pages, window_cache_bytes,
                      window_release)
 
@@ -48,6 +49,6 @@ __all__ = [
     "attention_fp64", "attention_bruteforce", "partitioned_fp64",
     "partition_states", "combine_partitions", "decode_batch_fp64",
     "INT8_MAX", "int8_encode", "int8_decode", "quantize_run_int8",
-    "RefPrefixCache", "reserve_cow",
+    "RefPrefixCache", "reserve_cow", "prefill_attention_fp64", "prefill_flops",
     "window_positions", "attention_window_fp64", "dead_pages", "window_cache_bytes", "window_release",
 ]
