@@ -316,6 +316,31 @@ int paged_attention_decode_append(kv_pool* pool, int32_t layer, void* out, const
                                   int32_t h_q, int32_t max_ctx, float scale, int32_t partition_tokens,
                                   void* workspace, int64_t workspace_bytes, void* hip_stream);
 
+/* --------------------------------------------------------------- prefill -- */
+
+/* Device: causal attention of each request's new tokens over its paged cache
+ * (the prompt pass of "KV cache and PagedAttention", askaiml §1, computed in
+ * tiles as the glossary's FlashAttention entry describes).  Request b's
+ * queries are rows query_start[b] .. query_start[b+1]-1 of q; they are the
+ * last n_q = query_start[b+1] - query_start[b] of its n = context_lens[b]
+ * cached positions (their K and V appended first, e.g. by kv_append), so
+ * query i sits at position n - n_q + i and
+ *   out[row][h] = sum_{t <= n - n_q + i} softmax_t(scale * <q[row][h], K_t>) V_t
+ * with query head h reading kv head h / (h_q / num_kv_heads).  Positions
+ * before the new tokens (a cached prefix, earlier chunks) are read as they
+ * are.  n_q <= n is required.
+ * q, out: device bf16 [total rows][h_q][head_dim]; query_start: device int32
+ * [B+1], non-decreasing from 0; block_tables, context_lens as for
+ * paged_attention_decode; max_q_len: host bound on every n_q (sizes the grid);
+ * max_ctx: host bound on context_lens (<= max_blocks_per_seq * block_size).
+ * bf16 pools and queries only, at most 64 query heads per kv head
+ * (KV_E_UNSUPPORTED otherwise).  No workspace: one workgroup covers all keys
+ * of its query tile. */
+int paged_attention_prefill(kv_pool* pool, int32_t layer, void* out, const void* q, int32_t q_dtype,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, const int32_t* query_start, int32_t B, int32_t h_q,
+                            int32_t max_q_len, int32_t max_ctx, float scale, void* hip_stream);
+
 /* ------------------------------------------------------ sliding window -- */
 
 /* Device: paged_attention_decode for a model with sliding-window attention

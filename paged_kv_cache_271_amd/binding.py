@@ -66,6 +66,8 @@ SIGNATURES = {
                                                      _I32, ctypes.c_float, _I32, _I32, _I32, _P, _I64,
                                                      _P]),
     "kv_window_release": (ctypes.c_int, [_P, _I32, _PI32, _I32, _PI32, _I32, _I32, _PI32]),
+    "paged_attention_prefill": (ctypes.c_int, [_P, _I32, _P, _P, _I32, _P, _I32, _P, _P, _I32, _I32, _I32,
+                                               _I32, ctypes.c_float, _P]),
     "kv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kv_last_error": (ctypes.c_char_p, []),
 }
@@ -404,6 +406,25 @@ def paged_attention_decode_window(h, desc, layer, out, q, block_tables, context_
                                               _stream_ptr(stream)))
 
 
+def paged_attention_prefill(h, desc, layer, out, q, block_tables, context_lens, query_start, max_q_len,
+                            max_ctx, scale, stream=None):
+    """q, out: bf16 [rows, h_q, d_h]; query_start: int32 [B+1] on the device."""
+    import torch
+    if q.dim() != 3 or q.shape[2] != desc.head_dim:
+        raise ValueError("q must be [rows, h_q, head_dim]")
+    rows, h_q, _ = q.shape
+    qp = _dev_ptr(q, "q", torch.bfloat16)
+    op = _dev_ptr(out, "out", torch.bfloat16, q.numel())
+    if block_tables.dim() != 2:
+        raise ValueError("block_tables must be [B, max_blocks]")
+    B = block_tables.shape[0]
+    tp = _dev_ptr(block_tables, "block_tables", torch.int32)
+    cp = _dev_ptr(context_lens, "context_lens", torch.int32, B)
+    sp = _dev_ptr(query_start, "query_start", torch.int32, B + 1)
+    _check(_lib.paged_attention_prefill(h, int(layer), op, qp, KV_BF16, tp, block_tables.shape[1], cp, sp, B,
+                                        h_q, int(max_q_len), int(max_ctx), float(scale), _stream_ptr(stream)))
+
+
 def kv_window_release(h, table, lens, sink_tokens, window_tokens):
     """Drop the dead pages of every request (table edited in place, -1 marks
     them); returns how many."""
@@ -540,6 +561,15 @@ class Pool:
         paged_attention_decode_window(self.handle, self.desc, layer, out, q, block_tables, context_lens,
                                       max_ctx, scale, sink_tokens, window_tokens, partition_tokens,
                                       workspace, stream)
+        return out
+
+    def prefill(self, layer, q, block_tables, context_lens, query_start, max_q_len, max_ctx, scale, out=None,
+                stream=None):
+        import torch
+        if out is None:
+            out = torch.empty_like(q)
+        paged_attention_prefill(self.handle, self.desc, layer, out, q, block_tables, context_lens, query_start,
+                                max_q_len, max_ctx, scale, stream)
         return out
 
     def window_release(self, table, lens, sink_tokens, window_tokens):

@@ -84,6 +84,9 @@ int launch_append(const kv_pool* pool, int32_t layer, const void* k_new, const v
                   const int32_t* slots, int32_t T, hipStream_t stream);
 int launch_block_copy(const kv_pool* pool, const int32_t* src, const int32_t* dst, int32_t n,
                       hipStream_t stream);
+int launch_prefill(const kv_pool* pool, int32_t layer, void* out, const void* q, const int32_t* tables,
+                   int32_t max_blocks, const int32_t* ctx, const int32_t* qstart, int32_t B, int32_t h_q,
+                   int32_t max_q_len, int32_t max_ctx, float scale, hipStream_t stream);
 
 // Host allocator primitives shared by pool.cpp and prefix.cpp.
 inline bool block_live(const kv_pool* p, int32_t b) {

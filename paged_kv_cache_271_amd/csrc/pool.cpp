@@ -384,6 +384,31 @@ int paged_attention_decode_window(kv_pool* p, int32_t layer, void* out, const vo
   return launch_decode(a, static_cast<hipStream_t>(stream));
 }
 
+int paged_attention_prefill(kv_pool* p, int32_t layer, void* out, const void* q, int32_t q_dtype,
+                            const int32_t* tables, int32_t max_blocks, const int32_t* ctx,
+                            const int32_t* query_start, int32_t B, int32_t h_q, int32_t max_q_len,
+                            int32_t max_ctx, float scale, void* stream) {
+  if (!p) return fail(KV_E_INVALID, "NULL pool");
+  const kv_pool_desc& d = p->desc;
+  if (layer < 0 || layer >= d.num_layers) return fail(KV_E_INVALID, "layer %d out of range", layer);
+  if (B < 0 || max_q_len < 0) return fail(KV_E_INVALID, "negative size");
+  if (B == 0 || max_q_len == 0) return ok();
+  if (B > 65535) return fail(KV_E_UNSUPPORTED, "batch %d above 65535", B);
+  if (d.cache_dtype != KV_BF16) return fail(KV_E_UNSUPPORTED, "prefill attention is built for bf16 pools");
+  if (q_dtype != KV_BF16) return fail(KV_E_UNSUPPORTED, "q dtype %d: bf16 queries only", q_dtype);
+  if (!out || !q || !tables || !ctx || !query_start) return fail(KV_E_INVALID, "NULL device array");
+  if (h_q <= 0 || h_q % d.num_kv_heads != 0)
+    return fail(KV_E_INVALID, "h_q %d is not a positive multiple of %d KV heads", h_q, d.num_kv_heads);
+  if (h_q / d.num_kv_heads > 64)
+    return fail(KV_E_UNSUPPORTED, "%d query heads per KV head (at most 64)", h_q / d.num_kv_heads);
+  if (max_blocks <= 0 || max_ctx < 0 || int64_t(max_ctx) > int64_t(max_blocks) * d.block_size)
+    return fail(KV_E_INVALID, "max_ctx %d outside [0, %d blocks * %d]", max_ctx, max_blocks, d.block_size);
+  const int64_t tiles = (int64_t(max_q_len) + 64 / (h_q / d.num_kv_heads) - 1) / (64 / (h_q / d.num_kv_heads));
+  if (tiles * B > INT32_MAX) return fail(KV_E_UNSUPPORTED, "too many query tiles");
+  return launch_prefill(p, layer, out, q, tables, max_blocks, ctx, query_start, B, h_q, max_q_len, max_ctx, scale,
+                        static_cast<hipStream_t>(stream));
+}
+
 int kv_window_release(kv_pool* p, int32_t B, int32_t* table, int32_t max_blocks, const int32_t* lens,
                       int32_t sink, int32_t window, int32_t* n_released) {
   if (!p || !n_released) return fail(KV_E_INVALID, "NULL argument");
