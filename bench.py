@@ -40,10 +40,11 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode-attention KV GB/s (% of HBM peak) + µs/step, Llama-3-8B shape"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix peak of MI355X
 EVENT_EVERY = 8
 DEFAULT_LAYERS = {"llama3_8b": 32, "llama3_70b_long": 8, "fp8": 16, "int8": 16, "llama3_8b_window": 4}
 DEFAULT_SEED = {"llama3_8b": 2, "llama3_70b_long": 3, "fp8": 5, "int8": 5, "prefix_churn": 4, "cow_fork": 6,
-                "llama3_8b_window": 7}
+                "llama3_8b_window": 7, "prefill": 8}
 
 # HBM bytes (read + written) per launch of decode_stream_kernel in the default
 # step of each workload, from the rocprofv3 FETCH_SIZE and WRITE_SIZE runs in
@@ -72,7 +73,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--workload", default="llama3_8b",
                     choices=["llama3_8b", "llama3_70b_long", "fp8", "int8", "prefix_churn", "cow_fork",
-                             "llama3_8b_window"])
+                             "llama3_8b_window", "prefill"])
     ap.add_argument("--layers", type=int, default=0, help="layers in the pool (0: workload default)")
     ap.add_argument("--seed", type=int, default=-1, help="input seed (-1: workload default)")
     ap.add_argument("--partition", type=int, default=0,
@@ -379,6 +380,60 @@ def cow_fork_workload(args, torch, synth, pk, dev):
                 metric="kv_block_copy GB/s (read + written), copy-on-write forks")
 
 
+def prefill_workload(args, torch, synth, pk, dev):
+    """Prompt processing: 8 Llama-3-8B-shaped requests (h_q 32, h_kv 8, d 128)
+    of 2048 new tokens each, their K/V already in a 4-layer pool; a step is
+    one paged_attention_prefill call for one layer (layers rotate).  value =
+    attention FLOP per second (2 per multiply-add: 2 d for each score and 2 d
+    for each weighted V row, causal keys only)."""
+    B, P, L, H, D, h_q = 8, 2048, 4, 8, 128, 32
+    rng = synth.streams(args.seed)
+    N = B * P // 16
+    pool = pk.Pool(L, N, H, D, "bf16", dev, initial_free_order=synth.permutation(rng["free_order"], N))
+    table = np.zeros((B, P // 16), np.int32)
+    lens = np.zeros(B, np.int32)
+    slots = pool.batch_reserve(table, lens, np.full(B, P, np.int32))
+    d_slots = torch.from_numpy(slots).to(dev)
+    for layer in range(L):
+        k = synth.device_normal((B * P, H, D), 4000 + 2 * layer, dev, torch.bfloat16)
+        v = synth.device_normal((B * P, H, D), 4001 + 2 * layer, dev, torch.bfloat16)
+        pool.append(layer, k, v, d_slots)
+        del k, v
+    q_all = synth.device_normal((L, B * P, h_q, D), 4100, dev, torch.bfloat16)
+    out = torch.empty((B * P, h_q, D), dtype=torch.bfloat16, device=dev)
+    d_table = torch.from_numpy(table).to(dev)
+    d_lens = torch.from_numpy(lens).to(dev)
+    d_qs = torch.from_numpy(np.arange(B + 1, dtype=np.int32) * P).to(dev)
+    flops = B * (P * (P + 1) // 2) * h_q * 4 * D
+    scale = 1.0 / math.sqrt(D)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        pool.prefill(i % L, q_all[i % L], d_table, d_lens, d_qs, P, P, scale, out=out)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events = [(TimingEvent(), TimingEvent()) if j % EVENT_EVERY == 0 else None for j in range(args.steps)]
+    t0 = time.perf_counter()
+    for j in range(args.steps):
+        step(args.warmup + j, events[j])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec_ms = np.array([e[0].elapsed_ms(e[1]) for e in events if e is not None])
+    config = {"workload": "llama3_8b_prefill_layer", "batch": B, "new_tokens": P, "h_q": h_q, "h_kv": H,
+              "head_dim": D, "cache_dtype": "bf16", "layers_in_pool": L, "flop_per_step": flops}
+    return dict(wall=wall, kv_total=float(flops) * args.steps, dec_ms=dec_ms,
+                dec_kv=np.full(len(dec_ms), float(flops)), config=config, cpu=None, traffic=None, dtype="bf16",
+                kernel="paged_attention_prefill call (prefill_kernel)",
+                metric="paged prefill attention TFLOP/s (causal, bf16 MFMA)", unit="TFLOP/s",
+                bound="mfma", peak=MFMA_BF16_PEAK_TFLOPS, scale=1e12)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -401,26 +456,32 @@ def main():
         r = churn_workload(args, torch, synth, pk, dev)
     elif args.workload == "cow_fork":
         r = cow_fork_workload(args, torch, synth, pk, dev)
+    elif args.workload == "prefill":
+        r = prefill_workload(args, torch, synth, pk, dev)
     else:
         r = decode_workload(args, torch, synth, pk, dev)
-    value = r["kv_total"] / r["wall"] / 1e9
+    # the metric's unit: GB/s (bytes per 1e9 s^-1) unless the workload counts FLOP
+    unit_scale = r.get("scale", 1e9)
+    unit = r.get("unit", "GB/s")
+    peak = r.get("peak", HBM_PEAK_GBS)
+    value = r["kv_total"] / r["wall"] / unit_scale
     ms_per_step = r["wall"] / args.steps * 1e3
     mean_kv = r["kv_total"] / args.steps
-    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step, {value:.0f} GB/s")
+    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step, {value:.0f} {unit}")
     roofline = None
     if r["dec_ms"] is not None:
         dec_mean_s = float(r["dec_ms"].mean()) / 1e3
-        achieved = float(r["dec_kv"].mean()) / dec_mean_s / 1e9
-        log(f"decode call {dec_mean_s * 1e6:.1f} us mean over {len(r['dec_ms'])} calls "
+        achieved = float(r["dec_kv"].mean()) / dec_mean_s / unit_scale
+        log(f"timed call {dec_mean_s * 1e6:.1f} us mean over {len(r['dec_ms'])} calls "
             f"(p10 {np.percentile(r['dec_ms'], 10) * 1e3:.1f}, p90 {np.percentile(r['dec_ms'], 90) * 1e3:.1f}), "
-            f"{achieved:.0f} GB/s")
+            f"{achieved:.0f} {unit}")
         roofline = {
-            "bound": "hbm",
+            "bound": r.get("bound", "hbm"),
             "kernel": r["kernel"],
             "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "peak": peak,
+            "unit": unit,
+            "frac": round(achieved / peak, 4),
             "traffic": r.get("traffic"),
             "traffic_note": "HBM bytes read + written per decode_stream_kernel launch (rocprofv3 "
                             "FETCH_SIZE/WRITE_SIZE, copy-calibrated); null if the kernel source changed",
@@ -429,12 +490,13 @@ def main():
         }
     config = dict(r["config"])
     config["us_per_step"] = round(ms_per_step * 1e3, 2)
-    config["hbm_fraction"] = round(value / HBM_PEAK_GBS, 4)
-    config["kv_bytes_per_step"] = int(mean_kv)
+    if unit == "GB/s":
+        config["hbm_fraction"] = round(value / HBM_PEAK_GBS, 4)
+        config["kv_bytes_per_step"] = int(mean_kv)
     res = {
         "metric": r.get("metric", METRIC),
         "value": round(value, 1),
-        "unit": "GB/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,

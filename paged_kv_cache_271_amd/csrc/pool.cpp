@@ -399,11 +399,12 @@ int paged_attention_prefill(kv_pool* p, int32_t layer, void* out, const void* q,
   if (!out || !q || !tables || !ctx || !query_start) return fail(KV_E_INVALID, "NULL device array");
   if (h_q <= 0 || h_q % d.num_kv_heads != 0)
     return fail(KV_E_INVALID, "h_q %d is not a positive multiple of %d KV heads", h_q, d.num_kv_heads);
-  if (h_q / d.num_kv_heads > 64)
-    return fail(KV_E_UNSUPPORTED, "%d query heads per KV head (at most 64)", h_q / d.num_kv_heads);
+  if (h_q / d.num_kv_heads > 128)
+    return fail(KV_E_UNSUPPORTED, "%d query heads per KV head (at most 128)", h_q / d.num_kv_heads);
   if (max_blocks <= 0 || max_ctx < 0 || int64_t(max_ctx) > int64_t(max_blocks) * d.block_size)
     return fail(KV_E_INVALID, "max_ctx %d outside [0, %d blocks * %d]", max_ctx, max_blocks, d.block_size);
-  const int64_t tiles = (int64_t(max_q_len) + 64 / (h_q / d.num_kv_heads) - 1) / (64 / (h_q / d.num_kv_heads));
+  const int64_t tpt = 128 / (h_q / d.num_kv_heads);  // tokens per 128-row query tile
+  const int64_t tiles = (int64_t(max_q_len) + tpt - 1) / tpt;
   if (tiles * B > INT32_MAX) return fail(KV_E_UNSUPPORTED, "too many query tiles");
   return launch_prefill(p, layer, out, q, tables, max_blocks, ctx, query_start, B, h_q, max_q_len, max_ctx, scale,
                         static_cast<hipStream_t>(stream));

@@ -10,11 +10,12 @@
 // ctx - n_q + i) attends to positions <= its own, every query head h reading
 // kv head h / G.
 //
-// Work split: one workgroup per (request, kv head, query tile).  A tile is 64
-// rows, each a (token, query head of the group) pair: 64 / G tokens times the
-// G heads, so the G heads share every K/V load.  The keys stream in chunks of
-// 64 (four pages) staged through LDS by the whole workgroup; each of the four
-// waves runs 16 rows with v_mfma_f32_16x16x32_bf16:
+// Work split: one workgroup per (request, kv head, query tile).  A tile is
+// 128 rows, each a (token, query head of the group) pair: 128 / G tokens times
+// the G heads, so the G heads share every K/V load.  The keys stream in chunks
+// of 64 (four pages) staged through LDS by the whole workgroup; each of the
+// four waves runs 32 rows (two 16-row MFMA tiles, so every K and V operand
+// read from LDS serves both) with v_mfma_f32_16x16x32_bf16:
 //   scores  S^T[token][row] = K[token][:] . Q^T[:][row]
 //   output  O^T[dim][row]  += V^T[dim][token] . P^T[token][row]
 // with the same lane layout as the decode (lane group q of a 32-token block
@@ -31,7 +32,8 @@ namespace {
 
 constexpr int kBS = kBlockSize;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kRows = 64;      // query rows per workgroup
+constexpr int kRT = 2;                 // 16-row MFMA tiles per wave
+constexpr int kRows = 4 * 16 * kRT;    // query rows per workgroup
 constexpr int kChunk = 64;     // keys per staged chunk (4 pages)
 
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
@@ -49,7 +51,7 @@ __device__ inline f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
                                                  0, 0);
 }
 
-// grid (B * tiles, H); 256 threads.  tpt = tokens per tile = 64 / G.
+// grid (B * tiles, H); 256 threads.  tpt = tokens per tile = kRows / G.
 template <int D>
 __global__ void __launch_bounds__(256)
 prefill_kernel(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc, const uint16_t* __restrict__ q,
@@ -75,26 +77,33 @@ prefill_kernel(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
   if (tok0 >= n_q) return;
   const int tok_end = min(tok0 + tpt, n_q);
 
-  // this lane's query row: (token tok0 + row / G, head row % G)
-  const int row = 16 * w + c;
-  const int tl = row / G;
-  const bool valid = tl < tpt && tok0 + tl < tok_end;
-  const int tok = tok0 + (valid ? tl : 0);
-  const int head = g * G + row % G;
-  const int pos = max(ctx - n_q + tok, 0);  // last key this row reads
-  const int64_t qrow = int64_t(q0 + tok) * h_q + head;
-  u32x4 qv[KK];
+  // this lane's query rows (one per row tile): (token tok0 + row / G, head row % G)
+  bool valid[kRT];
+  int pos[kRT];
+  int64_t qrow[kRT];
+  u32x4 qv[kRT][KK];
+  float m[kRT], l[kRT];
+  f32x4 acc[kRT][T8];
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    u32x4 v = {0, 0, 0, 0};
-    if (valid) v = *reinterpret_cast<const u32x4*>(q + qrow * D + 32 * kk + 8 * qg);
-    qv[kk] = v;
+  for (int rt = 0; rt < kRT; ++rt) {
+    const int row = 16 * (kRT * w + rt) + c;
+    const int tl = row / G;
+    valid[rt] = tl < tpt && tok0 + tl < tok_end;
+    const int tok = tok0 + (valid[rt] ? tl : 0);
+    const int head = g * G + row % G;
+    pos[rt] = max(ctx - n_q + tok, 0);  // last key this row reads
+    qrow[rt] = int64_t(q0 + tok) * h_q + head;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4 v = {0, 0, 0, 0};
+      if (valid[rt]) v = *reinterpret_cast<const u32x4*>(q + qrow[rt] * D + 32 * kk + 8 * qg);
+      qv[rt][kk] = v;
+    }
+    m[rt] = -INFINITY;
+    l[rt] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < T8; ++t) acc[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-
-  float m = -INFINITY, l = 0.0f;
-  f32x4 acc[T8];
-#pragma unroll
-  for (int t = 0; t < T8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int n_keys = min(ctx, max(ctx - n_q + tok_end, 0));  // keys the tile reads
   const int32_t* trow = tables + int64_t(b) * max_blocks;
@@ -139,64 +148,76 @@ prefill_kernel(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       if (k0 + 32 * kb >= n_keys) break;
-      f32x4 S[2];
+      f32x4 S[kRT][2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         // A operand row c is token 8 (c / 4) + 4 j + c % 4 of the block, so
         // lane group qg ends up holding tokens 8 qg .. 8 qg + 7
         const int ktok = 32 * kb + 8 * (c >> 2) + 4 * j + (c & 3);
-        S[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt) S[rt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           const u32x4 kv = *reinterpret_cast<const u32x4*>(&s_k[ktok * KS + 32 * kk + 8 * qg]);
-          S[j] = mfma(kv, qv[kk], S[j]);
+#pragma unroll
+          for (int rt = 0; rt < kRT; ++rt) S[rt][j] = mfma(kv, qv[rt][kk], S[rt][j]);
         }
       }
-      // causal mask and online softmax (row = column c of the tiles)
+      // causal mask and online softmax per row (column c of the tiles)
       const int base = k0 + 32 * kb + 8 * qg;  // position of this lane's first token
-      float mx = -INFINITY;
+      u32x4 pop[kRT];
+      float alpha[kRT];
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int rt = 0; rt < kRT; ++rt) {
+        float mx = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float s = base + 4 * j + i <= pos ? S[j][i] * scale_log2 : -INFINITY;
-          S[j][i] = s;
-          mx = fmaxf(mx, s);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m, mx);  // finite from the first block on (key 0 <= pos)
-      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-      float ps = 0.0f;
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+          for (int i = 0; i < 4; ++i) {
+            const float s = base + 4 * j + i <= pos[rt] ? S[rt][j][i] * scale_log2 : -INFINITY;
+            S[rt][j][i] = s;
+            mx = fmaxf(mx, s);
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m[rt], mx);  // finite from the first block on (key 0 <= pos)
+        alpha[rt] = __builtin_amdgcn_exp2f(m[rt] - m_new);
+        float ps = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = __builtin_amdgcn_exp2f(S[j][i] - m_new);
-          S[j][i] = e;
-          ps += e;
-        }
-      l = l * alpha + ps;
-      m = m_new;
-      const u32x4 pop = {pack2(S[0][0], S[0][1]), pack2(S[0][2], S[0][3]), pack2(S[1][0], S[1][1]),
-                         pack2(S[1][2], S[1][3])};
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float e = __builtin_amdgcn_exp2f(S[rt][j][i] - m_new);
+            S[rt][j][i] = e;
+            ps += e;
+          }
+        l[rt] = l[rt] * alpha[rt] + ps;
+        m[rt] = m_new;
+        pop[rt] = u32x4{pack2(S[rt][0][0], S[rt][0][1]), pack2(S[rt][0][2], S[rt][0][3]),
+                        pack2(S[rt][1][0], S[rt][1][1]), pack2(S[rt][1][2], S[rt][1][3])};
+      }
 #pragma unroll
       for (int t = 0; t < T8; ++t) {
         const u32x4 vv = *reinterpret_cast<const u32x4*>(&s_v[(16 * t + c) * VS + 32 * kb + 8 * qg]);
-        acc[t] = mfma(vv, pop, acc[t] * alpha);
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt) acc[rt][t] = mfma(vv, pop[rt], acc[rt][t] * alpha[rt]);
       }
     }
   }
 
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  if (valid) {
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
 #pragma unroll
-    for (int t = 0; t < T8; ++t) {
-      const f32x4 o = acc[t] * inv;
-      const u32x2 pk = {pack2(o[0], o[1]), pack2(o[2], o[3])};
-      *reinterpret_cast<u32x2*>(out + qrow * D + 16 * t + 4 * qg) = pk;
+  for (int rt = 0; rt < kRT; ++rt) {
+    float lt = l[rt];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    if (valid[rt]) {
+      const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+#pragma unroll
+      for (int t = 0; t < T8; ++t) {
+        const f32x4 o = acc[rt][t] * inv;
+        const u32x2 pk = {pack2(o[0], o[1]), pack2(o[2], o[3])};
+        *reinterpret_cast<u32x2*>(out + qrow[rt] * D + 16 * t + 4 * qg) = pk;
+      }
     }
   }
 }

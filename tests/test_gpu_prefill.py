@@ -1,7 +1,7 @@
 """GPU parity of paged_attention_prefill (causal attention of each request's
 new tokens over its paged cache) against the fp64 oracle: ragged prompts,
 cached prefixes before the new tokens, page and tile edges, group sizes from
-MHA to 64 query heads per kv head, a NaN-poisoned pool, and Llama-3-8B-shaped
+MHA to 128 query heads per kv head, a NaN-poisoned pool, and Llama-3-8B-shaped
 2048-token prompts at full size (sampled rows)."""
 
 import math
@@ -87,10 +87,10 @@ def test_prefill_ragged_matches_oracle(gpu_lib, D):
         assert_close(got[qs:qe], c.ref(b), "bf16", f"D {D} ctx {CTX[b]} new {NQ[b]}")
 
 
-@pytest.mark.parametrize("H,h_q", [(4, 4), (1, 8), (2, 40), (1, 64), (8, 32)])
+@pytest.mark.parametrize("H,h_q", [(4, 4), (1, 8), (2, 40), (1, 64), (8, 32), (1, 128)])
 def test_prefill_group_sizes(gpu_lib, H, h_q):
-    """MHA (64 tokens a tile), G 8, 20 (3 tokens, 60 rows a tile), 64 (one
-    token a tile), and the Llama-3-8B ratio."""
+    """MHA (128 tokens a tile), G 8, 20 (6 tokens, 120 rows a tile), 64 (two
+    tokens a tile), the Llama-3-8B ratio, and 128 (one token a tile)."""
     c = PrefillCase(H, 128, h_q, [200, 33, 7], [150, 33, 3], seed=63)
     got, _ = c.run()
     for b in range(3):
