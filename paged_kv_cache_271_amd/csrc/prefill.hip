@@ -10,18 +10,30 @@
 // ctx - n_q + i) attends to positions <= its own, every query head h reading
 // kv head h / G.
 //
-// Work split: one workgroup per (request, kv head, query tile).  A tile is
-// 128 rows, each a (token, query head of the group) pair: 128 / G tokens times
-// the G heads, so the G heads share every K/V load.  The keys stream in chunks
-// of 64 (four pages) staged through LDS by the whole workgroup; each of the
-// four waves runs 32 rows (two 16-row MFMA tiles, so every K and V operand
-// read from LDS serves both) with v_mfma_f32_16x16x32_bf16:
-//   scores  S^T[token][row] = K[token][:] . Q^T[:][row]
-//   output  O^T[dim][row]  += V^T[dim][token] . P^T[token][row]
-// with the same lane layout as the decode (lane group q of a 32-token block
-// owns tokens 8q..8q+7, which are exactly its 8 scores), an online softmax
-// per row, and the causal mask applied per (row, token).  Tiles are issued
-// latest first, so the tiles with the most keys start earliest.
+// Work split: one workgroup (4 waves) per (query tile, request, kv head).  A
+// tile is 128 rows, each a (token, query head of the group) pair: 128 / G
+// tokens times the G heads, so the G heads share every K/V load.  Each wave
+// holds 32 rows as two 16-row MFMA tiles, so every K and V operand read from
+// LDS feeds two v_mfma_f32_16x16x32_bf16:
+//   scores  S^T[key][row] = K[key][:] . Q^T[:][row]
+//   output  O^T[dim][row] += V^T[dim][key] . P^T[key][row]
+// Lane group q of a 32-key block owns keys 8q..8q+7, which are exactly its 8
+// scores of each row, so the softmax needs no data movement.
+//
+// Keys stream in chunks of 64 (four pages).  Wave w copies page w of the next
+// chunk from HBM straight into LDS (global_load_lds_dwordx4, no registers)
+// while the workgroup computes on the current one: two LDS buffers, one
+// barrier per chunk.  The copies place 16-byte granules with an XOR swizzle
+// so that the MFMA operand reads of every 16 lanes touch 16 different bank
+// groups.  Softmax per chunk (64 keys): the running row maximum only moves
+// when a chunk's maximum exceeds it by more than 2^8 (then the accumulators
+// are rescaled), otherwise the weights are formed against the stale maximum
+// and stay below 256, which changes no result beyond rounding.  The causal
+// mask is applied only on the chunks that reach a row's own position, and
+// the V rows past the context are zeroed in LDS on the request's last chunk
+// (unwritten slots may hold any bits).  Tiles with the most keys launch
+// first; the tiles of one (request, kv head) share an XCD when B * H is a
+// multiple of 8, so its K/V stays in that XCD's L2.
 
 #include <cstdint>
 
@@ -34,7 +46,11 @@ constexpr int kBS = kBlockSize;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kRT = 2;                 // 16-row MFMA tiles per wave
 constexpr int kRows = 4 * 16 * kRT;    // query rows per workgroup
-constexpr int kChunk = 64;     // keys per staged chunk (4 pages)
+constexpr int kChunk = 64;             // keys per chunk: four pages, one per wave
+constexpr float kSlack = 8.0f;         // log2 headroom of the running maximum
+// s_waitcnt immediates (vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitAll = 0x0070;       // vmcnt(0) lgkmcnt(0)
+constexpr int kWaitLds = 0xC07F;       // lgkmcnt(0)
 
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
@@ -51,24 +67,217 @@ __device__ inline f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
                                                  0, 0);
 }
 
-// grid (B * tiles, H); 256 threads.  tpt = tokens per tile = kRows / G.
+// Barrier with no memory fence: the waits before it are explicit, so copies
+// into the other buffer stay in flight across it.
+template <int kWait>
+__device__ inline void barrier() {
+  __builtin_amdgcn_s_waitcnt(kWait);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One 16-byte piece per lane from global memory straight into LDS: lane i
+// writes bytes [16 i, 16 i + 16) after the wave-uniform address `dst`.
+__device__ inline void copy_to_lds(const uint16_t* src, uint16_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
+// 16-byte granule swizzles.  K buffer: key row r, dim granule g at slot
+// r * (D/8) + (g ^ kswz(r)).  V buffer: page p, dim d, key half h at slot
+// p * 2D + 2d + (h ^ vswz(d)).  A 16-lane operand read then covers 16
+// distinct granule bank groups (8 within each half).
 template <int D>
-__global__ void __launch_bounds__(256)
+__device__ inline int kswz(int r) {
+  const int c = ((r >> 3) & 3) * 4 + (r & 3);
+  return D == 128 ? c : ((c & 7) ^ (c >> 3));
+}
+__device__ inline int vswz(int d) { return ((d >> 2) ^ (d >> 3)) & 1; }
+
+template <int D>
+struct Tile {
+  static constexpr int KK = D / 32;   // MFMA k-steps over the head dimension
+  static constexpr int T8 = D / 16;   // 16-dim output tiles
+  static constexpr int PG = 2 * D;    // 16-byte granules per page tile (16 keys x D x 2 B)
+  static constexpr int NI = PG / 64;  // wave copies per page tile
+  u32x4 qv[kRT][KK];
+  f32x4 acc[kRT][T8];
+  float m[kRT], l[kRT];
+  int pos[kRT];
+  uint32_t kaddr[KK], vaddr;  // LDS read offsets (elements) of this lane's operands
+  uint32_t ksrc[NI], vsrc[NI];  // element offsets within a page tile of this lane's copies
+};
+
+// Copy chunk `ci` (keys 64 ci .. 64 ci + 63): wave w takes page 4 ci + w,
+// clamped to the request's last page (keys past the context are masked and,
+// for V, zeroed before use).
+template <int D>
+__device__ __forceinline__ void issue_chunk(uint16_t* kbuf, uint16_t* vbuf, int ci, int nb, const int32_t* trow,
+                                            const uint16_t* kc, const uint16_t* vc, int H, int g, int w,
+                                            const Tile<D>& t) {
+  constexpr int PG = Tile<D>::PG;
+  const int page = min(ci * (kChunk / kBS) + w, nb - 1);
+  const int64_t tile = (int64_t(trow[page]) * H + g) * kBS * D;
+#pragma unroll
+  for (int m = 0; m < Tile<D>::NI; ++m) {
+    copy_to_lds(kc + tile + t.ksrc[m], kbuf + (w * PG + 64 * m) * 8);
+    copy_to_lds(vc + tile + t.vsrc[m], vbuf + (w * PG + 64 * m) * 8);
+  }
+}
+
+// Zero the V entries of keys >= ctx in a chunk buffer.
+template <int D>
+__device__ __forceinline__ void zero_tail(uint16_t* vbuf, int k0, int ctx, int tid) {
+#pragma unroll
+  for (int u = 0; u < D / 32; ++u) {
+    const int s = tid + 256 * u;
+    const int p = s / (2 * D), rem = s % (2 * D);
+    const int d = rem >> 1, h = (rem & 1) ^ vswz(d);
+    const int valid = ctx - (k0 + kBS * p + 8 * h);  // keys of the granule below ctx
+    if (valid < 8) {
+      u32x4* ptr = reinterpret_cast<u32x4*>(vbuf + 8 * s);
+      u32x4 v = *ptr;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (2 * e >= valid) v[e] = 0;
+        else if (2 * e + 1 >= valid) v[e] &= 0xFFFFu;
+      }
+      *ptr = v;
+    }
+  }
+}
+
+// One chunk: wait for its copies, start the next chunk's copies into the
+// other buffer, then scores, softmax and the weighted sum of V.
+template <int D>
+__device__ __forceinline__ void chunk_step(Tile<D>& t, uint16_t* kcur, uint16_t* vcur, uint16_t* knxt, uint16_t* vnxt,
+                                           int ci, int nch, int nb, int ctx, int pos_min, const int32_t* trow,
+                                           const uint16_t* kc, const uint16_t* vc, int H, int g, int w, int tid,
+                                           int qg, float sl) {
+  constexpr int KK = Tile<D>::KK, T8 = Tile<D>::T8;
+  barrier<kWaitAll>();  // this chunk is in LDS; everyone is done with the other buffer
+  if (ci + 1 < nch) issue_chunk<D>(knxt, vnxt, ci + 1, nb, trow, kc, vc, H, g, w, t);
+  const int k0 = ci * kChunk;
+  if (k0 + kChunk > ctx) {  // the request's last chunk: no copy is in flight
+    zero_tail<D>(vcur, k0, ctx, tid);
+    barrier<kWaitLds>();
+  }
+
+  // scores of keys k0 + 32 kb + 8 qg + 4 j + i (A operand row c is key
+  // 8 (c / 4) + 4 j + c % 4 of the block, so lane group qg gets keys 8 qg ..)
+  f32x4 S[kRT][2][2];
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) S[rt][kb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk)  // eight independent accumulators per k-step
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(kcur + (32 * kb + 4 * j) * D + t.kaddr[kk]);
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt) S[rt][kb][j] = mfma(kv, t.qv[rt][kk], S[rt][kb][j]);
+      }
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) S[rt][kb][j] *= sl;
+  if (k0 + kChunk - 1 > pos_min) {  // some key of the chunk lies after some row of this wave
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = k0 + 32 * kb + 8 * qg + 4 * j + i;
+            S[rt][kb][j][i] = key <= t.pos[rt] ? S[rt][kb][j][i] : -INFINITY;
+          }
+  }
+
+  float mloc[kRT];
+  bool grow = false;
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        mx = fmaxf(fmaxf(mx, fmaxf(S[rt][kb][j][0], S[rt][kb][j][1])), fmaxf(S[rt][kb][j][2], S[rt][kb][j][3]));
+    mloc[rt] = mx;
+    grow |= mx > t.m[rt] + kSlack;
+  }
+  if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // move the running maxima (rare after the first chunk)
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) {
+      float mx = mloc[rt];
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(t.m[rt], mx);  // finite: key 0 is visible to every row
+      const float alpha = __builtin_amdgcn_exp2f(t.m[rt] - m_new);
+      t.m[rt] = m_new;
+      t.l[rt] *= alpha;
+#pragma unroll
+      for (int t8 = 0; t8 < T8; ++t8) t.acc[rt][t8] *= alpha;
+    }
+  }
+
+  u32x4 pop[kRT][2];
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) {
+    float ps = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float e[2][4];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          e[j][i] = __builtin_amdgcn_exp2f(S[rt][kb][j][i] - t.m[rt]);
+          ps += e[j][i];
+        }
+      pop[rt][kb] = u32x4{pack2(e[0][0], e[0][1]), pack2(e[0][2], e[0][3]), pack2(e[1][0], e[1][1]),
+                          pack2(e[1][2], e[1][3])};
+    }
+    t.l[rt] += ps;
+  }
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int t8 = 0; t8 < T8; ++t8) {
+      const u32x4 vv = *reinterpret_cast<const u32x4*>(vcur + t.vaddr + 8 * (4 * D * kb + 32 * t8));
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt) t.acc[rt][t8] = mfma(vv, pop[rt][kb], t.acc[rt][t8]);
+    }
+}
+
+// grid: tiles * B * H workgroups of 256 threads, latest tiles first.
+template <int D>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_kernel(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc, const uint16_t* __restrict__ q,
                uint16_t* __restrict__ out, const int32_t* __restrict__ tables, int max_blocks,
                const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ qstart, int B, int tiles,
                int max_ctx, int H, int h_q, int G, int tpt, float scale_log2) {
-  constexpr int KK = D / 32;     // MFMA k-steps over the head dimension
-  constexpr int T8 = D / 16;     // output dim tiles
-  constexpr int KS = D + 8;      // LDS row stride of K (elements), padded
-  constexpr int VS = kChunk + 8; // LDS row stride of V (elements), padded
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[kChunk * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t s_v[D * VS];
+  using T = Tile<D>;
+  constexpr int KK = T::KK, T8 = T::T8, NI = T::NI, PG = T::PG;
+  __shared__ __attribute__((aligned(16))) uint16_t k_a[kChunk * D];
+  __shared__ __attribute__((aligned(16))) uint16_t v_a[kChunk * D];
+  __shared__ __attribute__((aligned(16))) uint16_t k_b[kChunk * D];
+  __shared__ __attribute__((aligned(16))) uint16_t v_b[kChunk * D];
 
-  const int b = blockIdx.x % B;
-  const int tile = tiles - 1 - blockIdx.x / B;  // latest tiles first
-  const int g = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int bh = B * H;
+  const int tile = tiles - 1 - int(blockIdx.x) / bh;
+  const int b = (int(blockIdx.x) % bh) / H, g = int(blockIdx.x) % H;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, qg = lane >> 4;
   const int q0 = qstart[b];
   const int n_q = qstart[b + 1] - q0;
@@ -77,13 +286,9 @@ prefill_kernel(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
   if (tok0 >= n_q) return;
   const int tok_end = min(tok0 + tpt, n_q);
 
-  // this lane's query rows (one per row tile): (token tok0 + row / G, head row % G)
+  T t;
   bool valid[kRT];
-  int pos[kRT];
   int64_t qrow[kRT];
-  u32x4 qv[kRT][KK];
-  float m[kRT], l[kRT];
-  f32x4 acc[kRT][T8];
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
     const int row = 16 * (kRT * w + rt) + c;
@@ -91,132 +296,64 @@ prefill_kernel(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     valid[rt] = tl < tpt && tok0 + tl < tok_end;
     const int tok = tok0 + (valid[rt] ? tl : 0);
     const int head = g * G + row % G;
-    pos[rt] = max(ctx - n_q + tok, 0);  // last key this row reads
+    t.pos[rt] = max(ctx - n_q + tok, 0);  // last key this row reads
     qrow[rt] = int64_t(q0 + tok) * h_q + head;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       u32x4 v = {0, 0, 0, 0};
       if (valid[rt]) v = *reinterpret_cast<const u32x4*>(q + qrow[rt] * D + 32 * kk + 8 * qg);
-      qv[rt][kk] = v;
+      t.qv[rt][kk] = v;
     }
-    m[rt] = -INFINITY;
-    l[rt] = 0.0f;
+    t.m[rt] = -INFINITY;
+    t.l[rt] = 0.0f;
 #pragma unroll
-    for (int t = 0; t < T8; ++t) acc[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t8 = 0; t8 < T8; ++t8) t.acc[rt][t8] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // smallest position among this wave's rows (rows past the tile take tok0's)
+  const int tl_first = (16 * kRT * w) / G, tl_last = (16 * kRT * w + 16 * kRT - 1) / G;
+  const bool all_valid = tl_last < tpt && tok0 + tl_last < tok_end;
+  const int pos_min = max(ctx - n_q + tok0 + (all_valid ? tl_first : 0), 0);
+
+  // per-lane LDS read offsets (elements) and copy source offsets within a page tile
+  {
+    const int r = 8 * (c >> 2) + (c & 3);
+    const int sw = kswz<D>(r);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) t.kaddr[kk] = r * D + 8 * ((4 * kk + qg) ^ sw);
+  }
+  t.vaddr = 8 * ((qg >> 1) * PG + 2 * c + ((qg & 1) ^ vswz(c)));
+#pragma unroll
+  for (int m = 0; m < NI; ++m) {
+    const int s = 64 * m + lane;  // granule of the page tile, in LDS order
+    const int rl = s / (D / 8), slot = s % (D / 8);
+    t.ksrc[m] = rl * D + 8 * (slot ^ kswz<D>(kBS * w + rl));
+    const int d = s >> 1;
+    t.vsrc[m] = d * kBS + 8 * ((s & 1) ^ vswz(d));
   }
 
   const int n_keys = min(ctx, max(ctx - n_q + tok_end, 0));  // keys the tile reads
+  const int nch = (n_keys + kChunk - 1) / kChunk;
+  const int nb = (ctx + kBS - 1) / kBS;
   const int32_t* trow = tables + int64_t(b) * max_blocks;
-  for (int k0 = 0; k0 < n_keys; k0 += kChunk) {
-    // ---- stage four pages of K (token-major) and V (dim-major) in LDS;
-    // positions at or past ctx are zeroed so stale bytes never reach a sum
-    __syncthreads();
-    constexpr int PC = kBS * D / 8;  // 16-byte pieces per page tile
-#pragma unroll
-    for (int u = 0; u < 4 * PC / 256; ++u) {
-      const int k = tid + 256 * u;
-      const int pg = k / PC, in = k % PC;
-      const int page = k0 / kBS + pg;
-      const bool live = page * kBS < n_keys;
-      const int64_t tile_off = live ? (int64_t(trow[page]) * H + g) * kBS * D : 0;
-      // K piece: token in / (D/8), dims 8 * (in % (D/8))
-      {
-        const int r = in / (D / 8), c8 = in % (D / 8);
-        u32x4 v = {0, 0, 0, 0};
-        if (live && page * kBS + r < ctx) v = *reinterpret_cast<const u32x4*>(kc + tile_off + r * D + 8 * c8);
-        *reinterpret_cast<u32x4*>(&s_k[(pg * kBS + r) * KS + 8 * c8]) = v;
-      }
-      // V piece: dim in / 2, tokens 8 * (in % 2) .. + 7 of the page
-      {
-        const int d = in / 2, h8 = in % 2;
-        u32x4 v = {0, 0, 0, 0};
-        if (live) {
-          v = *reinterpret_cast<const u32x4*>(vc + tile_off + d * kBS + 8 * h8);
-          const int valid_t = ctx - (page * kBS + 8 * h8);  // tokens of the 8 before ctx
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (2 * e >= valid_t) v[e] = 0;
-            else if (2 * e + 1 >= valid_t) v[e] &= 0xFFFFu;
-          }
-        }
-        *reinterpret_cast<u32x4*>(&s_v[d * VS + pg * kBS + 8 * h8]) = v;
-      }
-    }
-    __syncthreads();
-
-    // ---- two 32-token blocks of the chunk
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (k0 + 32 * kb >= n_keys) break;
-      f32x4 S[kRT][2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        // A operand row c is token 8 (c / 4) + 4 j + c % 4 of the block, so
-        // lane group qg ends up holding tokens 8 qg .. 8 qg + 7
-        const int ktok = 32 * kb + 8 * (c >> 2) + 4 * j + (c & 3);
-#pragma unroll
-        for (int rt = 0; rt < kRT; ++rt) S[rt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const u32x4 kv = *reinterpret_cast<const u32x4*>(&s_k[ktok * KS + 32 * kk + 8 * qg]);
-#pragma unroll
-          for (int rt = 0; rt < kRT; ++rt) S[rt][j] = mfma(kv, qv[rt][kk], S[rt][j]);
-        }
-      }
-      // causal mask and online softmax per row (column c of the tiles)
-      const int base = k0 + 32 * kb + 8 * qg;  // position of this lane's first token
-      u32x4 pop[kRT];
-      float alpha[kRT];
-#pragma unroll
-      for (int rt = 0; rt < kRT; ++rt) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float s = base + 4 * j + i <= pos[rt] ? S[rt][j][i] * scale_log2 : -INFINITY;
-            S[rt][j][i] = s;
-            mx = fmaxf(mx, s);
-          }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m[rt], mx);  // finite from the first block on (key 0 <= pos)
-        alpha[rt] = __builtin_amdgcn_exp2f(m[rt] - m_new);
-        float ps = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float e = __builtin_amdgcn_exp2f(S[rt][j][i] - m_new);
-            S[rt][j][i] = e;
-            ps += e;
-          }
-        l[rt] = l[rt] * alpha[rt] + ps;
-        m[rt] = m_new;
-        pop[rt] = u32x4{pack2(S[rt][0][0], S[rt][0][1]), pack2(S[rt][0][2], S[rt][0][3]),
-                        pack2(S[rt][1][0], S[rt][1][1]), pack2(S[rt][1][2], S[rt][1][3])};
-      }
-#pragma unroll
-      for (int t = 0; t < T8; ++t) {
-        const u32x4 vv = *reinterpret_cast<const u32x4*>(&s_v[(16 * t + c) * VS + 32 * kb + 8 * qg]);
-#pragma unroll
-        for (int rt = 0; rt < kRT; ++rt) acc[rt][t] = mfma(vv, pop[rt], acc[rt][t] * alpha[rt]);
-      }
-    }
+  if (nch > 0) issue_chunk<D>(k_a, v_a, 0, nb, trow, kc, vc, H, g, w, t);
+  for (int ci = 0; ci < nch; ci += 2) {
+    chunk_step<D>(t, k_a, v_a, k_b, v_b, ci, nch, nb, ctx, pos_min, trow, kc, vc, H, g, w, tid, qg, scale_log2);
+    if (ci + 1 < nch)
+      chunk_step<D>(t, k_b, v_b, k_a, v_a, ci + 1, nch, nb, ctx, pos_min, trow, kc, vc, H, g, w, tid, qg, scale_log2);
   }
 
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
-    float lt = l[rt];
+    float lt = t.l[rt];
     lt += __shfl_xor(lt, 16);
     lt += __shfl_xor(lt, 32);
     if (valid[rt]) {
       const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
 #pragma unroll
-      for (int t = 0; t < T8; ++t) {
-        const f32x4 o = acc[rt][t] * inv;
+      for (int t8 = 0; t8 < T8; ++t8) {
+        const f32x4 o = t.acc[rt][t8] * inv;
         const u32x2 pk = {pack2(o[0], o[1]), pack2(o[2], o[3])};
-        *reinterpret_cast<u32x2*>(out + qrow[rt] * D + 16 * t + 4 * qg) = pk;
+        *reinterpret_cast<u32x2*>(out + qrow[rt] * D + 16 * t8 + 4 * qg) = pk;
       }
     }
   }
@@ -236,7 +373,7 @@ int launch_prefill(const kv_pool* p, int32_t layer, void* out, const void* q, co
   const int64_t lo = int64_t(layer) * layer_elems(d);
   const auto* kc = static_cast<const uint16_t*>(p->k_cache) + lo;
   const auto* vc = static_cast<const uint16_t*>(p->v_cache) + lo;
-  const dim3 grid(uint32_t(int64_t(B) * tiles), H);
+  const dim3 grid(uint32_t(int64_t(tiles) * B * H));
   const float sl = scale * kLog2e;
   if (d.head_dim == 128)
     prefill_kernel<128><<<grid, 256, 0, stream>>>(kc, vc, static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
