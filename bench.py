@@ -44,7 +44,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix peak of MI355X
 EVENT_EVERY = 8
 DEFAULT_LAYERS = {"llama3_8b": 32, "llama3_70b_long": 8, "fp8": 16, "int8": 16, "llama3_8b_window": 4}
 DEFAULT_SEED = {"llama3_8b": 2, "llama3_70b_long": 3, "fp8": 5, "int8": 5, "prefix_churn": 4, "cow_fork": 6,
-                "llama3_8b_window": 7, "prefill": 8}
+                "llama3_8b_window": 7, "prefill": 8, "ctx_sweep": 2}
 
 # HBM bytes (read + written) per launch of decode_stream_kernel in the default
 # step of each workload, from the rocprofv3 FETCH_SIZE and WRITE_SIZE runs in
@@ -74,7 +74,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--workload", default="llama3_8b",
                     choices=["llama3_8b", "llama3_70b_long", "fp8", "int8", "prefix_churn", "cow_fork",
-                             "llama3_8b_window", "prefill"])
+                             "llama3_8b_window", "prefill", "ctx_sweep"])
     ap.add_argument("--layers", type=int, default=0, help="layers in the pool (0: workload default)")
     ap.add_argument("--seed", type=int, default=-1, help="input seed (-1: workload default)")
     ap.add_argument("--partition", type=int, default=0,
@@ -143,13 +143,14 @@ def copy_calibration(torch, dev):
     log("copy calibration: 1 GiB read + 1 GiB written by one copy kernel")
 
 
-def decode_workload(args, torch, synth, pk, dev):
-    """Single-layer decode steps over a multi-layer pool (see the module doc)."""
+def decode_workload(args, torch, synth, pk, dev, spec=None, layers=0):
+    """Single-layer decode steps over a multi-layer pool (see the module doc).
+    `spec` / `layers` replace the workload's shape and pool depth (sweeps)."""
     name = args.workload
-    w = synth.WORKLOADS[name]
+    w = spec or synth.WORKLOADS[name]
     dtype = w["dtype"]
     B, H, h_q, D = w["batch"], w["h_kv"], w["h_q"], w["head_dim"]
-    L = args.layers or DEFAULT_LAYERS[name]
+    L = layers or args.layers or DEFAULT_LAYERS[name]
     elem = 1 if dtype in ("fp8", "int8") else 2
     outlier = w.get("outlier_p", 0.0)
     total = args.warmup + args.steps
@@ -268,7 +269,7 @@ def decode_workload(args, torch, synth, pk, dev):
     dec_kv = np.array([per_step_kv[j] for j in range(args.steps) if events[j] is not None], float)
 
     cpu = None
-    if name == "llama3_8b" and not args.no_cpu_baseline:
+    if name == "llama3_8b" and spec is None and not args.no_cpu_baseline:
         cpu = cpu_baseline(ctx0, T0, k_new, v_new, q_all, args, B, H, h_q, D, L, dev)
     config = {
         "workload": f"{name}_decode_layer",
@@ -283,6 +284,53 @@ def decode_workload(args, torch, synth, pk, dev):
                 kernel=("paged_attention_decode_window" if window else
                         "paged_attention_decode" if two_calls else "paged_attention_decode_append")
                 + " call (decode_stream_kernel + stream_reduce_kernel)")
+
+
+SWEEP_CTX = (512, 1024, 2048, 4096, 8192, 16384)
+
+
+def ctx_sweep_workload(args, torch, synth, pk, dev):
+    """The Llama-3-8B batch (64 requests) with one fixed context length per
+    point, the fused step timed at each: the call time should be affine in the
+    total context, t = a + bytes / R.  Reports R (the streaming rate) as the
+    value, with the per-point times and the fixed cost a."""
+    base = dict(synth.WORKLOADS["llama3_8b"])
+    base.pop("ctx_range")
+    B, H, D = base["batch"], base["h_kv"], base["head_dim"]
+    pts = []
+    last = None
+    for c in SWEEP_CTX:
+        spec = dict(base, contexts=tuple([c] * B))
+        per_layer = B * c * H * D * 2 * 2
+        layers = max(2, -(-4 * 10 ** 9 // per_layer))  # >= 4 GB of pool: every step reads cold lines
+        r = decode_workload(args, torch, synth, pk, dev, spec=spec, layers=layers)
+        call_us = float(r["dec_ms"].mean()) * 1e3
+        kv = float(r["dec_kv"].mean())
+        pts.append((c, kv, call_us, r["wall"] / args.steps * 1e6))
+        log(f"ctx {c}: {kv / 1e6:.1f} MB, call {call_us:.1f} us ({kv / call_us / 1e3:.0f} GB/s), "
+            f"step {pts[-1][3]:.1f} us")
+        last = r
+        torch.cuda.empty_cache()
+    x = np.array([p[1] for p in pts])
+    y = np.array([p[2] for p in pts])
+    slope, icept = np.polyfit(x, y, 1)          # us per byte, us
+    fit = icept + slope * x
+    r2 = 1.0 - float(((y - fit) ** 2).sum()) / float(((y - y.mean()) ** 2).sum())
+    rate = 1.0 / slope / 1e3                     # GB/s
+    log(f"affine fit: call = {icept:.1f} us + bytes / {rate:.0f} GB/s (R^2 {r2:.5f})")
+    config = {"workload": "llama3_8b_ctx_sweep", "batch": B, "h_q": base["h_q"], "h_kv": H, "head_dim": D,
+              "block_size": 16, "cache_dtype": "bf16", "step": "paged_attention_decode_append",
+              "ctx_points": list(SWEEP_CTX),
+              "kv_bytes": [int(p[1]) for p in pts],
+              "us_per_call": [round(p[2], 2) for p in pts],
+              "us_per_step_points": [round(p[3], 2) for p in pts],
+              "fit_fixed_us": round(float(icept), 2), "fit_rate_gbs": round(rate, 1), "fit_r2": round(r2, 6)}
+    return dict(wall=last["wall"], kv_total=last["kv_total"], dec_ms=last["dec_ms"], dec_kv=last["dec_kv"],
+                config=config, cpu=None, traffic=None, traffic_note="HBM counters not taken for this sweep",
+                dtype="bf16", value=rate, metric="paged decode call: streaming rate of the affine fit "
+                "over context length (GB/s), Llama-3-8B shape",
+                kernel="paged_attention_decode_append call at the longest context (decode_stream_kernel + "
+                       "stream_reduce_kernel)")
 
 
 def churn_workload(args, torch, synth, pk, dev):
@@ -459,13 +507,15 @@ def main():
         r = cow_fork_workload(args, torch, synth, pk, dev)
     elif args.workload == "prefill":
         r = prefill_workload(args, torch, synth, pk, dev)
+    elif args.workload == "ctx_sweep":
+        r = ctx_sweep_workload(args, torch, synth, pk, dev)
     else:
         r = decode_workload(args, torch, synth, pk, dev)
     # the metric's unit: GB/s (bytes per 1e9 s^-1) unless the workload counts FLOP
     unit_scale = r.get("scale", 1e9)
     unit = r.get("unit", "GB/s")
     peak = r.get("peak", HBM_PEAK_GBS)
-    value = r["kv_total"] / r["wall"] / unit_scale
+    value = r["value"] if "value" in r else r["kv_total"] / r["wall"] / unit_scale
     ms_per_step = r["wall"] / args.steps * 1e3
     mean_kv = r["kv_total"] / args.steps
     log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step, {value:.0f} {unit}")

@@ -151,17 +151,21 @@ __device__ inline uint16_t to_out<uint16_t>(float x) { return uint16_t(f2bf_bits
 //
 // The work of the whole batch is a list of units (request b, kv-head group gh,
 // block j), ordered by b, then gh, then j; one kv-head group is a kv-head and
-// up to 16 of its query heads.  The list is cut into equal chunks of C units
-// and every wave streams whole chunks: a chunk is a run of segments, each a
+// up to 16 of its query heads.  The list is cut into chunks of consecutive
+// units and every wave streams whole chunks: a chunk is a run of segments, each a
 // range of blocks of one (b, gh).  A segment that covers all of its (b, gh)
 // is finished in place and written to `out`; the others (at most the first
 // and the last of a chunk) store their (m, l, acc) state in the workspace and
 // stream_reduce_kernel merges the pieces of each (b, gh) in chunk order.
-// C = ceil(units / workers) by default, so every wave gets the same number
-// of blocks whatever the context lengths; a caller-chosen chunk length forces
+// By default the units are cut into one chunk per worker (or per unit when
+// there are fewer), sizes differing by at most one, so every wave gets the
+// same number of blocks
+// whatever the context lengths; a caller-chosen chunk length forces
 // more pieces (each wave then takes every workers-th chunk).  When the number
 // of kv-head groups is a multiple of four, a workgroup's four waves move
-// together over four adjacent groups (see the kernel).
+// together over four adjacent groups (see the kernel).  Waves lower their
+// issue priority as their chunk completes (progress_prio), so the workgroups
+// sharing a CU finish together.
 //
 // Inside a segment a wave takes NB = 2 blocks per step.  Lane group q (lanes
 // 16q..16q+15) owns tokens 8(q&1)..8(q&1)+7 of block q>>1 of the step:
@@ -211,6 +215,29 @@ __device__ inline u32x4 mask_bits(u32x4 v, uint32_t keep) {
   return v;
 }
 
+// Wave issue priority from the progress of the wave's chunk: `done` of `total`
+// units streamed.  Waves of the three workgroups that share a CU would
+// otherwise issue oldest first, so the first-dispatched workgroup runs ahead
+// and the last ones finish long after it with the CU half idle; lowering the
+// priority as a chunk completes lets the lagging waves catch up.  Both values
+// are wave-uniform (scalar branches); total = 0 leaves the priority alone.
+__device__ inline int64_t uniform64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(x)));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(x) >> 32));
+  return int64_t((uint64_t(hi) << 32) | lo);
+}
+
+__device__ inline void progress_prio(int64_t done, int64_t total) {
+  done = uniform64(done);
+  total = uniform64(total);
+  if (total <= 0) return;
+  const int64_t x = done * 20;
+  if (x < 12 * total) __builtin_amdgcn_s_setprio(3);
+  else if (x < 17 * total) __builtin_amdgcn_s_setprio(2);
+  else if (x < 19 * total) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // Stream blocks [j0, j1) of one (request, kv-head) into the wave state.
 // Positions at or past ctx are masked.  WIN: so are positions in
 // [sink, win_lo) (a sliding window with attention sinks).
@@ -220,7 +247,7 @@ __device__ inline void run_segment(WaveState<D>& st, const uint8_t* __restrict__
                                    const float* __restrict__ vscale, const int32_t* __restrict__ trow,
                                    int ctx, int H, int g, int j0, int j1, float scale_log2,
                                    const u32x4 (&qv)[D / 32], int r, int grp, int sink = 0,
-                                   int win_lo = 0) {
+                                   int win_lo = 0, int64_t done0 = 0, int64_t total = 0) {
   constexpr int NB = kStreamNB;
   constexpr int KK = D / 32;
   constexpr int T8 = D / 16;
@@ -234,6 +261,7 @@ __device__ inline void run_segment(WaveState<D>& st, const uint8_t* __restrict__
   int32_t tK = trow[min(j0 + kb_rel, jlast)];
   int32_t tV = trow[min(j0 + vb_rel, jlast)];
   for (int cb = j0; cb < j1; cb += NB) {
+    progress_prio(done0 + (cb - j0), total);
     const int bK = cb + kb_rel;
     const int bV = cb + vb_rel;
     const bool vK = bK < j1;
@@ -454,6 +482,22 @@ __device__ inline void block_prefix_blocks(int32_t* s_pref, int32_t* s_tmp, cons
   __syncthreads();
 }
 
+// The chunks of the unit list [0, U) for W workers (shared by the decode and
+// reduce kernels).  Fixed: chunk c holds [c C, c C + C) and worker w takes
+// chunks w, w + W, ...  Balanced: N = min(W, U) chunks, one per worker, chunk c
+// holding [c U / N, (c + 1) U / N).  No chunk is empty and chunk ids follow
+// the unit order, so the chunks holding one (b, gh) are consecutive.
+struct StreamChunks {
+  int64_t U, C, N;
+  __device__ StreamChunks(int64_t U_, int W, int chunk_fixed) : U(U_), C(chunk_fixed) {
+    N = C > 0 ? (U + C - 1) / C : min<int64_t>(W, U);
+  }
+  __device__ int64_t start(int64_t c) const { return C > 0 ? c * C : c * U / N; }
+  __device__ int64_t end(int64_t c) const { return C > 0 ? min(U, c * C + C) : (c + 1) * U / N; }
+  // chunk holding unit x (0 <= x < U)
+  __device__ int64_t chunk_of(int64_t x) const { return C > 0 ? x / C : ((x + 1) * N - 1) / U; }
+};
+
 // grid = workers / 4 workgroups of 256 threads; chunk_fixed = 0 for balanced chunks.
 //
 // APPEND (bf16 caches): request b also appends one token, k_new[b] / v_new[b]
@@ -531,19 +575,20 @@ decode_stream_kernel(void* __restrict__ kc_, void* __restrict__ vc_,
   // fp8 scales in one L2.  Otherwise every wave streams chunks of its own.
   const bool coop = (hge & 3) == 0;
   const int hsets = coop ? hge >> 2 : hge;
-  const int64_t U = int64_t(hsets) * s_pref[B];
+  const int64_t U = uniform64(int64_t(hsets) * s_pref[B]);
   const int W = coop ? gridDim.x : gridDim.x * 4;
-  const int64_t C = chunk_fixed > 0 ? chunk_fixed : max<int64_t>(1, (U + W - 1) / W);
-  const int64_t NC = (U + C - 1) / C;
+  const StreamChunks ch(U, W, chunk_fixed);
   const int lane = threadIdx.x & 63;
   const int r = lane & 15;
   const int grp = lane >> 4;
   const uint8_t* kc = static_cast<const uint8_t*>(kc_);
   const uint8_t* vc = static_cast<const uint8_t*>(vc_);
 
-  for (int64_t c = coop ? int64_t(blockIdx.x) : int64_t(blockIdx.x) * 4 + wv; c < NC; c += W) {
-    int64_t u = c * C;
-    const int64_t u_end = min(U, u + C);
+  for (int64_t c = coop ? int64_t(blockIdx.x) : int64_t(blockIdx.x) * 4 + wv; c < ch.N; c += W) {
+    int64_t u = ch.start(c);
+    const int64_t u_end = ch.end(c);
+    const int64_t u0 = u;
+    const int64_t ctot = chunk_fixed > 0 ? 0 : u_end - u0;  // progress priority on balanced chunks
     // request holding unit u: the last b with hsets * pref[b] <= u
     const int64_t x = u / hsets;
     int lo = 0, hi = B - 1;
@@ -584,7 +629,8 @@ decode_stream_kernel(void* __restrict__ kc_, void* __restrict__ vc_,
           const int off = part == 0 ? 0 : vp.c - vp.a;
           if (lo < hi)
             run_segment<QT, D, true>(st, kc, vc, kscale, vscale, tables + int64_t(b) * max_blocks, ctx, H, g,
-                                      lo + off, hi + off, scale_log2, qv, r, grp, sink, win_lo);
+                                      lo + off, hi + off, scale_log2, qv, r, grp, sink, win_lo, u - u0 + (lo - j),
+                                      ctot);
         }
       } else if constexpr (APPEND) {
         // the cache holds positions < ctx - 1; a segment cut down to nothing
@@ -594,14 +640,14 @@ decode_stream_kernel(void* __restrict__ kc_, void* __restrict__ vc_,
         const int jc1 = min(j1, (ctx_c + kBS - 1) / kBS);
         if (j < jc1)
           run_segment<QT, D>(st, kc, vc, kscale, vscale, tables + int64_t(b) * max_blocks, ctx_c, H, g,
-                              j, jc1, scale_log2, qv, r, grp);
+                              j, jc1, scale_log2, qv, r, grp, 0, 0, u - u0, ctot);
         if (app && j1 == nb) {
           const int64_t nrow = (int64_t(b) * H + g) * D;
           add_token<D>(st, k_new + nrow, v_new + nrow, qv, scale_log2, grp);
         }
       } else {
         run_segment<QT, D>(st, kc, vc, kscale, vscale, tables + int64_t(b) * max_blocks, ctx, H, g, j, j1,
-                            scale_log2, qv, r, grp);
+                            scale_log2, qv, r, grp, 0, 0, u - u0, ctot);
       }
       const float l = wave_sum16(st.l);
       if (j == 0 && j1 == nb) {  // the whole (b, gh): finish here
@@ -664,7 +710,6 @@ stream_reduce_kernel(uint16_t* __restrict__ out, const float* __restrict__ ws_ml
   const int hsets = coop ? hge >> 2 : hge;
   const int streams = coop ? workers / 4 : workers;
   const int64_t U = int64_t(hsets) * ws_pref[B];
-  const int64_t C = chunk_fixed > 0 ? chunk_fixed : max<int64_t>(1, (U + streams - 1) / streams);
   const int g = h / G;
   const int hg = (h - g * G) / 16;
   const int hh = (h - g * G) % 16;
@@ -672,11 +717,12 @@ stream_reduce_kernel(uint16_t* __restrict__ out, const float* __restrict__ ws_ml
   const int gs = coop ? gh >> 2 : gh;
   const int wv = coop ? gh & 3 : 0;
   const int64_t start = int64_t(hsets) * ws_pref[b] + int64_t(gs) * nb;
-  const int64_t c0 = start / C;
-  const int64_t c1 = (start + nb - 1) / C;
+  const StreamChunks ch(U, streams, chunk_fixed);
+  const int64_t c0 = ch.chunk_of(start);
+  const int64_t c1 = ch.chunk_of(start + nb - 1);
   if (c0 == c1) return;  // finished inside one chunk by the decode kernel
   const int K = int(c1 - c0 + 1);
-  const int first_role = start > c0 * C ? 1 : 0;
+  const int first_role = start > ch.start(c0) ? 1 : 0;
   auto slot = [&](int k) -> int64_t {
     const int64_t cr = (c0 + k) * 2 + (k == 0 ? first_role : 0);
     return (coop ? cr * 4 + wv : cr) * HS + hh;
@@ -977,12 +1023,12 @@ int launch_decode_d(const DecodeArgs& a, hipStream_t s) {
   if (e != hipSuccess) return fail(KV_E_HIP, "decode launch: %s", hipGetErrorString(e));
   if (win)
     stream_reduce_kernel<D, true><<<dim3(a.h_q, a.B), 256, 0, s>>>(
-        out, a.ws_ml, a.ws_acc, a.ws_pref, a.ctx, a.B, a.max_ctx, a.h_q, G, nhg, H, a.hs, a.workers, a.chunk,
-        a.sink, a.window);
+        out, a.ws_ml, a.ws_acc, a.ws_pref, a.ctx, a.B, a.max_ctx, a.h_q, G, nhg, H, a.hs, a.workers,
+        a.chunk, a.sink, a.window);
   else
     stream_reduce_kernel<D, false><<<dim3(a.h_q, a.B), 256, 0, s>>>(
-        out, a.ws_ml, a.ws_acc, a.ws_pref, a.ctx, a.B, a.max_ctx, a.h_q, G, nhg, H, a.hs, a.workers, a.chunk,
-        0, 0);
+        out, a.ws_ml, a.ws_acc, a.ws_pref, a.ctx, a.B, a.max_ctx, a.h_q, G, nhg, H, a.hs, a.workers,
+        a.chunk, 0, 0);
   e = hipGetLastError();
   if (e != hipSuccess) return fail(KV_E_HIP, "decode reduce launch: %s", hipGetErrorString(e));
   return ok();
