@@ -698,7 +698,8 @@ stream_reduce_kernel(uint16_t* __restrict__ out, const float* __restrict__ ws_ml
   __shared__ __attribute__((aligned(16))) float s_a[PL][D];
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int64_t row = int64_t(b) * h_q + h;
-  const int nb = visited_pages<WIN>(clamp_ctx(ctx_lens, b, max_ctx), sink, window).count();
+  // the decode kernel's block prefix holds each request's visited block count
+  const int nb = ws_pref[b + 1] - ws_pref[b];
   if (nb == 0) {
     if (tid < D) out[row * D + tid] = 0;
     return;
