@@ -537,6 +537,7 @@ def main():
                                   "launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated); null if "
                                   "the kernel source changed"),
             "us_per_call": round(dec_mean_s * 1e6, 2),
+            "us_per_call_p10_p50_p90": [round(float(np.percentile(r["dec_ms"], x)) * 1e3, 2) for x in (10, 50, 90)],
             "calls_timed": int(len(r["dec_ms"])),
         }
     config = dict(r["config"])
@@ -566,9 +567,12 @@ def main():
 
 def cpu_baseline(ctx0, slots0_len, k_new, v_new, q_all, args, B, H, h_q, D, L, dev):
     """The fp64 oracle on the host cores, on a bounded sample of the same
-    workload: 8 of the requests of the last decoded layer, repeated until about
-    `cpu_seconds` have passed.  Its inputs are regenerated from the same seeded
-    generator (never read back from the pool)."""
+    workload: 16 of the requests of the last decoded layer (every fourth),
+    one request per task on a thread pool as wide as the cores this process
+    may use (at most 16), BLAS limited to one thread per task, repeated until
+    about `cpu_seconds` have passed.  Its inputs are regenerated from the same
+    seeded generator (never read back from the pool)."""
+    from concurrent.futures import ThreadPoolExecutor
     import torch
     import oracle
     import synth
@@ -582,18 +586,19 @@ def cpu_baseline(ctx0, slots0_len, k_new, v_new, q_all, args, B, H, h_q, D, L, d
     starts = np.concatenate([[0], np.cumsum(ctx0.astype(np.int64) - 1)])
     q = oracle.bf16_bits_to_f64(to_bits(q_all[s_last, layer]))
     seqs = []
-    for b in range(0, B, 8):
+    for b in range(0, B, 4):
         kb = torch.cat([k_pre[starts[b]:starts[b + 1]], k_new[:s_last + 1, layer, b]])
         vb = torch.cat([v_pre[starts[b]:starts[b + 1]], v_new[:s_last + 1, layer, b]])
         seqs.append((b, oracle.bf16_bits_to_f64(to_bits(kb)), oracle.bf16_bits_to_f64(to_bits(vb))))
     del k_pre, v_pre
     kv_bytes = sum(kk.shape[0] for _, kk, _ in seqs) * H * D * 2 * 2
     reps = 0
-    with threadpool_limits(limits=1):
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    one = lambda t: oracle.attention_fp64(q[t[0]], t[1], t[2], 1.0 / math.sqrt(D))
+    with threadpool_limits(limits=1), ThreadPoolExecutor(max_workers=workers) as ex:
         t0 = time.perf_counter()
         while True:
-            for b, kk, vv in seqs:
-                oracle.attention_fp64(q[b], kk, vv, 1.0 / math.sqrt(D))
+            list(ex.map(one, seqs))
             reps += 1
             if time.perf_counter() - t0 >= args.cpu_seconds:
                 break
@@ -601,11 +606,11 @@ def cpu_baseline(ctx0, slots0_len, k_new, v_new, q_all, args, B, H, h_q, D, L, d
     return {
         "value": round(kv_bytes * reps / dt / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": workers,
         "kind": "oracle",
         "sample": f"fp64 oracle decode of {len(seqs)} of {B} requests of one layer "
                   f"({kv_bytes / 1e6:.0f} MB of bf16 K/V), {reps} repetitions in {dt:.1f} s, "
-                  "BLAS limited to 1 thread",
+                  f"one request per task on {workers} threads, BLAS limited to 1 thread per task",
     }
 
 
