@@ -56,11 +56,20 @@ typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
 typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-__device__ inline uint32_t bf_bits(float x) {
-  return uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x)));  // round to nearest even
+// Two floats -> two bf16 (round to nearest even) in one dword: one
+// v_cvt_pk_bf16_f32.
+__device__ inline uint32_t pack2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
-__device__ inline uint32_t pack2(float lo, float hi) { return bf_bits(lo) | (bf_bits(hi) << 16); }
+
+// Largest of the arguments, NaN-propagating (v_maximum3_f32; the scores it
+// sees are finite or -inf).
+__device__ inline float max4(float a, float b, float c, float d) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), __builtin_elementwise_maximum(c, d));
+}
 
 __device__ inline f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
@@ -108,21 +117,17 @@ struct Tile {
   uint32_t ksrc[NI], vsrc[NI];  // element offsets within a page tile of this lane's copies
 };
 
-// Copy chunk `ci` (keys 64 ci .. 64 ci + 63): wave w takes page 4 ci + w,
-// clamped to the request's last page (keys past the context are masked and,
-// for V, zeroed before use).
+// Copy the K (or V) tiles of chunk `ci` (keys 64 ci .. 64 ci + 63): wave w
+// takes page 4 ci + w, clamped to the request's last page (keys past the
+// context are masked and, for V, zeroed before use).
 template <int D>
-__device__ __forceinline__ void issue_chunk(uint16_t* kbuf, uint16_t* vbuf, int ci, int nb, const int32_t* trow,
-                                            const uint16_t* kc, const uint16_t* vc, int H, int g, int w,
-                                            const Tile<D>& t) {
+__device__ __forceinline__ void issue_tiles(uint16_t* buf, const uint16_t* cache, const uint32_t (&src)[Tile<D>::NI],
+                                            int ci, int nb, const int32_t* trow, int H, int g, int w) {
   constexpr int PG = Tile<D>::PG;
   const int page = min(ci * (kChunk / kBS) + w, nb - 1);
   const int64_t tile = (int64_t(trow[page]) * H + g) * kBS * D;
 #pragma unroll
-  for (int m = 0; m < Tile<D>::NI; ++m) {
-    copy_to_lds(kc + tile + t.ksrc[m], kbuf + (w * PG + 64 * m) * 8);
-    copy_to_lds(vc + tile + t.vsrc[m], vbuf + (w * PG + 64 * m) * 8);
-  }
+  for (int m = 0; m < Tile<D>::NI; ++m) copy_to_lds(cache + tile + src[m], buf + (w * PG + 64 * m) * 8);
 }
 
 // Zero the V entries of keys >= ctx in a chunk buffer.
@@ -147,25 +152,11 @@ __device__ __forceinline__ void zero_tail(uint16_t* vbuf, int k0, int ctx, int t
   }
 }
 
-// One chunk: wait for its copies, start the next chunk's copies into the
-// other buffer, then scores, softmax and the weighted sum of V.
+// Raw scores of a chunk: S[rt][kb][j][i] is key 32 kb + 8 qg + 4 j + i of the
+// chunk against row 16 (kRT w + rt) + c (A operand row c is key
+// 8 (c / 4) + 4 j + c % 4 of the block, so lane group qg gets keys 8 qg ..).
 template <int D>
-__device__ __forceinline__ void chunk_step(Tile<D>& t, uint16_t* kcur, uint16_t* vcur, uint16_t* knxt, uint16_t* vnxt,
-                                           int ci, int nch, int nb, int ctx, int pos_min, const int32_t* trow,
-                                           const uint16_t* kc, const uint16_t* vc, int H, int g, int w, int tid,
-                                           int qg, float sl) {
-  constexpr int KK = Tile<D>::KK, T8 = Tile<D>::T8;
-  barrier<kWaitAll>();  // this chunk is in LDS; everyone is done with the other buffer
-  if (ci + 1 < nch) issue_chunk<D>(knxt, vnxt, ci + 1, nb, trow, kc, vc, H, g, w, t);
-  const int k0 = ci * kChunk;
-  if (k0 + kChunk > ctx) {  // the request's last chunk: no copy is in flight
-    zero_tail<D>(vcur, k0, ctx, tid);
-    barrier<kWaitLds>();
-  }
-
-  // scores of keys k0 + 32 kb + 8 qg + 4 j + i (A operand row c is key
-  // 8 (c / 4) + 4 j + c % 4 of the block, so lane group qg gets keys 8 qg ..)
-  f32x4 S[kRT][2][2];
+__device__ __forceinline__ void chunk_scores(f32x4 (&S)[kRT][2][2], const uint16_t* kbuf, const Tile<D>& t) {
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt)
 #pragma unroll
@@ -173,21 +164,40 @@ __device__ __forceinline__ void chunk_step(Tile<D>& t, uint16_t* kcur, uint16_t*
 #pragma unroll
       for (int j = 0; j < 2; ++j) S[rt][kb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk)  // eight independent accumulators per k-step
+  for (int kk = 0; kk < Tile<D>::KK; ++kk)  // eight independent accumulators per k-step
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const u32x4 kv = *reinterpret_cast<const u32x4*>(kcur + (32 * kb + 4 * j) * D + t.kaddr[kk]);
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(kbuf + (32 * kb + 4 * j) * D + t.kaddr[kk]);
 #pragma unroll
         for (int rt = 0; rt < kRT; ++rt) S[rt][kb][j] = mfma(kv, t.qv[rt][kk], S[rt][kb][j]);
       }
-#pragma unroll
-  for (int rt = 0; rt < kRT; ++rt)
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) S[rt][kb][j] *= sl;
+}
+
+// Step ci of the pipeline.  On entry S holds the raw scores of chunk ci,
+// K of chunk ci + 1 and V of chunk ci are on their way into k_next / v_cur,
+// and k_free / v_free (K of ci, V of ci - 1) are being read no more once
+// everyone passes the barrier.  The step starts the copies of K(ci + 2) and
+// V(ci + 1), issues the score MFMAs of chunk ci + 1 (into S for the next
+// step) among the softmax instructions of chunk ci, then the weighted sum of
+// V(ci).  On the last step the next scores come from stale LDS and are
+// dropped.
+template <int D>
+__device__ __forceinline__ void chunk_step(Tile<D>& t, f32x4 (&S)[kRT][2][2], uint16_t* k_next, uint16_t* k_free,
+                                           uint16_t* v_cur, uint16_t* v_free, int ci, int nch, int nb, int ctx,
+                                           int pos_min, const int32_t* trow, const uint16_t* kc,
+                                           const uint16_t* vc, int H, int g, int w, int tid, int qg, float sl) {
+  constexpr int T8 = Tile<D>::T8;
+  barrier<kWaitAll>();  // K(ci + 1) and V(ci) are in LDS; the free buffers are free
+  if (ci + 2 < nch) issue_tiles<D>(k_free, kc, t.ksrc, ci + 2, nb, trow, H, g, w);
+  if (ci + 1 < nch) issue_tiles<D>(v_free, vc, t.vsrc, ci + 1, nb, trow, H, g, w);
+  const int k0 = ci * kChunk;
+  if (k0 + kChunk > ctx) {  // the request's last chunk: no V copy is in flight
+    zero_tail<D>(v_cur, k0, ctx, tid);
+    barrier<kWaitLds>();
+  }
+  // raw scores; sl > 0 is folded into the exponent below
   if (k0 + kChunk - 1 > pos_min) {  // some key of the chunk lies after some row of this wave
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt)
@@ -202,7 +212,7 @@ __device__ __forceinline__ void chunk_step(Tile<D>& t, uint16_t* kcur, uint16_t*
           }
   }
 
-  float mloc[kRT];
+  float mloc[kRT];  // this lane group's largest scaled score per row (log2 units)
   bool grow = false;
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
@@ -211,17 +221,18 @@ __device__ __forceinline__ void chunk_step(Tile<D>& t, uint16_t* kcur, uint16_t*
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        mx = fmaxf(fmaxf(mx, fmaxf(S[rt][kb][j][0], S[rt][kb][j][1])), fmaxf(S[rt][kb][j][2], S[rt][kb][j][3]));
-    mloc[rt] = mx;
-    grow |= mx > t.m[rt] + kSlack;
+        mx = __builtin_elementwise_maximum(mx, max4(S[rt][kb][j][0], S[rt][kb][j][1], S[rt][kb][j][2],
+                                                    S[rt][kb][j][3]));
+    mloc[rt] = mx * sl;
+    grow |= mloc[rt] > t.m[rt] + kSlack;
   }
   if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // move the running maxima (rare after the first chunk)
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt) {
       float mx = mloc[rt];
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(t.m[rt], mx);  // finite: key 0 is visible to every row
+      mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 16));
+      mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32));
+      const float m_new = __builtin_elementwise_maximum(t.m[rt], mx);  // finite: key 0 is visible to every row
       const float alpha = __builtin_amdgcn_exp2f(t.m[rt] - m_new);
       t.m[rt] = m_new;
       t.l[rt] *= alpha;
@@ -230,6 +241,9 @@ __device__ __forceinline__ void chunk_step(Tile<D>& t, uint16_t* kcur, uint16_t*
     }
   }
 
+  // weights of chunk ci, with the score MFMAs of chunk ci + 1 in flight
+  f32x4 Sn[kRT][2][2];
+  chunk_scores<D>(Sn, k_next, t);
   u32x4 pop[kRT][2];
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
@@ -241,7 +255,7 @@ __device__ __forceinline__ void chunk_step(Tile<D>& t, uint16_t* kcur, uint16_t*
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          e[j][i] = __builtin_amdgcn_exp2f(S[rt][kb][j][i] - t.m[rt]);
+          e[j][i] = __builtin_amdgcn_exp2f(fmaf(S[rt][kb][j][i], sl, -t.m[rt]));
           ps += e[j][i];
         }
       pop[rt][kb] = u32x4{pack2(e[0][0], e[0][1]), pack2(e[0][2], e[0][3]), pack2(e[1][0], e[1][1]),
@@ -253,10 +267,16 @@ __device__ __forceinline__ void chunk_step(Tile<D>& t, uint16_t* kcur, uint16_t*
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int t8 = 0; t8 < T8; ++t8) {
-      const u32x4 vv = *reinterpret_cast<const u32x4*>(vcur + t.vaddr + 8 * (4 * D * kb + 32 * t8));
+      const u32x4 vv = *reinterpret_cast<const u32x4*>(v_cur + t.vaddr + 8 * (4 * D * kb + 32 * t8));
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt) t.acc[rt][t8] = mfma(vv, pop[rt][kb], t.acc[rt][t8]);
     }
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) S[rt][kb][j] = Sn[rt][kb][j];
 }
 
 // grid: tiles * B * H workgroups of 256 threads, latest tiles first.
@@ -265,7 +285,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 prefill_kernel(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc, const uint16_t* __restrict__ q,
                uint16_t* __restrict__ out, const int32_t* __restrict__ tables, int max_blocks,
                const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ qstart, int B, int tiles,
-               int max_ctx, int H, int h_q, int G, int tpt, float scale_log2) {
+               int max_ctx, int H, int h_q, int G, int tpt, float scale_log2, uint32_t q_sign) {
   using T = Tile<D>;
   constexpr int KK = T::KK, T8 = T::T8, NI = T::NI, PG = T::PG;
   __shared__ __attribute__((aligned(16))) uint16_t k_a[kChunk * D];
@@ -302,7 +322,7 @@ prefill_kernel(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     for (int kk = 0; kk < KK; ++kk) {
       u32x4 v = {0, 0, 0, 0};
       if (valid[rt]) v = *reinterpret_cast<const u32x4*>(q + qrow[rt] * D + 32 * kk + 8 * qg);
-      t.qv[rt][kk] = v;
+      t.qv[rt][kk] = v ^ q_sign;  // negated for negative scales (exact)
     }
     t.m[rt] = -INFINITY;
     t.l[rt] = 0.0f;
@@ -335,11 +355,20 @@ prefill_kernel(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
   const int nch = (n_keys + kChunk - 1) / kChunk;
   const int nb = (ctx + kBS - 1) / kBS;
   const int32_t* trow = tables + int64_t(b) * max_blocks;
-  if (nch > 0) issue_chunk<D>(k_a, v_a, 0, nb, trow, kc, vc, H, g, w, t);
-  for (int ci = 0; ci < nch; ci += 2) {
-    chunk_step<D>(t, k_a, v_a, k_b, v_b, ci, nch, nb, ctx, pos_min, trow, kc, vc, H, g, w, tid, qg, scale_log2);
-    if (ci + 1 < nch)
-      chunk_step<D>(t, k_b, v_b, k_a, v_a, ci + 1, nch, nb, ctx, pos_min, trow, kc, vc, H, g, w, tid, qg, scale_log2);
+  if (nch > 0) {
+    issue_tiles<D>(k_a, kc, t.ksrc, 0, nb, trow, H, g, w);
+    issue_tiles<D>(v_a, vc, t.vsrc, 0, nb, trow, H, g, w);
+    if (nch > 1) issue_tiles<D>(k_b, kc, t.ksrc, 1, nb, trow, H, g, w);
+    barrier<kWaitAll>();
+    f32x4 S[kRT][2][2];
+    chunk_scores<D>(S, k_a, t);
+    for (int ci = 0; ci < nch; ci += 2) {
+      chunk_step<D>(t, S, k_b, k_a, v_a, v_b, ci, nch, nb, ctx, pos_min, trow, kc, vc, H, g, w, tid, qg,
+                    scale_log2);
+      if (ci + 1 < nch)
+        chunk_step<D>(t, S, k_a, k_b, v_b, v_a, ci + 1, nch, nb, ctx, pos_min, trow, kc, vc, H, g, w, tid, qg,
+                      scale_log2);
+    }
   }
 
 #pragma unroll
@@ -374,15 +403,22 @@ int launch_prefill(const kv_pool* p, int32_t layer, void* out, const void* q, co
   const auto* kc = static_cast<const uint16_t*>(p->k_cache) + lo;
   const auto* vc = static_cast<const uint16_t*>(p->v_cache) + lo;
   const dim3 grid(uint32_t(int64_t(tiles) * B * H));
-  const float sl = scale * kLog2e;
+  // The kernel wants a positive score scale (it folds the scale into the
+  // exponent after taking maxima of the raw scores): a negative scale negates
+  // q instead, and a zero scale becomes the smallest normal float, which
+  // leaves every weight 2^0 as a zero scale does.
+  float sl = scale * kLog2e;
+  const uint32_t q_sign = sl < 0.0f ? 0x80008000u : 0u;
+  sl = sl < 0.0f ? -sl : sl;
+  if (sl == 0.0f) sl = 1.17549435e-38f;
   if (d.head_dim == 128)
     prefill_kernel<128><<<grid, 256, 0, stream>>>(kc, vc, static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
                                                   tables, max_blocks, ctx, qstart, B, tiles, max_ctx, H, h_q, G, tpt,
-                                                  sl);
+                                                  sl, q_sign);
   else
     prefill_kernel<64><<<grid, 256, 0, stream>>>(kc, vc, static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
                                                  tables, max_blocks, ctx, qstart, B, tiles, max_ctx, H, h_q, G, tpt,
-                                                 sl);
+                                                 sl, q_sign);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KV_E_HIP, "prefill launch: %s", hipGetErrorString(e));
   return ok();

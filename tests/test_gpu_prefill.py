@@ -53,21 +53,21 @@ class PrefillCase:
         self.qstart = np.concatenate([[0], np.cumsum(self.n_q)]).astype(np.int32)
         check_indices(self.table, self.ctx, N, int(self.ctx.max()))
 
-    def run(self):
-        scale = 1.0 / math.sqrt(self.D)
+    def run(self, scale=None):
+        scale = 1.0 / math.sqrt(self.D) if scale is None else scale
         out = self.pool.prefill(0, self.dq, torch.from_numpy(self.table).to(DEV),
                                 torch.from_numpy(self.ctx).to(DEV), torch.from_numpy(self.qstart).to(DEV),
                                 int(self.n_q.max()), int(self.ctx.max()), scale)
         torch.cuda.synchronize()
         return oracle.bf16_bits_to_f64(from_dev_bits(out)), scale
 
-    def ref(self, b, rows=None):
+    def ref(self, b, rows=None, scale=None):
         s, e = int(self.kstart[b]), int(self.kstart[b + 1])
         qs, qe = int(self.qstart[b]), int(self.qstart[b + 1])
         K = oracle.bf16_bits_to_f64(from_dev_bits(self.dk[s:e]))
         V = oracle.bf16_bits_to_f64(from_dev_bits(self.dv[s:e]))
         q = oracle.bf16_bits_to_f64(from_dev_bits(self.dq[qs:qe]))
-        scale = 1.0 / math.sqrt(self.D)
+        scale = 1.0 / math.sqrt(self.D) if scale is None else scale
         if rows is None:
             return oracle.prefill_attention_fp64(q, K, V, scale)
         n, P = len(K), len(q)
@@ -107,6 +107,18 @@ def test_prefill_poisoned_pool(gpu_lib):
     for b in range(len(CTX)):
         qs, qe = int(c.qstart[b]), int(c.qstart[b + 1])
         assert_close(got[qs:qe], c.ref(b), "bf16", f"poisoned ctx {CTX[b]}")
+
+
+@pytest.mark.parametrize("scale", [-0.2, 0.0, 0.02])
+def test_prefill_any_scale(gpu_lib, scale):
+    """Negative, zero and small score scales (the kernel takes maxima of raw
+    scores and applies a positive scale in the exponent; the host negates q
+    for a negative one)."""
+    c = PrefillCase(2, 128, 8, CTX, NQ, seed=66)
+    got, _ = c.run(scale)
+    for b in range(len(CTX)):
+        qs, qe = int(c.qstart[b]), int(c.qstart[b + 1])
+        assert_close(got[qs:qe], c.ref(b, scale=scale), "bf16", f"scale {scale} ctx {CTX[b]}")
 
 
 def test_prefill_one_query_equals_decode(gpu_lib):
