@@ -266,3 +266,27 @@ def test_balanced_split_reused_workspace(gpu_lib):
         assert_close(got[b], ref[b], "bf16", f"request {b} of {lens[b]} tokens")
     fixed = c.decode(partition_tokens=256)
     assert np.max(np.abs(fixed - got)) <= 2e-2
+
+
+def test_largest_batch(gpu_lib):
+    """8192 requests (the largest batch of the balanced decode) of 0-40
+    tokens: the block prefix is scanned in 32 passes, chunks hold many whole
+    requests, empty requests give zeros.  Plain decode, then the fused step
+    (which also appends 8192 rows); a sample of requests is checked against
+    the oracle, and every output is finite."""
+    rng = np.random.default_rng(81)
+    lens = rng.integers(0, 41, 8192)
+    lens[rng.choice(8192, 200, replace=False)] = 0
+    need = int(sum(oracle.blocks_for(int(n), 16) for n in lens))
+    c = Case("bf16", 2, 64, 8, lens, num_blocks=need + 8192, max_blocks=4, seed=81)
+    sample = sorted(set(rng.choice(8192, 48, replace=False).tolist()) | {0, 8191, int(np.argmax(lens))})
+    got = c.decode()
+    assert np.all(np.isfinite(got))
+    ref = c.oracle(batch=sample)
+    for b in sample:
+        assert_close(got[b], ref[b], "bf16", f"request {b} of {c.lens_list[b]} tokens")
+    assert np.all(got[np.array(c.lens_list) == 0] == 0)
+    got = c.decode_append_step(seed=82)
+    ref = c.oracle(batch=sample)
+    for b in sample:
+        assert_close(got[b], ref[b], "bf16", f"fused step, request {b} of {c.lens_list[b]} tokens")
