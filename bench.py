@@ -142,6 +142,27 @@ def copy_calibration(torch, dev):
     log("copy calibration: 1 GiB read + 1 GiB written by one copy kernel")
 
 
+def stream_copy_gbs(torch, dev, nbytes=2 ** 30, reps=5):
+    """Bandwidth of a plain device-to-device copy of `nbytes` (read + written
+    bytes over the mean time of `reps` copies): the box's practical HBM
+    ceiling, reported beside the published peak."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    stream = torch.cuda.current_stream()
+    e0, e1 = TimingEvent(), TimingEvent()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_ms(e1) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
+
+
 def decode_workload(args, torch, synth, pk, dev, spec=None, layers=0):
     """Single-layer decode steps over a multi-layer pool (see the module doc).
     `spec` / `layers` replace the workload's shape and pool depth (sweeps)."""
@@ -536,6 +557,7 @@ def main():
             "traffic_note": r.get("traffic_note", "HBM bytes read + written per decode_stream_kernel "
                                   "launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated); null if "
                                   "the kernel source changed"),
+            "stream_copy_gbs": stream_copy_gbs(torch, dev),
             "us_per_call": round(dec_mean_s * 1e6, 2),
             "us_per_call_p10_p50_p90": [round(float(np.percentile(r["dec_ms"], x)) * 1e3, 2) for x in (10, 50, 90)],
             "calls_timed": int(len(r["dec_ms"])),
