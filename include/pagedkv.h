@@ -333,9 +333,10 @@ int paged_attention_decode_append(kv_pool* pool, int32_t layer, void* out, const
  * [B+1], non-decreasing from 0; block_tables, context_lens as for
  * paged_attention_decode; max_q_len: host bound on every n_q (sizes the grid);
  * max_ctx: host bound on context_lens (<= max_blocks_per_seq * block_size).
- * bf16 pools and queries only, at most 128 query heads per kv head
- * (KV_E_UNSUPPORTED otherwise).  No workspace: one workgroup covers all keys
- * of its query tile. */
+ * Any finite scale (a negative one negates q exactly inside the call, zero
+ * gives equal weights).  bf16 pools and queries only, at most 128 query heads
+ * per kv head (KV_E_UNSUPPORTED otherwise).  No workspace: one workgroup
+ * covers all keys of its query tile. */
 int paged_attention_prefill(kv_pool* pool, int32_t layer, void* out, const void* q, int32_t q_dtype,
                             const int32_t* block_tables, int32_t max_blocks_per_seq,
                             const int32_t* context_lens, const int32_t* query_start, int32_t B, int32_t h_q,
