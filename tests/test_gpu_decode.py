@@ -290,3 +290,25 @@ def test_largest_batch(gpu_lib):
     ref = c.oracle(batch=sample)
     for b in sample:
         assert_close(got[b], ref[b], "bf16", f"fused step, request {b} of {c.lens_list[b]} tokens")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_shapes(gpu_lib, seed):
+    """Seeded random batches for the decode: element type, kv heads, group
+    size (1-20 query heads per kv head), head_dim, 1-24 requests of 0-2500
+    tokens (fp8/int8: 1-8 of 0-1200), and the split (balanced, or pieces of
+    16-512 tokens)."""
+    rng = np.random.default_rng(3000 + seed)
+    dtype = str(rng.choice(["bf16", "fp8", "int8", "f32"]))
+    H = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.integers(1, 21))
+    D = int(rng.choice([64, 128]))
+    q8 = dtype in ("fp8", "int8")   # the oracle reads a host mirror of the quantised pool
+    B = int(rng.integers(1, 9 if q8 else 25))
+    lens = [int(x) for x in rng.integers(0, 1201 if q8 else 2501, B)]
+    part = int(rng.choice([0, 0, 16, 64, 512]))
+    c = Case(dtype, H, D, H * G, lens, seed=4000 + seed, mirror=q8)
+    got = c.decode(partition_tokens=part)
+    ref = c.oracle()
+    for b in range(B):
+        assert_close(got[b], ref[b], c.tol_key, f"{dtype} H {H} G {G} D {D} part {part} ctx {lens[b]}")

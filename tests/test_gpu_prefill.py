@@ -146,3 +146,21 @@ def test_llama3_8b_prompts_full_size(gpu_lib):
         ref = c.ref(b, rows)
         assert_close(got[qs + np.array(rows)], ref, "bf16", f"request {b}: {len(rows)} rows")
     log(f"prefill FLOP: {oracle.prefill_flops(ctx, nq, 32, 128) / 1e9:.1f} G")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_prefill_random_shapes(gpu_lib, seed):
+    """Seeded random batches: 1-6 requests, contexts 1-700 with 1..ctx new
+    tokens, groups of 1-32 query heads per kv head, head_dim 64 or 128."""
+    rng = np.random.default_rng(1000 + seed)
+    B = int(rng.integers(1, 7))
+    ctx = [int(x) for x in rng.integers(1, 701, B)]
+    nq = [int(rng.integers(1, n + 1)) for n in ctx]
+    H = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([1, 2, 3, 4, 8, 16, 32]))
+    D = int(rng.choice([64, 128]))
+    c = PrefillCase(H, D, H * G, ctx, nq, seed=2000 + seed)
+    got, _ = c.run()
+    for b in range(B):
+        qs, qe = int(c.qstart[b]), int(c.qstart[b + 1])
+        assert_close(got[qs:qe], c.ref(b), "bf16", f"B {B} H {H} G {G} D {D} ctx {ctx[b]} new {nq[b]}")
