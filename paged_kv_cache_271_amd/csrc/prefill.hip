@@ -270,14 +270,29 @@ __device__ __forceinline__ void chunk_step(Tile<D>& t, f32x4 (&S)[kRT][2][2], ui
     }
     t.l[rt] += ps;
   }
+  // PV: the eight V operands of key block 0 are read up front, and each
+  // block-1 read is issued beside two block-0 MFMAs, so eight LDS reads stay
+  // in flight (left alone, the compiler waited on every read after two).
+  u32x4 vv[2][T8];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int t8 = 0; t8 < T8; ++t8) vv[0][t8] = *reinterpret_cast<const u32x4*>(v_cur + t.vaddr + 8 * (32 * t8));
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int t8 = 0; t8 < T8; ++t8) {
-      const u32x4 vv = *reinterpret_cast<const u32x4*>(v_cur + t.vaddr + 8 * (4 * D * kb + 32 * t8));
+  for (int t8 = 0; t8 < T8; ++t8) {
+    vv[1][t8] = *reinterpret_cast<const u32x4*>(v_cur + t.vaddr + 8 * (4 * D + 32 * t8));
 #pragma unroll
-      for (int rt = 0; rt < kRT; ++rt) t.acc[rt][t8] = mfma(vv, pop[rt][kb], t.acc[rt][t8]);
-    }
+    for (int rt = 0; rt < kRT; ++rt) t.acc[rt][t8] = mfma(vv[0][t8], pop[rt][0], t.acc[rt][t8]);
+  }
+#pragma unroll
+  for (int t8 = 0; t8 < T8; ++t8) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    __builtin_amdgcn_sched_group_barrier(0x008, kRT, 0);  // then kRT MFMAs
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int t8 = 0; t8 < T8; ++t8)
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) t.acc[rt][t8] = mfma(vv[1][t8], pop[rt][1], t.acc[rt][t8]);
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt)
 #pragma unroll
