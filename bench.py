@@ -52,8 +52,8 @@ DEFAULT_SEED = {"llama3_8b": 2, "llama3_70b_long": 3, "fp8": 5, "int8": 5, "pref
 # calibration there (fetch x2, write x1).  They hold for the kernel source they
 # were taken on, identified by its SHA-256; any other source reports null.
 TRAFFIC_SOURCE = "paged_kv_cache_271_amd/csrc/decode.hip"
-TRAFFIC_SHA256 = "eb8dbd2f833b4aa0d1e9d5894614ea84344a454e6135310b1a75101ef6ed401d"
-TRAFFIC_BYTES = {"llama3_8b": 594_931_507, "fp8": 1_235_790_541, "llama3_70b_long": 1_360_047_002, "int8": 1_237_010_125, "llama3_8b_window": 1_095_950_029}
+TRAFFIC_SHA256 = "b24903c30fad8fa8824c79d139ba5c2fbc071b31f0f9eac989d65f62c8f56e42"
+TRAFFIC_BYTES = {"llama3_8b": 594_945_229, "fp8": 1_235_771_597, "llama3_70b_long": 1_360_146_227, "int8": 1_236_131_328, "llama3_8b_window": 1_095_975_629}
 
 
 def measured_traffic(workload, two_calls_asked):

@@ -72,11 +72,13 @@ constexpr int kQBf16 = 0, kQFp8 = 1, kQInt8 = 2;
 
 // Four symmetric int8 codes (one dword) -> four fp16 (two dwords), exact:
 // with the sign bit flipped a code c is the byte u = c + 128, 0x6400 | u is
-// the fp16 1024 + u, and subtracting 1152 leaves c.
+// the fp16 1024 + u, and subtracting 1152 leaves c.  Each pair's high bytes
+// come from one v_perm_b32: selector bytes 0-3 take bytes of the second
+// operand (u), 4-7 bytes of the first (0x64 everywhere).
 __device__ inline u32x2 int8x4_to_f16x4(uint32_t w) {
   const uint32_t u = w ^ 0x80808080u;
-  const uint32_t lo = 0x64006400u | (u & 0xFFu) | ((u & 0xFF00u) << 8);
-  const uint32_t hi = 0x64006400u | ((u >> 16) & 0xFFu) | ((u >> 8) & 0xFF0000u);
+  const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);  // [u0, 64, u1, 64]
+  const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);  // [u2, 64, u3, 64]
   const f16x2 bias = {static_cast<_Float16>(-1152.0f), static_cast<_Float16>(-1152.0f)};
   u32x2 r;
   r[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, lo) + bias);
