@@ -54,16 +54,29 @@ DEFAULT_SEED = {"llama3_8b": 2, "llama3_70b_long": 3, "fp8": 5, "int8": 5, "pref
 TRAFFIC_SOURCE = "paged_kv_cache_271_amd/csrc/decode.hip"
 TRAFFIC_SHA256 = "b24903c30fad8fa8824c79d139ba5c2fbc071b31f0f9eac989d65f62c8f56e42"
 TRAFFIC_BYTES = {"llama3_8b": 594_945_229, "fp8": 1_235_771_597, "llama3_70b_long": 1_360_146_227, "int8": 1_236_131_328, "llama3_8b_window": 1_095_975_629}
+# The same per launch of prefill_kernel and of block_copy_kernel, from
+# profiles/prefill_llama3_8b_counters.md and
+# profiles/block_copy_cow_fork_hbm_counters.md: (source, its SHA-256, bytes).
+TRAFFIC_OTHER = {
+    "prefill": ("paged_kv_cache_271_amd/csrc/prefill.hip",
+                "40d38543edea2e06f68c0d6da0127566fc6313d02540da9c7573ea14264047d7", 433_608_499),
+    "cow_fork": ("paged_kv_cache_271_amd/csrc/copy.hip",
+                 "06367c5bcbf1b2856b1a3729463a1093d9928cc8dab6c0ca5b114bb07073ec79", 1_073_901_158),
+}
 
 
-def measured_traffic(workload, two_calls_asked):
+def measured_traffic(workload, two_calls_asked=False):
     import hashlib
     if two_calls_asked and workload in ("llama3_8b", "llama3_70b_long"):
         return None  # their counters were taken on the fused kernel
-    with open(os.path.join(ROOT, TRAFFIC_SOURCE), "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != TRAFFIC_SHA256:
+    source, sha, table = TRAFFIC_SOURCE, TRAFFIC_SHA256, TRAFFIC_BYTES
+    if workload in TRAFFIC_OTHER:
+        source, sha, nbytes = TRAFFIC_OTHER[workload]
+        table = {workload: nbytes}
+    with open(os.path.join(ROOT, source), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != sha:
             return None
-    return TRAFFIC_BYTES.get(workload)
+    return table.get(workload)
 
 
 def parse():
@@ -429,6 +442,8 @@ def cow_fork_workload(args, torch, synth, pk, dev):
         pool.release_n(ctable.reshape(-1))          # the children retire
         return moved
 
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -444,7 +459,9 @@ def cow_fork_workload(args, torch, synth, pk, dev):
               "cache_dtype": "bf16", "page_bytes_per_layer_kv": 2 * page_bytes,
               "bytes_moved_per_step": moved}
     return dict(wall=wall, kv_total=float(total), dec_ms=dec_ms, dec_kv=np.full(len(dec_ms), float(moved)),
-                config=config, cpu=None, traffic=None, traffic_note="HBM counters not taken for this kernel", dtype="bf16",
+                config=config, cpu=None, traffic=measured_traffic("cow_fork"),
+                traffic_note="HBM bytes read + written per block_copy_kernel launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, "
+                             "copy-calibrated); null if the kernel source changed", dtype="bf16",
                 kernel="kv_block_copy call (block_copy_kernel), bytes read + written",
                 metric="kv_block_copy GB/s (read + written), copy-on-write forks")
 
@@ -484,6 +501,8 @@ def prefill_workload(args, torch, synth, pk, dev):
         if ev is not None:
             ev[1].record(stream)
 
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -497,7 +516,9 @@ def prefill_workload(args, torch, synth, pk, dev):
     config = {"workload": "llama3_8b_prefill_layer", "batch": B, "new_tokens": P, "h_q": h_q, "h_kv": H,
               "head_dim": D, "cache_dtype": "bf16", "layers_in_pool": L, "flop_per_step": flops}
     return dict(wall=wall, kv_total=float(flops) * args.steps, dec_ms=dec_ms,
-                dec_kv=np.full(len(dec_ms), float(flops)), config=config, cpu=None, traffic=None, traffic_note="HBM counters not taken for this kernel", dtype="bf16",
+                dec_kv=np.full(len(dec_ms), float(flops)), config=config, cpu=None, traffic=measured_traffic("prefill"),
+                traffic_note="HBM bytes read + written per prefill_kernel launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, "
+                             "copy-calibrated); null if the kernel source changed", dtype="bf16",
                 kernel="paged_attention_prefill call (prefill_kernel)",
                 metric="paged prefill attention TFLOP/s (causal, bf16 MFMA)", unit="TFLOP/s",
                 bound="mfma", peak=MFMA_BF16_PEAK_TFLOPS, scale=1e12)
