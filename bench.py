@@ -302,8 +302,8 @@ def decode_workload(args, torch, synth, pk, dev, spec=None, layers=0):
     dec_kv = np.array([per_step_kv[j] for j in range(args.steps) if events[j] is not None], float)
 
     cpu = None
-    if name == "llama3_8b" and spec is None and not args.no_cpu_baseline:
-        cpu = cpu_baseline(ctx0, T0, k_new, v_new, q_all, args, B, H, h_q, D, L, dev)
+    if spec is None and not args.no_cpu_baseline:
+        cpu = cpu_baseline(ctx0, T0, k_new, v_new, q_all, args, w, L, dev)
     config = {
         "workload": f"{name}_decode_layer",
         "cache_dtype": dtype, "batch": B, "h_q": h_q, "h_kv": H, "head_dim": D, "block_size": 16,
@@ -608,51 +608,92 @@ def main():
     print(json.dumps(res), flush=True)
 
 
-def cpu_baseline(ctx0, slots0_len, k_new, v_new, q_all, args, B, H, h_q, D, L, dev):
-    """The fp64 oracle on the host cores, on a bounded sample of the same
-    workload: 16 of the requests of the last decoded layer (every fourth),
-    one request per task on a thread pool as wide as the cores this process
-    may use (at most 16), BLAS limited to one thread per task, repeated until
-    about `cpu_seconds` have passed.  Its inputs are regenerated from the same
-    seeded generator (never read back from the pool)."""
+def cpu_baseline(ctx0, slots0_len, k_new, v_new, q_all, args, w, L, dev):
+    """The oracle on the host cores, on a bounded sample of the same decode
+    workload: every (B / 16)-th request of the last decoded layer, as many as
+    fit in 131072 tokens (at least one), one request per task on a thread pool
+    as wide as the cores this process may use (at most 16), BLAS limited to one
+    thread per task, repeated until about `cpu_seconds` have passed.
+
+    What is timed is the oracle's decode of each sampled request as it
+    stands: for bf16 caches the fp64 attention over the request's contiguous
+    K/V (through the window's positions for a windowed workload); for fp8 and
+    int8 caches the oracle pool's gather, which decodes the codes and applies
+    the tile scales, followed by the same attention.  The inputs are
+    regenerated from the same seeded generators (never read back from the
+    GPU pool); the 8-bit codes come from the oracle's own append of those
+    inputs, in the same calls the GPU pool received (the prefill in one call,
+    then one token per model step)."""
     from concurrent.futures import ThreadPoolExecutor
     import torch
     import oracle
     import synth
     from threadpoolctl import threadpool_limits
 
+    dtype = w["dtype"]
+    B, H, h_q, D = w["batch"], w["h_kv"], w["h_q"], w["head_dim"]
+    sink, window = w.get("sink", 0), w.get("window", 0)
+    outlier = w.get("outlier_p", 0.0)
     last = args.warmup + args.steps - 1
     s_last, layer = divmod(last, L)
     to_bits = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-    k_pre = synth.device_normal((slots0_len, H, D), 1000 + 2 * layer, dev, torch.bfloat16)
-    v_pre = synth.device_normal((slots0_len, H, D), 1001 + 2 * layer, dev, torch.bfloat16)
+    k_pre = synth.device_normal((slots0_len, H, D), 1000 + 2 * layer, dev, torch.bfloat16, outlier, 8.0)
+    v_pre = synth.device_normal((slots0_len, H, D), 1001 + 2 * layer, dev, torch.bfloat16, outlier, 8.0)
     starts = np.concatenate([[0], np.cumsum(ctx0.astype(np.int64) - 1)])
     q = oracle.bf16_bits_to_f64(to_bits(q_all[s_last, layer]))
-    seqs = []
-    for b in range(0, B, 4):
-        kb = torch.cat([k_pre[starts[b]:starts[b + 1]], k_new[:s_last + 1, layer, b]])
-        vb = torch.cat([v_pre[starts[b]:starts[b + 1]], v_new[:s_last + 1, layer, b]])
-        seqs.append((b, oracle.bf16_bits_to_f64(to_bits(kb)), oracle.bf16_bits_to_f64(to_bits(vb))))
+    scale = 1.0 / math.sqrt(D)
+    sample, tokens = [], 0
+    for b in range(0, B, max(1, B // 16)):
+        n = int(ctx0[b]) + s_last
+        if sample and (len(sample) == 16 or tokens + n > 131072):
+            break
+        sample.append(b)
+        tokens += n
+    tasks, read = [], 0
+    for b in sample:
+        kb = to_bits(torch.cat([k_pre[starts[b]:starts[b + 1]], k_new[:s_last + 1, layer, b]]))
+        vb = to_bits(torch.cat([v_pre[starts[b]:starts[b + 1]], v_new[:s_last + 1, layer, b]]))
+        n, n0 = kb.shape[0], int(ctx0[b]) - 1
+        read += n if not window else min(n, min(n, sink) + window)
+        if dtype in ("fp8", "int8"):
+            pool = oracle.RefPool(1, (n + 15) // 16, H, D, dtype=dtype)
+            pool.append(0, kb[:n0], vb[:n0], np.arange(n0))
+            for t in range(n0, n):
+                pool.append(0, kb[t:t + 1], vb[t:t + 1], [t])
+            table = np.arange((n + 15) // 16)
+            tasks.append(lambda b=b, pool=pool, table=table, n=n:
+                         oracle.attention_fp64(q[b], *pool.gather_f64(0, table, n), scale))
+        else:
+            K, V = oracle.bf16_bits_to_f64(kb), oracle.bf16_bits_to_f64(vb)
+            if window:
+                tasks.append(lambda b=b, K=K, V=V:
+                             oracle.attention_window_fp64(q[b], K, V, scale, sink, window))
+            else:
+                tasks.append(lambda b=b, K=K, V=V: oracle.attention_fp64(q[b], K, V, scale))
     del k_pre, v_pre
-    kv_bytes = sum(kk.shape[0] for _, kk, _ in seqs) * H * D * 2 * 2
+    elem = 1 if dtype in ("fp8", "int8") else 2
+    kv_bytes = read * H * D * 2 * elem
     reps = 0
     workers = max(1, min(16, len(os.sched_getaffinity(0))))
-    one = lambda t: oracle.attention_fp64(q[t[0]], t[1], t[2], 1.0 / math.sqrt(D))
     with threadpool_limits(limits=1), ThreadPoolExecutor(max_workers=workers) as ex:
         t0 = time.perf_counter()
         while True:
-            list(ex.map(one, seqs))
+            list(ex.map(lambda f: f(), tasks))
             reps += 1
             if time.perf_counter() - t0 >= args.cpu_seconds:
                 break
         dt = time.perf_counter() - t0
+    what = {"fp8": "fp8 codes (oracle pool gather + fp64 attention)",
+            "int8": "int8 codes (oracle pool gather + fp64 attention)"}.get(dtype, "bf16 K/V")
+    if window:
+        what += f" through a {window}-token window + {sink} sinks"
     return {
         "value": round(kv_bytes * reps / dt / 1e9, 4),
         "unit": "GB/s",
         "cores": workers,
         "kind": "oracle",
-        "sample": f"fp64 oracle decode of {len(seqs)} of {B} requests of one layer "
-                  f"({kv_bytes / 1e6:.0f} MB of bf16 K/V), {reps} repetitions in {dt:.1f} s, "
+        "sample": f"fp64 oracle decode of {len(sample)} of {B} requests of one layer "
+                  f"({kv_bytes / 1e6:.0f} MB of {what}), {reps} repetitions in {dt:.1f} s, "
                   f"one request per task on {workers} threads, BLAS limited to 1 thread per task",
     }
 
