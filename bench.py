@@ -388,6 +388,7 @@ def churn_workload(args, torch, synth, pk, dev):
         unique.append(run.unique_kv_bytes() * w["num_layers"])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    cpu = None if args.no_cpu_baseline else churn_cpu_baseline(run, args, torch, synth, dev)
     config = {"workload": "prefix_churn_model_step", "batch": w["batch"], "layers": w["num_layers"],
               "prefix_tokens": w["prefix_tokens"], "suffix_range": list(w["suffix_range"]),
               "churn_per_step": w["churn"], "partition_tokens": 0,
@@ -396,7 +397,7 @@ def churn_workload(args, torch, synth, pk, dev):
               "admission": "kv_prefix_match of the 2000-token prefix (125 pages)",
               "admission_host_us_per_request": round(run.admit_seconds / (args.steps * w["churn"]) * 1e6, 2)}
     return dict(wall=wall, kv_total=float(sum(logical)), dec_ms=None, dec_kv=None, config=config,
-                cpu=None, dtype="bf16", kernel=None)
+                cpu=cpu, dtype="bf16", kernel=None)
 
 
 def cow_fork_workload(args, torch, synth, pk, dev):
@@ -513,10 +514,14 @@ def prefill_workload(args, torch, synth, pk, dev):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     dec_ms = np.array([e[0].elapsed_ms(e[1]) for e in events if e is not None])
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = prefill_cpu_baseline(args, torch, synth, dev, q_all[(args.warmup + args.steps - 1) % L],
+                                   (args.warmup + args.steps - 1) % L, B, P, H, h_q, D)
     config = {"workload": "llama3_8b_prefill_layer", "batch": B, "new_tokens": P, "h_q": h_q, "h_kv": H,
               "head_dim": D, "cache_dtype": "bf16", "layers_in_pool": L, "flop_per_step": flops}
     return dict(wall=wall, kv_total=float(flops) * args.steps, dec_ms=dec_ms,
-                dec_kv=np.full(len(dec_ms), float(flops)), config=config, cpu=None, traffic=measured_traffic("prefill"),
+                dec_kv=np.full(len(dec_ms), float(flops)), config=config, cpu=cpu, traffic=measured_traffic("prefill"),
                 traffic_note="HBM bytes read + written per prefill_kernel launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, "
                              "copy-calibrated); null if the kernel source changed", dtype="bf16",
                 kernel="paged_attention_prefill call (prefill_kernel)",
@@ -624,11 +629,9 @@ def cpu_baseline(ctx0, slots0_len, k_new, v_new, q_all, args, w, L, dev):
     GPU pool); the 8-bit codes come from the oracle's own append of those
     inputs, in the same calls the GPU pool received (the prefill in one call,
     then one token per model step)."""
-    from concurrent.futures import ThreadPoolExecutor
     import torch
     import oracle
     import synth
-    from threadpoolctl import threadpool_limits
 
     dtype = w["dtype"]
     B, H, h_q, D = w["batch"], w["h_kv"], w["h_q"], w["head_dim"]
@@ -673,16 +676,7 @@ def cpu_baseline(ctx0, slots0_len, k_new, v_new, q_all, args, w, L, dev):
     del k_pre, v_pre
     elem = 1 if dtype in ("fp8", "int8") else 2
     kv_bytes = read * H * D * 2 * elem
-    reps = 0
-    workers = max(1, min(16, len(os.sched_getaffinity(0))))
-    with threadpool_limits(limits=1), ThreadPoolExecutor(max_workers=workers) as ex:
-        t0 = time.perf_counter()
-        while True:
-            list(ex.map(lambda f: f(), tasks))
-            reps += 1
-            if time.perf_counter() - t0 >= args.cpu_seconds:
-                break
-        dt = time.perf_counter() - t0
+    reps, dt, workers = _time_tasks(tasks, args.cpu_seconds)
     what = {"fp8": "fp8 codes (oracle pool gather + fp64 attention)",
             "int8": "int8 codes (oracle pool gather + fp64 attention)"}.get(dtype, "bf16 K/V")
     if window:
@@ -695,6 +689,95 @@ def cpu_baseline(ctx0, slots0_len, k_new, v_new, q_all, args, w, L, dev):
         "sample": f"fp64 oracle decode of {len(sample)} of {B} requests of one layer "
                   f"({kv_bytes / 1e6:.0f} MB of {what}), {reps} repetitions in {dt:.1f} s, "
                   f"one request per task on {workers} threads, BLAS limited to 1 thread per task",
+    }
+
+
+def _time_tasks(tasks, seconds):
+    """Run every task once per repetition on a thread pool as wide as the
+    cores this process may use (at most 16), BLAS limited to one thread per
+    task, until about `seconds` have passed.  Returns (repetitions, seconds,
+    threads)."""
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    reps = 0
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    with threadpool_limits(limits=1), ThreadPoolExecutor(max_workers=workers) as ex:
+        t0 = time.perf_counter()
+        while True:
+            list(ex.map(lambda f: f(), tasks))
+            reps += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = time.perf_counter() - t0
+    return reps, dt, workers
+
+
+def churn_cpu_baseline(run, args, torch, synth, dev):
+    """The fp64 oracle decode of every 16th of the 256 requests of the last
+    layer, with the lengths they have after the timed steps: the layer's
+    shared 2000-token prefix, regenerated from its seed, followed by the
+    request's suffix.  The suffix values are the leading rows of the seeded
+    input buffer the steps append from (the same shape and distribution; the
+    exact rows a request took depend on the order of admissions).  Value:
+    logical K/V GB/s, as the workload's."""
+    import oracle
+    layer = run.layers - 1
+    to_bits = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    pk_ = oracle.bf16_bits_to_f64(to_bits(synth.device_normal(
+        (run.prefix_len, 8, 128), run._seed("prefix_k", layer), dev, torch.bfloat16)))
+    pv_ = oracle.bf16_bits_to_f64(to_bits(synth.device_normal(
+        (run.prefix_len, 8, 128), run._seed("prefix_v", layer), dev, torch.bfloat16)))
+    q = oracle.bf16_bits_to_f64(to_bits(run.reuse[2]))
+    scale = 1.0 / math.sqrt(128)
+    tasks, tokens = [], 0
+    for b in range(0, run.batch, 16):
+        n = int(run.lens[b])
+        ns = n - run.prefix_len
+        K = np.concatenate([pk_, oracle.bf16_bits_to_f64(to_bits(run.reuse[0][:ns]))])
+        V = np.concatenate([pv_, oracle.bf16_bits_to_f64(to_bits(run.reuse[1][:ns]))])
+        tasks.append(lambda b=b, K=K, V=V: oracle.attention_fp64(q[b], K, V, scale))
+        tokens += n
+    kv_bytes = tokens * 8 * 128 * 2 * 2
+    reps, dt, workers = _time_tasks(tasks, args.cpu_seconds)
+    return {
+        "value": round(kv_bytes * reps / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": workers,
+        "kind": "oracle",
+        "sample": f"fp64 oracle decode of {len(tasks)} of {run.batch} requests of one layer "
+                  f"({kv_bytes / 1e6:.0f} MB of bf16 K/V, {run.prefix_len}-token prefix + suffix each), {reps} "
+                  f"repetitions in {dt:.1f} s, one request per task on {workers} threads, BLAS limited "
+                  f"to 1 thread per task",
+    }
+
+
+def prefill_cpu_baseline(args, torch, synth, dev, q_layer, layer, B, P, H, h_q, D):
+    """The fp64 oracle prefill of every 16th query of the first request of
+    the last layer run: query i over positions 0..i (the oracle called on
+    that one query and its causal keys).  Inputs regenerated from the same
+    seeds.  Value: attention TFLOP/s counted as the workload's."""
+    import oracle
+    to_bits = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    # the layer's K/V as appended (all requests, drawn in one call), request 0's rows
+    K = oracle.bf16_bits_to_f64(to_bits(synth.device_normal((B * P, H, D), 4000 + 2 * layer, dev,
+                                                            torch.bfloat16)[:P]))
+    V = oracle.bf16_bits_to_f64(to_bits(synth.device_normal((B * P, H, D), 4001 + 2 * layer, dev,
+                                                            torch.bfloat16)[:P]))
+    q = oracle.bf16_bits_to_f64(to_bits(q_layer[:P]))
+    scale = 1.0 / math.sqrt(D)
+    rows = list(range(15, P, 16))
+    tasks = [lambda i=i: oracle.prefill_attention_fp64(q[i:i + 1], K[:i + 1], V[:i + 1], scale)
+             for i in rows]
+    flops = sum(i + 1 for i in rows) * h_q * 4 * D
+    reps, dt, workers = _time_tasks(tasks, args.cpu_seconds)
+    return {
+        "value": round(flops * reps / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": workers,
+        "kind": "oracle",
+        "sample": f"fp64 oracle prefill of {len(rows)} of the {P} queries of one request of one layer "
+                  f"(every 16th, each over its causal keys; {flops / 1e9:.2f} GFLOP), {reps} repetitions "
+                  f"in {dt:.1f} s, one query per task on {workers} threads, BLAS limited to 1 thread per task",
     }
 
 
