@@ -23,6 +23,12 @@
  *    throws.  On a non-OK return, kv_last_error() gives a message for the
  *    calling thread.  Host-side state is unchanged by a failed call unless the
  *    function says otherwise.
+ *  - Exhausted host memory is reported as KV_E_INVALID with a "host memory"
+ *    message.  kv_pool_create then creates nothing, and the batch
+ *    reservations and kv_window_release change nothing (they allocate before
+ *    they change any state).  After such an error from kv_prefix_match,
+ *    kv_prefix_insert or kv_prefix_evict, the prefix cache and the
+ *    reference counts it holds are unspecified.
  *  - Device pointers are HIP device addresses on the current device; host
  *    pointers are ordinary process memory.  The library never allocates,
  *    frees or copies device memory itself: the caller owns every buffer, and

@@ -4,6 +4,7 @@
 
 #include <array>
 #include <cstdint>
+#include <exception>
 #include <set>
 #include <string>
 #include <unordered_map>
@@ -65,9 +66,35 @@ namespace pagedkv {
 constexpr int kBlockSize = 16;
 constexpr int kDefaultPartition = 512;
 
-// Records a message for kv_last_error() and returns `status`.
+// Records a message for kv_last_error() and returns `status` (never throws).
 int fail(int status, const char* fmt, ...);
 int ok();
+
+// Runs the body of an entry point that allocates host memory, turning a
+// failed allocation into an error status so that no C++ exception crosses
+// the C interface.
+template <class F>
+int nothrow_call(F&& body) {
+  try {
+    return body();
+  } catch (const std::exception& e) {
+    return fail(KV_E_INVALID, "host memory: %s", e.what());
+  }
+}
+
+// Upper bound on the blocks a batch reservation can take: the new blocks
+// every request needs (requests with negative sizes count none; the
+// reservation rejects them), and never more than the free list holds.
+inline size_t reserve_bound(int32_t B, const int32_t* lens, const int32_t* n_new, int32_t bs, size_t n_free) {
+  size_t total = 0;
+  for (int32_t b = 0; b < B && total < n_free; ++b) {
+    if (lens[b] < 0 || n_new[b] <= 0) continue;
+    const int64_t have = (int64_t(lens[b]) + bs - 1) / bs;
+    const int64_t need = (int64_t(lens[b]) + n_new[b] + bs - 1) / bs;
+    total += size_t(need - have);
+  }
+  return total < n_free ? total : n_free;
+}
 
 inline int elem_bytes(int dtype) { return dtype == KV_F32 ? 4 : dtype == KV_BF16 ? 2 : 1; }
 

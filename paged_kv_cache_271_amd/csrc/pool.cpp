@@ -10,11 +10,12 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <memory>
 
 #include "internal.h"
 
 namespace {
-thread_local std::string g_last_error;
+thread_local char g_last_error[512];
 
 bool desc_valid(const kv_pool_desc* d) {
   return d && d->num_layers >= 1 && d->num_blocks >= 1 && d->block_size >= 1 &&
@@ -26,12 +27,10 @@ bool desc_valid(const kv_pool_desc* d) {
 namespace pagedkv {
 
 int fail(int status, const char* fmt, ...) {
-  char buf[512];
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof buf, fmt, ap);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
   va_end(ap);
-  g_last_error = buf;
   return status;
 }
 
@@ -66,41 +65,41 @@ int kv_pool_buffer_bytes(const kv_pool_desc* d, int64_t* cache_bytes, int64_t* s
 
 int kv_pool_create(const kv_pool_desc* d, void* k_cache, void* v_cache, float* k_scale,
                    float* v_scale, const int32_t* order, kv_pool** out) {
-  if (!out) return fail(KV_E_INVALID, "out is NULL");
-  *out = nullptr;
-  if (!desc_valid(d)) return fail(KV_E_INVALID, "invalid pool descriptor");
-  if (d->block_size != kBlockSize)
-    return fail(KV_E_UNSUPPORTED, "block_size %d not supported (16 only)", d->block_size);
-  if (d->head_dim != 64 && d->head_dim != 128)
-    return fail(KV_E_UNSUPPORTED, "head_dim %d not supported (64 or 128)", d->head_dim);
-  if (!k_cache || !v_cache) return fail(KV_E_INVALID, "k_cache and v_cache are required");
-  const bool scaled = scaled_dtype(d->cache_dtype);
-  if (scaled && (!k_scale || !v_scale))
-    return fail(KV_E_INVALID, "fp8 and int8 pools need k_scale and v_scale");
-  if (!scaled && (k_scale || v_scale))
-    return fail(KV_E_INVALID, "scale arrays are only for fp8 and int8 pools");
-  const int32_t n = d->num_blocks;
-  std::vector<int32_t> seen(n, 0);
-  auto* p = new (std::nothrow) kv_pool();
-  if (!p) return fail(KV_E_INVALID, "out of host memory");
-  p->desc = *d;
-  p->k_cache = k_cache;
-  p->v_cache = v_cache;
-  p->k_scale = k_scale;
-  p->v_scale = v_scale;
-  p->rc.assign(n, 0);
-  p->stack.resize(n);
-  for (int32_t i = 0; i < n; ++i) {
-    const int32_t b = order ? order[i] : i;
-    if (b < 0 || b >= n || seen[b]) {
-      delete p;
-      return fail(KV_E_INVALID, "initial_free_order is not a permutation (entry %d = %d)", i, b);
+  return nothrow_call([&]() -> int {
+    if (!out) return fail(KV_E_INVALID, "out is NULL");
+    *out = nullptr;
+    if (!desc_valid(d)) return fail(KV_E_INVALID, "invalid pool descriptor");
+    if (d->block_size != kBlockSize)
+      return fail(KV_E_UNSUPPORTED, "block_size %d not supported (16 only)", d->block_size);
+    if (d->head_dim != 64 && d->head_dim != 128)
+      return fail(KV_E_UNSUPPORTED, "head_dim %d not supported (64 or 128)", d->head_dim);
+    if (!k_cache || !v_cache) return fail(KV_E_INVALID, "k_cache and v_cache are required");
+    const bool scaled = scaled_dtype(d->cache_dtype);
+    if (scaled && (!k_scale || !v_scale))
+      return fail(KV_E_INVALID, "fp8 and int8 pools need k_scale and v_scale");
+    if (!scaled && (k_scale || v_scale))
+      return fail(KV_E_INVALID, "scale arrays are only for fp8 and int8 pools");
+    const int32_t n = d->num_blocks;
+    std::vector<int32_t> seen(n, 0);
+    std::unique_ptr<kv_pool> owned(new kv_pool());
+    kv_pool* p = owned.get();
+    p->desc = *d;
+    p->k_cache = k_cache;
+    p->v_cache = v_cache;
+    p->k_scale = k_scale;
+    p->v_scale = v_scale;
+    p->rc.assign(n, 0);
+    p->stack.resize(n);
+    for (int32_t i = 0; i < n; ++i) {
+      const int32_t b = order ? order[i] : i;
+      if (b < 0 || b >= n || seen[b])
+        return fail(KV_E_INVALID, "initial_free_order is not a permutation (entry %d = %d)", i, b);
+      seen[b] = 1;
+      p->stack[n - 1 - i] = b;  // order[0] ends on top
     }
-    seen[b] = 1;
-    p->stack[n - 1 - i] = b;  // order[0] ends on top
-  }
-  *out = p;
-  return ok();
+    *out = owned.release();
+    return ok();
+  });
 }
 
 int kv_pool_destroy(kv_pool* p) {
@@ -196,73 +195,81 @@ int kv_slot_mapping(const kv_pool* p, const int32_t* table_row, int32_t n_table,
 
 int kv_batch_reserve(kv_pool* p, int32_t B, int32_t* table, int32_t max_blocks, int32_t* lens,
                      const int32_t* n_new, int32_t* slots_out) {
-  if (!p) return fail(KV_E_INVALID, "NULL pool");
-  if (B < 0 || max_blocks < 0) return fail(KV_E_INVALID, "negative size");
-  if (B == 0) return ok();
-  if (!table || !lens || !n_new || !slots_out) return fail(KV_E_INVALID, "NULL array");
-  const int32_t bs = p->desc.block_size;
-  // (request, block index, previous table value) of every block taken here
-  std::vector<int64_t> taken_at;
-  std::vector<int32_t> taken_prev, taken_blk;
-  int status = KV_OK;
-  int64_t o = 0;
-  int32_t b = 0;
-  for (; b < B && status == KV_OK; ++b) {
-    const int32_t len = lens[b], add = n_new[b];
-    if (len < 0 || add < 0) {
-      status = fail(KV_E_INVALID, "request %d: negative length", b);
-      break;
+  return nothrow_call([&]() -> int {
+    if (!p) return fail(KV_E_INVALID, "NULL pool");
+    if (B < 0 || max_blocks < 0) return fail(KV_E_INVALID, "negative size");
+    if (B == 0) return ok();
+    if (!table || !lens || !n_new || !slots_out) return fail(KV_E_INVALID, "NULL array");
+    const int32_t bs = p->desc.block_size;
+    // (request, block index, previous table value) of every block taken here
+    std::vector<int64_t> taken_at;
+    std::vector<int32_t> taken_prev, taken_blk;
+    {  // room for every block this call can take, before anything changes
+      const size_t cap = reserve_bound(B, lens, n_new, bs, p->stack.size());
+      taken_at.reserve(cap);
+      taken_prev.reserve(cap);
+      taken_blk.reserve(cap);
     }
-    const int64_t end = int64_t(len) + add;
-    if (kv_blocks_for_tokens(int32_t(end), bs) > max_blocks || end > INT32_MAX) {
-      status = fail(KV_E_INVALID, "request %d grows to %lld tokens, beyond %d blocks", b,
-                    (long long)end, max_blocks);
-      break;
-    }
-    if (add == 0) continue;
-    int32_t* row = table + int64_t(b) * max_blocks;
-    const int32_t have = kv_blocks_for_tokens(len, bs);
-    if (len % bs != 0) {  // the partially filled last block is written in place
-      const int32_t last = row[have - 1];
-      if (!block_live(p, last)) {
-        status = fail(KV_E_BAD_BLOCK, "request %d: last block %d out of range or free", b, last);
+    int status = KV_OK;
+    int64_t o = 0;
+    int32_t b = 0;
+    for (; b < B && status == KV_OK; ++b) {
+      const int32_t len = lens[b], add = n_new[b];
+      if (len < 0 || add < 0) {
+        status = fail(KV_E_INVALID, "request %d: negative length", b);
         break;
       }
-      if (p->rc[last] > 1) {
-        status = fail(KV_E_SHARED, "request %d: last block %d is shared", b, last);
+      const int64_t end = int64_t(len) + add;
+      if (kv_blocks_for_tokens(int32_t(end), bs) > max_blocks || end > INT32_MAX) {
+        status = fail(KV_E_INVALID, "request %d grows to %lld tokens, beyond %d blocks", b,
+                      (long long)end, max_blocks);
         break;
       }
-    }
-    const int32_t need = kv_blocks_for_tokens(int32_t(end), bs);
-    for (int32_t j = have; j < need; ++j) {
-      if (p->stack.empty()) {
-        status = fail(KV_E_NO_BLOCKS, "request %d: no free block for logical block %d", b, j);
-        break;
+      if (add == 0) continue;
+      int32_t* row = table + int64_t(b) * max_blocks;
+      const int32_t have = kv_blocks_for_tokens(len, bs);
+      if (len % bs != 0) {  // the partially filled last block is written in place
+        const int32_t last = row[have - 1];
+        if (!block_live(p, last)) {
+          status = fail(KV_E_BAD_BLOCK, "request %d: last block %d out of range or free", b, last);
+          break;
+        }
+        if (p->rc[last] > 1) {
+          status = fail(KV_E_SHARED, "request %d: last block %d is shared", b, last);
+          break;
+        }
       }
-      const int32_t nb = p->stack.back();
-      p->stack.pop_back();
-      p->rc[nb] = 1;
-      taken_at.push_back(int64_t(b) * max_blocks + j);
-      taken_prev.push_back(row[j]);
-      taken_blk.push_back(nb);
-      row[j] = nb;
+      const int32_t need = kv_blocks_for_tokens(int32_t(end), bs);
+      for (int32_t j = have; j < need; ++j) {
+        if (p->stack.empty()) {
+          status = fail(KV_E_NO_BLOCKS, "request %d: no free block for logical block %d", b, j);
+          break;
+        }
+        const int32_t nb = p->stack.back();
+        p->stack.pop_back();
+        p->rc[nb] = 1;
+        taken_at.push_back(int64_t(b) * max_blocks + j);
+        taken_prev.push_back(row[j]);
+        taken_blk.push_back(nb);
+        row[j] = nb;
+      }
+      if (status != KV_OK) break;
+      for (int32_t i = 0; i < add; ++i) {
+        const int32_t pos = len + i;
+        slots_out[o++] = row[pos / bs] * bs + pos % bs;
+      }
     }
-    if (status != KV_OK) break;
-    for (int32_t i = 0; i < add; ++i) {
-      const int32_t pos = len + i;
-      slots_out[o++] = row[pos / bs] * bs + pos % bs;
+    if (status != KV_OK) {
+      for (size_t i = taken_blk.size(); i-- > 0;) {  // undo in reverse: stack as before
+        p->rc[taken_blk[i]] = 0;
+        p->stack.push_back(taken_blk[i]);
+        table[taken_at[i]] = taken_prev[i];
+      }
+      return status;
     }
-  }
-  if (status != KV_OK) {
-    for (size_t i = taken_blk.size(); i-- > 0;) {  // undo in reverse: stack as before
-      p->rc[taken_blk[i]] = 0;
-      p->stack.push_back(taken_blk[i]);
-      table[taken_at[i]] = taken_prev[i];
-    }
-    return status;
-  }
-  for (int32_t i = 0; i < B; ++i) lens[i] += n_new[i];
-  return ok();
+    for (int32_t i = 0; i < B; ++i) lens[i] += n_new[i];
+    return ok();
+  });
 }
 
 int kv_append(kv_pool* p, int32_t layer, const void* k_new, const void* v_new,
@@ -412,43 +419,45 @@ int paged_attention_prefill(kv_pool* p, int32_t layer, void* out, const void* q,
 
 int kv_window_release(kv_pool* p, int32_t B, int32_t* table, int32_t max_blocks, const int32_t* lens,
                       int32_t sink, int32_t window, int32_t* n_released) {
-  if (!p || !n_released) return fail(KV_E_INVALID, "NULL argument");
-  if (B < 0 || max_blocks < 0) return fail(KV_E_INVALID, "negative size");
-  if (sink < 0 || window < 1)
-    return fail(KV_E_INVALID, "sink %d must be >= 0 and window %d >= 1", sink, window);
-  *n_released = 0;
-  if (B == 0) return ok();
-  if (!table || !lens) return fail(KV_E_INVALID, "NULL array");
-  const int32_t bs = p->desc.block_size;
-  // check everything first (a block may be dropped by several tables, at most
-  // as often as it is mapped): nothing changes on an error
-  std::unordered_map<int32_t, int32_t> drops;
-  for (int32_t b = 0; b < B; ++b) {
-    const int32_t n = lens[b];
-    if (n < 0 || kv_blocks_for_tokens(n, bs) > max_blocks)
-      return fail(KV_E_INVALID, "request %d: length %d outside a table of %d blocks", b, n, max_blocks);
-    const int32_t* row = table + int64_t(b) * max_blocks;
-    for (int32_t j = 0; int64_t(j + 1) * bs <= int64_t(n) - window; ++j) {
-      if (int64_t(j) * bs < sink || row[j] == -1) continue;
-      if (!block_live(p, row[j]) || ++drops[row[j]] > p->rc[row[j]])
-        return fail(KV_E_BAD_BLOCK, "request %d: block %d (page %d) out of range, free or over-released", b,
-                    row[j], j);
+  return nothrow_call([&]() -> int {
+    if (!p || !n_released) return fail(KV_E_INVALID, "NULL argument");
+    if (B < 0 || max_blocks < 0) return fail(KV_E_INVALID, "negative size");
+    if (sink < 0 || window < 1)
+      return fail(KV_E_INVALID, "sink %d must be >= 0 and window %d >= 1", sink, window);
+    *n_released = 0;
+    if (B == 0) return ok();
+    if (!table || !lens) return fail(KV_E_INVALID, "NULL array");
+    const int32_t bs = p->desc.block_size;
+    // check everything first (a block may be dropped by several tables, at most
+    // as often as it is mapped): nothing changes on an error
+    std::unordered_map<int32_t, int32_t> drops;
+    for (int32_t b = 0; b < B; ++b) {
+      const int32_t n = lens[b];
+      if (n < 0 || kv_blocks_for_tokens(n, bs) > max_blocks)
+        return fail(KV_E_INVALID, "request %d: length %d outside a table of %d blocks", b, n, max_blocks);
+      const int32_t* row = table + int64_t(b) * max_blocks;
+      for (int32_t j = 0; int64_t(j + 1) * bs <= int64_t(n) - window; ++j) {
+        if (int64_t(j) * bs < sink || row[j] == -1) continue;
+        if (!block_live(p, row[j]) || ++drops[row[j]] > p->rc[row[j]])
+          return fail(KV_E_BAD_BLOCK, "request %d: block %d (page %d) out of range, free or over-released", b,
+                      row[j], j);
+      }
     }
-  }
-  int32_t released = 0;
-  for (int32_t b = 0; b < B; ++b) {
-    int32_t* row = table + int64_t(b) * max_blocks;
-    // dead pages: every position at or past the sinks and before n - window
-    for (int32_t j = 0; int64_t(j + 1) * bs <= int64_t(lens[b]) - window; ++j) {
-      if (int64_t(j) * bs < sink || row[j] == -1) continue;
-      const int32_t blk = row[j];
-      if (--p->rc[blk] == 0) p->stack.push_back(blk);
-      row[j] = -1;
-      ++released;
+    int32_t released = 0;
+    for (int32_t b = 0; b < B; ++b) {
+      int32_t* row = table + int64_t(b) * max_blocks;
+      // dead pages: every position at or past the sinks and before n - window
+      for (int32_t j = 0; int64_t(j + 1) * bs <= int64_t(lens[b]) - window; ++j) {
+        if (int64_t(j) * bs < sink || row[j] == -1) continue;
+        const int32_t blk = row[j];
+        if (--p->rc[blk] == 0) p->stack.push_back(blk);
+        row[j] = -1;
+        ++released;
+      }
     }
-  }
-  *n_released = released;
-  return ok();
+    *n_released = released;
+    return ok();
+  });
 }
 
 const char* kv_status_string(int s) {
@@ -465,6 +474,6 @@ const char* kv_status_string(int s) {
   }
 }
 
-const char* kv_last_error(void) { return g_last_error.c_str(); }
+const char* kv_last_error(void) { return g_last_error; }
 
 }  // extern "C"
