@@ -301,6 +301,10 @@ def decode_workload(args, torch, synth, pk, dev, spec=None, layers=0):
     dec_ms = np.array([e[0].elapsed_ms(e[1]) for e in events if e is not None])
     dec_kv = np.array([per_step_kv[j] for j in range(args.steps) if events[j] is not None], float)
 
+    probe = None
+    if spec is None and not window and (H % 4) == 0 and h_q // H <= 16:
+        probe = gather_probe(pool, table, lens, L, H, D, elem, torch, pk, dev)
+        log(f"gather probe: {probe['us']:.1f} us for {probe['bytes'] / 1e6:.1f} MB ({probe['gbs']:.0f} GB/s)")
     cpu = None
     if spec is None and not args.no_cpu_baseline:
         cpu = cpu_baseline(ctx0, T0, k_new, v_new, q_all, args, w, L, dev)
@@ -312,7 +316,7 @@ def decode_workload(args, torch, synth, pk, dev, spec=None, layers=0):
         **({"sink_tokens": sink, "window_tokens": window} if window else {}),
         "step": "kv_append + paged_attention_decode" if two_calls else "paged_attention_decode_append",
     }
-    return dict(wall=wall, kv_total=float(sum(per_step_kv)), dec_ms=dec_ms, dec_kv=dec_kv,
+    return dict(wall=wall, kv_total=float(sum(per_step_kv)), dec_ms=dec_ms, dec_kv=dec_kv, probe=probe,
                 config=config, cpu=cpu, traffic=measured_traffic(name, args.two_calls), dtype={"fp8": "fp8-e4m3 K/V, bf16 q", "int8": "int8 K/V, bf16 q"}.get(dtype, "bf16"),
                 kernel=("paged_attention_decode_window" if window else
                         "paged_attention_decode" if two_calls else "paged_attention_decode_append")
@@ -588,6 +592,14 @@ def main():
             "us_per_call_p10_p50_p90": [round(float(np.percentile(r["dec_ms"], x)) * 1e3, 2) for x in (10, 50, 90)],
             "calls_timed": int(len(r["dec_ms"])),
         }
+        if r.get("probe"):
+            pr = r["probe"]
+            roofline["gather_probe"] = {
+                "us_per_launch": round(pr["us"], 2), "bytes": pr["bytes"], "gbs": round(pr["gbs"], 1),
+                "call_over_probe_time": round(dec_mean_s * 1e6 / pr["us"], 4),
+                "note": "kv_probe_gather over the 16 KiB K and V runs of the final step's tables, same split "
+                        "and grid as the decode, no arithmetic: the gather alone on this GPU",
+            }
     config = dict(r["config"])
     config["us_per_step"] = round(ms_per_step * 1e3, 2)
     if unit == "GB/s":
@@ -690,6 +702,45 @@ def cpu_baseline(ctx0, slots0_len, k_new, v_new, q_all, args, w, L, dev):
                   f"({kv_bytes / 1e6:.0f} MB of {what}), {reps} repetitions in {dt:.1f} s, "
                   f"one request per task on {workers} threads, BLAS limited to 1 thread per task",
     }
+
+
+def gather_probe(pool, table, lens, L, H, D, elem, torch, pk, dev, launches=64, warm=8):
+    """Time kv_probe_gather over the K/V runs the decode reads for the current
+    tables: for every request b, set of four kv heads s and block j the
+    decode's unit (b, s, j) reads the four adjacent tiles of heads 4s..4s+3 in
+    block table[b][j], one run in K and one in V.  Units go in the decode's
+    order over the decode's 768 workgroups.  Launches rotate over the pool's
+    layers, as the decode steps do, and each is bracketed by HIP events on the
+    launch stream; the reported time is the median launch.  Bytes are the
+    runs' bytes (whole blocks)."""
+    tile = 16 * D * elem
+    offs = []
+    for b in range(len(lens)):
+        nb = (int(lens[b]) + 15) // 16
+        for s in range(H // 4):
+            offs.extend((int(table[b, j]) * H + 4 * s) * tile for j in range(nb))
+    offs = np.array(offs, np.int64)
+    assert offs.size and offs.min() >= 0 and offs.max() + 4 * tile <= pool.k_cache[0].numel() * pool.k_cache.element_size()
+    d_off = torch.from_numpy(offs).to(dev)
+    sink = torch.empty(768, dtype=torch.int32, device=dev)
+    layer_bytes = pool.k_cache[0].numel() * pool.k_cache.element_size()
+    kb, vb = pool.k_cache.data_ptr(), pool.v_cache.data_ptr()
+    stream = torch.cuda.current_stream()
+    # every event exists before the first launch and lives until the end, so
+    # no event is created or destroyed between a record and its launch
+    events = [(TimingEvent(), TimingEvent()) for _ in range(warm + launches)]
+    torch.cuda.synchronize()
+    for i, ev in enumerate(events):
+        layer = i % L
+        ev[0].record(stream)
+        pk.kv_probe_gather(kb + layer * layer_bytes, vb + layer * layer_bytes, d_off, d_off, 4 * tile, sink)
+        ev[1].record(stream)
+    torch.cuda.synchronize()
+    t_us = np.array([a.elapsed_ms(b) for a, b in events[warm:]]) * 1e3
+    us = float(np.median(t_us))
+    nbytes = int(offs.size) * 2 * 4 * tile
+    log(f"gather probe launches: median {us:.1f} us, min {t_us.min():.1f}, max {t_us.max():.1f} over {len(t_us)}")
+    return {"us": us, "bytes": nbytes, "gbs": nbytes / us / 1e3}
 
 
 def _time_tasks(tasks, seconds):

@@ -19,7 +19,7 @@ STATUS = {0: "KV_OK", -1: "KV_E_INVALID", -2: "KV_E_UNSUPPORTED", -3: "KV_E_NO_B
 DTYPE_NAMES = {"f32": KV_F32, "bf16": KV_BF16, "fp8": KV_FP8_E4M3, "int8": KV_INT8}
 BLOCK_SIZE = 16
 
-# every function pagedkv.h declares: name -> (restype, argtypes)
+# every function include/*.h declares: name -> (restype, argtypes)
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
@@ -68,6 +68,8 @@ SIGNATURES = {
     "kv_window_release": (ctypes.c_int, [_P, _I32, _PI32, _I32, _PI32, _I32, _I32, _PI32]),
     "paged_attention_prefill": (ctypes.c_int, [_P, _I32, _P, _P, _I32, _P, _I32, _P, _P, _I32, _I32, _I32,
                                                _I32, ctypes.c_float, _P]),
+    # pagedkv_probe.h (a measurement aid, not part of the attention path)
+    "kv_probe_gather": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _P, _I32, _P]),
     "kv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kv_last_error": (ctypes.c_char_p, []),
 }
@@ -309,6 +311,20 @@ def kv_block_copy(h, src, dst, stream=None):
     sp = _dev_ptr(src, "src", torch.int32)
     dp = _dev_ptr(dst, "dst", torch.int32, n)
     _check(_lib.kv_block_copy(h, sp, dp, n, _stream_ptr(stream)))
+
+
+def kv_probe_gather(k_base, v_base, k_offsets, v_offsets, run_bytes, sink, stream=None):
+    """Measurement aid: read run_bytes at k_base + k_offsets[i] and v_base +
+    v_offsets[i] for every i (int64 device tensors); k_base, v_base: device
+    addresses (ints); sink: uint32-sized int32 device tensor, one entry per
+    workgroup, receiving XORs of the words read."""
+    import torch
+    n = k_offsets.numel()
+    kp = _dev_ptr(k_offsets, "k_offsets", torch.int64)
+    vp = _dev_ptr(v_offsets, "v_offsets", torch.int64, n)
+    sp = _dev_ptr(sink, "sink", torch.int32)
+    _check(_lib.kv_probe_gather(ctypes.c_void_p(k_base), ctypes.c_void_p(v_base), kp, vp, n, int(run_bytes),
+                                sp, sink.numel(), _stream_ptr(stream)))
 
 
 def kv_append(h, desc, layer, k_new, v_new, slot_mapping, stream=None):
