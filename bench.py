@@ -52,8 +52,9 @@ DEFAULT_SEED = {"llama3_8b": 2, "llama3_70b_long": 3, "fp8": 5, "int8": 5, "pref
 # calibration there (fetch x2, write x1).  They hold for the kernel source they
 # were taken on, identified by its SHA-256; any other source reports null.
 TRAFFIC_SOURCE = "paged_kv_cache_271_amd/csrc/decode.hip"
-TRAFFIC_SHA256 = "b24903c30fad8fa8824c79d139ba5c2fbc071b31f0f9eac989d65f62c8f56e42"
-TRAFFIC_BYTES = {"llama3_8b": 594_945_229, "fp8": 1_235_771_597, "llama3_70b_long": 1_360_146_227, "int8": 1_236_131_328, "llama3_8b_window": 1_095_975_629}
+TRAFFIC_SHA256 = "97e4da76de18ac7d8c254a29b690939b29be450e6a5b77ef45f15bea1548a426"
+TRAFFIC_BYTES = {"llama3_8b": 594_975_095, "fp8": 1_235_695_533, "llama3_70b_long": 1_360_392_307, "int8": 1_235_975_238,
+                 "llama3_8b_window": 1_096_168_225}
 # The same per launch of prefill_kernel and of block_copy_kernel, from
 # profiles/prefill_llama3_8b_counters.md and
 # profiles/block_copy_cow_fork_hbm_counters.md: (source, its SHA-256, bytes).

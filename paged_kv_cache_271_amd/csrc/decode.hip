@@ -233,10 +233,10 @@ __device__ inline void progress_prio(int64_t done, int64_t total) {
   done = uniform64(done);
   total = uniform64(total);
   if (total <= 0) return;
-  const int64_t x = done * 20;
-  if (x < 12 * total) __builtin_amdgcn_s_setprio(3);
-  else if (x < 17 * total) __builtin_amdgcn_s_setprio(2);
-  else if (x < 19 * total) __builtin_amdgcn_s_setprio(1);
+  const int64_t x = done * 20;  // priority 3 below 50% done, 2 below 75%, 1 below 90%, then 0
+  if (x < 10 * total) __builtin_amdgcn_s_setprio(3);
+  else if (x < 15 * total) __builtin_amdgcn_s_setprio(2);
+  else if (x < 18 * total) __builtin_amdgcn_s_setprio(1);
   else __builtin_amdgcn_s_setprio(0);
 }
 
