@@ -12,6 +12,7 @@
 // spelled out in pagedkv.h at kv_append.
 
 #include <cstdint>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -21,27 +22,71 @@ namespace {
 constexpr int kBS = kBlockSize;
 
 // ---------------------------------------------------------------- copy ----
-// One workgroup per (token, kv-head); thread d moves element d of K (to a
-// contiguous row) and of V (to a column of the dim-major tile).
-template <typename T>
-__global__ void __launch_bounds__(128) append_copy_kernel(T* __restrict__ kc, T* __restrict__ vc,
+// One workgroup of 256 threads per (token t, kv-head g); only the first token
+// of a run works, for the whole run.  A run is a maximal sequence of tokens
+// of the call whose slots are consecutive within one block (1 to 16 tokens).
+// The slots of tokens t - 1 .. t + 16 are read in one round trip by wave 0,
+// and a ballot gives the run's length.  K rows go over in 16-byte pieces
+// (a row is contiguous in the tile); V rows pass through LDS so that each
+// thread writes its dimension's entries of the run into the dim-major tile,
+// a whole 16-token row in 16-byte stores when the run fills the block.
+template <typename T, int D>
+__global__ void __launch_bounds__(256) append_copy_kernel(T* __restrict__ kc, T* __restrict__ vc,
                                                           const T* __restrict__ k_new,
                                                           const T* __restrict__ v_new,
-                                                          const int32_t* __restrict__ slots,
-                                                          int H, int D) {
+                                                          const int32_t* __restrict__ slots, int n_tok,
+                                                          int H) {
+  constexpr int RB = D * int(sizeof(T));  // bytes of one token row
+  constexpr int PR = RB / 16;             // 16-byte pieces per row
+  __shared__ __attribute__((aligned(16))) T s_v[kBS][D];
+  __shared__ int32_t s_run[2];  // first slot, run length (0: not a run start)
   const int t = blockIdx.x;
   const int g = blockIdx.y;
-  const int d = threadIdx.x;  // blockDim.x == D
-  // the inputs do not depend on the slot: load them alongside it
-  const T kx = k_new[(int64_t(t) * H + g) * D + d];
-  const T vx = v_new[(int64_t(t) * H + g) * D + d];
-  const int32_t slot = slots[t];
-  if (slot < 0) return;
-  const int64_t blk = slot / kBS;
-  const int off = slot % kBS;
-  const int64_t tile = (blk * H + g) * int64_t(kBS) * D;
-  kc[tile + int64_t(off) * D + d] = kx;
-  vc[tile + int64_t(d) * kBS + off] = vx;
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const int i = tid - 1;  // lane 1 + i reads the slot of token t + i
+    int32_t sl = -1;
+    if (tid <= kBS && t + i >= 0 && t + i < n_tok) sl = slots[t + i];
+    const int32_t s0 = __shfl(sl, 1);
+    const int32_t sp = __shfl(sl, 0);
+    const bool start = s0 >= 0 && !(sp >= 0 && sp + 1 == s0 && s0 % kBS != 0);
+    const bool ok = tid >= 1 && tid <= kBS && s0 >= 0 && sl == s0 + i && s0 % kBS + i < kBS;
+    // leading lanes 1.. that continue the run; lane 17 never does
+    const uint64_t broken = ~(uint64_t(__ballot(ok)) >> 1);
+    if (tid == 0) {
+      s_run[0] = s0;
+      s_run[1] = start ? __builtin_ctzll(broken) : 0;
+    }
+  }
+  __syncthreads();
+  const int n = s_run[1];
+  if (n == 0) return;
+  const int32_t s0 = s_run[0];
+  const int o0 = s0 % kBS;
+  const int64_t tile = (int64_t(s0 / kBS) * H + g) * kBS * D;  // elements
+  uint8_t* kt = reinterpret_cast<uint8_t*>(kc + tile);
+  for (int p = tid; p < n * PR; p += 256) {
+    const int r = p / PR, c = p - r * PR;
+    const int64_t src = (int64_t(t + r) * H + g) * RB + 16 * c;
+    *reinterpret_cast<uint4*>(kt + (o0 + r) * RB + 16 * c) =
+        *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(k_new) + src);
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(&s_v[r][0]) + 16 * c) =
+        *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(v_new) + src);
+  }
+  __syncthreads();
+  if (tid < D) {
+    T* row = vc + tile + int64_t(tid) * kBS;  // the tile's row of dimension tid
+    if (n == kBS) {
+      alignas(16) T e[kBS];
+#pragma unroll
+      for (int r = 0; r < kBS; ++r) e[r] = s_v[r][tid];
+#pragma unroll
+      for (int w = 0; w < kBS * int(sizeof(T)) / 16; ++w)
+        reinterpret_cast<uint4*>(row)[w] = reinterpret_cast<const uint4*>(e)[w];
+    } else {
+      for (int r = 0; r < n; ++r) row[o0 + r] = s_v[r][tid];
+    }
+  }
 }
 
 // ----------------------------------------------------------------- fp8 ----
@@ -202,16 +247,23 @@ int launch_append(const kv_pool* p, int32_t layer, const void* k_new, const void
   const int64_t lo = int64_t(layer) * layer_elems(d);
   const dim3 grid(T, d.num_kv_heads);
   const int D = d.head_dim;
-  if (d.cache_dtype == KV_F32) {
-    append_copy_kernel<float><<<grid, D, 0, stream>>>(
-        static_cast<float*>(p->k_cache) + lo, static_cast<float*>(p->v_cache) + lo,
-        static_cast<const float*>(k_new), static_cast<const float*>(v_new), slots, d.num_kv_heads,
-        d.head_dim);
-  } else if (d.cache_dtype == KV_BF16) {
-    append_copy_kernel<uint16_t><<<grid, D, 0, stream>>>(
-        static_cast<uint16_t*>(p->k_cache) + lo, static_cast<uint16_t*>(p->v_cache) + lo,
-        static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), slots,
-        d.num_kv_heads, d.head_dim);
+  if (d.cache_dtype == KV_F32 || d.cache_dtype == KV_BF16) {
+    auto go = [&](auto elem, auto dim) {
+      using E = decltype(elem);
+      constexpr int DD = decltype(dim)::value;
+      append_copy_kernel<E, DD><<<grid, 256, 0, stream>>>(
+          static_cast<E*>(p->k_cache) + lo, static_cast<E*>(p->v_cache) + lo, static_cast<const E*>(k_new),
+          static_cast<const E*>(v_new), slots, T, d.num_kv_heads);
+    };
+    using D64 = std::integral_constant<int, 64>;
+    using D128 = std::integral_constant<int, 128>;
+    if (d.cache_dtype == KV_F32) {
+      if (D == 128) go(float{}, D128{});
+      else go(float{}, D64{});
+    } else {
+      if (D == 128) go(uint16_t{}, D128{});
+      else go(uint16_t{}, D64{});
+    }
   } else {
     const int64_t so = int64_t(layer) * d.num_blocks * d.num_kv_heads;
     auto* kc8 = static_cast<uint8_t*>(p->k_cache) + lo;

@@ -18,10 +18,32 @@ pytestmark = pytest.mark.gpu
 
 
 # ------------------------------------------------------------- append -------
+def _run_slots(rng, N, T):
+    """Slots shaped like request appends: runs of positions of requests whose
+    pages are random blocks (partial first and last pages, a request
+    continuing into the physically next block, single tokens), a few -1
+    entries.  No slot repeats."""
+    free = list(rng.permutation(N))
+    out = []
+    while len(out) < T and len(free) >= 3:
+        start = int(rng.integers(0, 16))
+        n = int(rng.integers(1, 48))
+        pages = [free.pop(), free.pop(), free.pop()]
+        if rng.random() < 0.3 and pages[0] + 1 < N and (pages[0] + 1) in free:
+            free.remove(pages[0] + 1)
+            pages[1] = pages[0] + 1        # slots run on across a block boundary
+        for pos in range(start, min(start + n, 48)):
+            out.append(pages[pos // 16] * 16 + pos % 16)
+    out = np.array(out[:T], np.int32)
+    out[rng.random(len(out)) < 0.03] = -1
+    return out
+
+
+@pytest.mark.parametrize("pattern", ["scattered", "runs"])
 @pytest.mark.parametrize("dtype,D", [("f32", 64), ("bf16", 128), ("bf16", 64)])
-def test_append_copy_bit_exact(gpu_lib, dtype, D):
-    log(f"append {dtype} D={D}")
-    H, N = 2, 12
+def test_append_copy_bit_exact(gpu_lib, dtype, D, pattern):
+    log(f"append {dtype} D={D} {pattern}")
+    H, N = 2, 12 if pattern == "scattered" else 60
     rng = np.random.default_rng(1)
     order = rng.permutation(N)
     pool = pk.Pool(2, N, H, D, dtype, DEV, initial_free_order=order)
@@ -36,9 +58,13 @@ def test_append_copy_bit_exact(gpu_lib, dtype, D):
     ref.V = bg_v.reshape(-1).view(ref.V.dtype).reshape(ref.V.shape).copy()
     for layer in range(2):
         for call in range(4):
-            T = int(rng.integers(1, 40))
-            slots = rng.choice(N * 16, T, replace=False).astype(np.int32)
-            slots[rng.random(T) < 0.1] = -1
+            if pattern == "scattered":
+                T = int(rng.integers(1, 40))
+                slots = rng.choice(N * 16, T, replace=False).astype(np.int32)
+                slots[rng.random(T) < 0.1] = -1
+            else:
+                slots = _run_slots(rng, N, int(rng.integers(1, 160)))
+                T = len(slots)
             check_slots(slots, N)
             if dtype == "f32":
                 k = synth.normal_f32(rng, (T, H, D))
