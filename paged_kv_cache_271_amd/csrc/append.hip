@@ -22,8 +22,106 @@ namespace {
 constexpr int kBS = kBlockSize;
 
 // ---------------------------------------------------------------- copy ----
-// One workgroup of 256 threads per (token t, kv-head g); only the first token
-// of a run works, for the whole run.  A run is a maximal sequence of tokens
+// f32 and bf16 pools copy bits.  Two launch shapes: bulk calls (prefills,
+// admitted prompts) take one workgroup per 16 tokens and move whole runs;
+// short calls take one workgroup per token, which keeps their latency to one
+// slot read and one data round trip.
+constexpr int kAppendRangeMin = 1024;  // tokens per call from which ranges are used
+
+// Bulk calls: one workgroup of 256 threads per (range of 16 tokens, kv-head g).  A run is
+// a maximal sequence of tokens of the call whose slots are consecutive within
+// one block (1 to 16 tokens).  The workgroup copies the K rows of its own
+// tokens (a row is contiguous in the tile: 16-byte pieces) and writes V for
+// the runs that start in its range, which may reach up to 15 tokens past it:
+// those tokens' V rows pass through LDS, and each thread writes one (run,
+// dimension) pair's entries into the dim-major tile at a time, a whole
+// 16-token row in 16-byte stores when the run fills the block.  The slots of tokens
+// t0 - 1 .. t0 + 31 are read in one round trip.
+constexpr int kAppendRange = 16;
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256) append_copy_range_kernel(T* __restrict__ kc, T* __restrict__ vc,
+                                                          const T* __restrict__ k_new,
+                                                          const T* __restrict__ v_new,
+                                                          const int32_t* __restrict__ slots, int n_tok,
+                                                          int H) {
+  constexpr int RB = D * int(sizeof(T));  // bytes of one token row
+  constexpr int PR = RB / 16;             // 16-byte pieces per row
+  constexpr int R = kAppendRange;
+  __shared__ int32_t s_slot[2 * R + 1];  // tokens t0 - 1 .. t0 + 2R - 1 (-1: none or beyond)
+  __shared__ int32_t s_len[R];           // length of the run starting at t0 + i (0: none)
+  __shared__ int32_t s_first[R + 1];     // range indices of the runs starting here; [R]: their count
+  __shared__ __attribute__((aligned(16))) T s_v[2 * R][D];
+  const int t0 = blockIdx.x * R;
+  const int g = blockIdx.y;
+  const int tid = threadIdx.x;
+  if (tid <= 2 * R) {
+    const int t = t0 - 1 + tid;
+    s_slot[tid] = t >= 0 && t < n_tok ? slots[t] : -1;
+  }
+  __syncthreads();
+  if (tid < R) {
+    const int32_t sl = s_slot[tid + 1], sp = s_slot[tid];
+    int len = 0;
+    if (sl >= 0 && !(sp >= 0 && sp + 1 == sl && sl % kBS != 0)) {
+      len = 1;  // then at most to the end of the block (index <= tid + 16)
+      while (len < kBS - sl % kBS && s_slot[tid + 1 + len] == sl + len) ++len;
+    }
+    s_len[tid] = len;
+  }
+  // K rows of this range's tokens
+  for (int p = tid; p < R * PR; p += 256) {
+    const int r = p / PR, c = p - r * PR;
+    const int32_t sl = s_slot[r + 1];
+    if (t0 + r < n_tok && sl >= 0) {
+      const int64_t tile = (int64_t(sl / kBS) * H + g) * kBS * D;  // elements
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(kc + tile) + (sl % kBS) * RB + 16 * c) =
+          *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(k_new) +
+                                          (int64_t(t0 + r) * H + g) * RB + 16 * c);
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int k = 0;
+    for (int i = 0; i < R; ++i)
+      if (s_len[i] > 0) s_first[k++] = i;
+    s_first[R] = k;
+  }
+  // V rows of the tokens up to the end of the last run starting here (every
+  // one of them exists: a run only holds tokens whose slot was read)
+  int rows = 0;
+#pragma unroll
+  for (int i = 0; i < R; ++i) rows = s_len[i] > 0 ? i + s_len[i] : rows;
+  for (int p = tid; p < rows * PR; p += 256) {
+    const int r = p / PR, c = p - r * PR;
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(&s_v[r][0]) + 16 * c) =
+        *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(v_new) +
+                                        (int64_t(t0 + r) * H + g) * RB + 16 * c);
+  }
+  __syncthreads();
+  // one (run, dimension) pair per thread and pass
+  for (int p = tid; p < s_first[R] * D; p += 256) {
+    const int i = s_first[p / D], d = p % D;
+    const int n = s_len[i];
+    const int32_t sl = s_slot[i + 1];
+    const int o0 = sl % kBS;
+    T* row = vc + (int64_t(sl / kBS) * H + g) * kBS * D + int64_t(d) * kBS;  // dimension d
+    if (n == kBS) {
+      alignas(16) T e[kBS];
+#pragma unroll
+      for (int r = 0; r < kBS; ++r) e[r] = s_v[i + r][d];
+#pragma unroll
+      for (int w = 0; w < kBS * int(sizeof(T)) / 16; ++w)
+        reinterpret_cast<uint4*>(row)[w] = reinterpret_cast<const uint4*>(e)[w];
+    } else {
+      for (int r = 0; r < n; ++r) row[o0 + r] = s_v[i + r][d];
+    }
+  }
+}
+
+// Calls of up to kAppendRangeMin tokens (a decode step's one token per
+// request): one workgroup of 256 threads per (token t, kv-head g); only the
+// first token of a run works, for the whole run.  A run is a maximal sequence of tokens
 // of the call whose slots are consecutive within one block (1 to 16 tokens).
 // The slots of tokens t - 1 .. t + 16 are read in one round trip by wave 0,
 // and a ballot gives the run's length.  K rows go over in 16-byte pieces
@@ -31,7 +129,7 @@ constexpr int kBS = kBlockSize;
 // thread writes its dimension's entries of the run into the dim-major tile,
 // a whole 16-token row in 16-byte stores when the run fills the block.
 template <typename T, int D>
-__global__ void __launch_bounds__(256) append_copy_kernel(T* __restrict__ kc, T* __restrict__ vc,
+__global__ void __launch_bounds__(256) append_copy_run_kernel(T* __restrict__ kc, T* __restrict__ vc,
                                                           const T* __restrict__ k_new,
                                                           const T* __restrict__ v_new,
                                                           const int32_t* __restrict__ slots, int n_tok,
@@ -251,9 +349,16 @@ int launch_append(const kv_pool* p, int32_t layer, const void* k_new, const void
     auto go = [&](auto elem, auto dim) {
       using E = decltype(elem);
       constexpr int DD = decltype(dim)::value;
-      append_copy_kernel<E, DD><<<grid, 256, 0, stream>>>(
-          static_cast<E*>(p->k_cache) + lo, static_cast<E*>(p->v_cache) + lo, static_cast<const E*>(k_new),
-          static_cast<const E*>(v_new), slots, T, d.num_kv_heads);
+      E* kcp = static_cast<E*>(p->k_cache) + lo;
+      E* vcp = static_cast<E*>(p->v_cache) + lo;
+      if (T > kAppendRangeMin) {
+        const dim3 ranges((T + kAppendRange - 1) / kAppendRange, d.num_kv_heads);
+        append_copy_range_kernel<E, DD><<<ranges, 256, 0, stream>>>(
+            kcp, vcp, static_cast<const E*>(k_new), static_cast<const E*>(v_new), slots, T, d.num_kv_heads);
+      } else {
+        append_copy_run_kernel<E, DD><<<grid, 256, 0, stream>>>(
+            kcp, vcp, static_cast<const E*>(k_new), static_cast<const E*>(v_new), slots, T, d.num_kv_heads);
+      }
     };
     using D64 = std::integral_constant<int, 64>;
     using D128 = std::integral_constant<int, 128>;

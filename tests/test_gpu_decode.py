@@ -39,11 +39,11 @@ def _run_slots(rng, N, T):
     return out
 
 
-@pytest.mark.parametrize("pattern", ["scattered", "runs"])
+@pytest.mark.parametrize("pattern", ["scattered", "runs", "bulk"])
 @pytest.mark.parametrize("dtype,D", [("f32", 64), ("bf16", 128), ("bf16", 64)])
 def test_append_copy_bit_exact(gpu_lib, dtype, D, pattern):
     log(f"append {dtype} D={D} {pattern}")
-    H, N = 2, 12 if pattern == "scattered" else 60
+    H, N = 2, {"scattered": 12, "runs": 60, "bulk": 600}[pattern]
     rng = np.random.default_rng(1)
     order = rng.permutation(N)
     pool = pk.Pool(2, N, H, D, dtype, DEV, initial_free_order=order)
@@ -62,9 +62,11 @@ def test_append_copy_bit_exact(gpu_lib, dtype, D, pattern):
                 T = int(rng.integers(1, 40))
                 slots = rng.choice(N * 16, T, replace=False).astype(np.int32)
                 slots[rng.random(T) < 0.1] = -1
-            else:
-                slots = _run_slots(rng, N, int(rng.integers(1, 160)))
+            else:   # bulk calls (over 1024 tokens) take the kernel's other launch shape
+                T = int(rng.integers(1, 160)) if pattern == "runs" else int(rng.integers(1100, 3000))
+                slots = _run_slots(rng, N, T)
                 T = len(slots)
+                assert pattern == "runs" or T > 1024
             check_slots(slots, N)
             if dtype == "f32":
                 k = synth.normal_f32(rng, (T, H, D))
