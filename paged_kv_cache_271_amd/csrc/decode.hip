@@ -16,9 +16,10 @@
 //
 // bf16 / fp8 caches: decode_stream_kernel splits the blocks of the whole
 // batch evenly over its waves (details at the kernel) and uses MFMA
-// (v_mfma_f32_16x16x32_bf16) for q.K^T and p.V; stream_reduce_kernel merges
-// the pieces.  fp8 codes are widened to bf16 exactly (every E4M3 value is a
-// bf16 value); the K scale multiplies the scores and the V scale multiplies p.
+// (v_mfma_f32_16x16x32_bf16) for q.K^T and p.V; stream_reduce_kernel (or
+// stream_reduce_rows_kernel, when rows have few pieces) merges the pieces.
+// fp8 codes are widened to bf16 exactly (every E4M3 value is a bf16 value);
+// the K scale multiplies the scores and the V scale multiplies p.
 // Padding columns of the MFMA (query heads beyond the group) carry zero
 // queries and are never stored.
 //
@@ -158,7 +159,7 @@ __device__ inline uint16_t to_out<uint16_t>(float x) { return uint16_t(f2bf_bits
 // range of blocks of one (b, gh).  A segment that covers all of its (b, gh)
 // is finished in place and written to `out`; the others (at most the first
 // and the last of a chunk) store their (m, l, acc) state in the workspace and
-// stream_reduce_kernel merges the pieces of each (b, gh) in chunk order.
+// a reduce kernel merges the pieces of each (b, gh) in chunk order.
 // By default the units are cut into one chunk per worker (or per unit when
 // there are fewer), sizes differing by at most one, so every wave gets the
 // same number of blocks
@@ -786,6 +787,105 @@ stream_reduce_kernel(uint16_t* __restrict__ out, const float* __restrict__ ws_ml
   }
 }
 
+// The same merge for batches whose rows have few pieces (the host's estimate
+// is at most kNarrowPieces per row): one wave per (request, query head),
+// four rows per workgroup, lane = (piece lane, dimension quad); each lane
+// merges its pieces in one pass with a running maximum, then the piece lanes
+// merge by shuffles.  A quarter of the workgroups and no LDS stage; with many
+// pieces per row its two (D = 128) piece lanes make long chains, where the
+// kernel above spreads them over eight.
+template <int D, bool WIN>
+__global__ void __launch_bounds__(256)
+stream_reduce_rows_kernel(uint16_t* __restrict__ out, const float* __restrict__ ws_ml,
+                     const float* __restrict__ ws_acc, const int32_t* __restrict__ ws_pref,
+                     const int32_t* __restrict__ ctx_lens, int B, int max_ctx, int h_q, int G,
+                     int n_hgroups, int H, int HS, int workers, int chunk_fixed, int sink, int window) {
+  constexpr int DQ = D / 4;
+  constexpr int PL = 64 / DQ;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= int64_t(B) * h_q) return;
+  const int b = int(row / h_q), h = int(row - int64_t(b) * h_q);
+  const int nb = ws_pref[b + 1] - ws_pref[b];
+  if (nb == 0) {
+    if (lane < D / 2) reinterpret_cast<uint32_t*>(out + row * D)[lane] = 0u;  // D / 2 dwords
+    return;
+  }
+  const int hge = H * n_hgroups;
+  const bool coop = (hge & 3) == 0;
+  const int hsets = coop ? hge >> 2 : hge;
+  const int streams = coop ? workers / 4 : workers;
+  const int64_t U = int64_t(hsets) * ws_pref[B];
+  const int g = h / G;
+  const int hg = (h - g * G) / 16;
+  const int hh = (h - g * G) % 16;
+  const int gh = g * n_hgroups + hg;
+  const int gs = coop ? gh >> 2 : gh;
+  const int wv = coop ? gh & 3 : 0;
+  const int64_t start = int64_t(hsets) * ws_pref[b] + int64_t(gs) * nb;
+  const StreamChunks ch(U, streams, chunk_fixed);
+  const int64_t c0 = ch.chunk_of(start);
+  const int64_t c1 = ch.chunk_of(start + nb - 1);
+  if (c0 == c1) return;  // finished inside one chunk by the decode kernel
+  const int K = int(c1 - c0 + 1);
+  const int first_role = start > ch.start(c0) ? 1 : 0;
+  auto slot = [&](int k) -> int64_t {
+    const int64_t cr = (c0 + k) * 2 + (k == 0 ? first_role : 0);
+    return (coop ? cr * 4 + wv : cr) * HS + hh;
+  };
+  const int pl = lane / DQ, dq = lane - pl * DQ;
+  float M = -INFINITY, L = 0.0f;
+  f32x4 A = {0.f, 0.f, 0.f, 0.f};
+  int k = pl;
+  for (; k + 3 * PL < K; k += 4 * PL) {
+    float m4[4], l4[4];
+    f32x4 a4[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t s = slot(k + u * PL);
+      m4[u] = ws_ml[s * 2];
+      l4[u] = ws_ml[s * 2 + 1];
+      a4[u] = *reinterpret_cast<const f32x4*>(ws_acc + s * D + 4 * dq);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float Mn = fmaxf(M, m4[u]);
+      const float eo = __builtin_amdgcn_exp2f(M - Mn), en = __builtin_amdgcn_exp2f(m4[u] - Mn);
+      L = L * eo + l4[u] * en;
+      A = A * eo + a4[u] * en;
+      M = Mn;
+    }
+  }
+  for (; k < K; k += PL) {
+    const int64_t s = slot(k);
+    const float mp = ws_ml[s * 2];
+    const float Mn = fmaxf(M, mp);
+    const float eo = __builtin_amdgcn_exp2f(M - Mn), en = __builtin_amdgcn_exp2f(mp - Mn);
+    L = L * eo + ws_ml[s * 2 + 1] * en;
+    A = A * eo + *reinterpret_cast<const f32x4*>(ws_acc + s * D + 4 * dq) * en;
+    M = Mn;
+  }
+  // merge the piece lanes of each dimension quad (a lane without pieces holds M = -inf)
+#pragma unroll
+  for (int o = DQ; o < 64; o <<= 1) {
+    const float Mo = __shfl_xor(M, o), Lo = __shfl_xor(L, o);
+    f32x4 Ao;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Ao[i] = __shfl_xor(A[i], o);
+    const float Mn = fmaxf(M, Mo);
+    const float e1 = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
+    const float e2 = Mo == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(Mo - Mn);
+    L = L * e1 + Lo * e2;
+    A = A * e1 + Ao * e2;
+    M = Mn;
+  }
+  if (pl == 0) {
+    const float inv = 1.0f / L;
+    const u32x2 pk = {pack_bf16(A[0] * inv, A[1] * inv), pack_bf16(A[2] * inv, A[3] * inv)};
+    *reinterpret_cast<u32x2*>(out + row * D + 4 * dq) = pk;
+  }
+}
+
 // ------------------------------------------------------------------------
 // fp32 partition kernel (VALU).  grid (num_part, H * n_hgroups, B), 256
 // threads; up to 16 query heads per workgroup; tokens in chunks of 256 with
@@ -960,6 +1060,8 @@ reduce_kernel(OutT* __restrict__ out, const float* __restrict__ ws_ml,
 // Waves of the balanced decode kernel: 256 compute units x 4 SIMDs x 3
 // resident waves, so one launch fills MI355X once.
 constexpr int kStreamWorkers = 256 * 4 * 3;
+// Rows with at most this many pieces (estimated) are merged one wave per row.
+constexpr int64_t kNarrowPieces = 16;
 
 template <int D>
 int launch_decode_d(const DecodeArgs& a, hipStream_t s) {
@@ -1024,14 +1126,29 @@ int launch_decode_d(const DecodeArgs& a, hipStream_t s) {
   }
   e = hipGetLastError();
   if (e != hipSuccess) return fail(KV_E_HIP, "decode launch: %s", hipGetErrorString(e));
-  if (win)
-    stream_reduce_kernel<D, true><<<dim3(a.h_q, a.B), 256, 0, s>>>(
-        out, a.ws_ml, a.ws_acc, a.ws_pref, a.ctx, a.B, a.max_ctx, a.h_q, G, nhg, H, a.hs, a.workers,
-        a.chunk, a.sink, a.window);
-  else
-    stream_reduce_kernel<D, false><<<dim3(a.h_q, a.B), 256, 0, s>>>(
-        out, a.ws_ml, a.ws_acc, a.ws_pref, a.ctx, a.B, a.max_ctx, a.h_q, G, nhg, H, a.hs, a.workers,
-        a.chunk, 0, 0);
+  // pieces per (request, set of kv-head groups): on average the chunks of
+  // the balanced split over the batch's sets, at most the partitions of the
+  // longest request with forced chunks
+  const int64_t hge = int64_t(H) * nhg;
+  const int64_t sets = hge % 4 == 0 ? hge / 4 : hge;
+  const int64_t streams = hge % 4 == 0 ? a.workers / 4 : a.workers;
+  const int64_t pieces = a.chunk > 0 ? (int64_t(a.max_ctx) + kBS - 1) / kBS / a.chunk + 2
+                                     : streams / std::max<int64_t>(1, sets * a.B) + 1;
+  const dim3 rows_grid(unsigned((int64_t(a.B) * a.h_q + 3) / 4));
+  auto reduce = [&](auto window) {
+    constexpr bool WN = decltype(window)::value;
+    const int sk = WN ? a.sink : 0, wn = WN ? a.window : 0;
+    if (pieces <= kNarrowPieces)
+      stream_reduce_rows_kernel<D, WN><<<rows_grid, 256, 0, s>>>(out, a.ws_ml, a.ws_acc, a.ws_pref, a.ctx, a.B,
+                                                                  a.max_ctx, a.h_q, G, nhg, H, a.hs, a.workers,
+                                                                  a.chunk, sk, wn);
+    else
+      stream_reduce_kernel<D, WN><<<dim3(a.h_q, a.B), 256, 0, s>>>(out, a.ws_ml, a.ws_acc, a.ws_pref, a.ctx, a.B,
+                                                                    a.max_ctx, a.h_q, G, nhg, H, a.hs, a.workers,
+                                                                    a.chunk, sk, wn);
+  };
+  if (win) reduce(std::true_type{});
+  else reduce(std::false_type{});
   e = hipGetLastError();
   if (e != hipSuccess) return fail(KV_E_HIP, "decode reduce launch: %s", hipGetErrorString(e));
   return ok();
