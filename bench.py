@@ -52,9 +52,9 @@ DEFAULT_SEED = {"llama3_8b": 2, "llama3_70b_long": 3, "fp8": 5, "int8": 5, "pref
 # calibration there (fetch x2, write x1).  They hold for the kernel source they
 # were taken on, identified by its SHA-256; any other source reports null.
 TRAFFIC_SOURCE = "paged_kv_cache_271_amd/csrc/decode.hip"
-TRAFFIC_SHA256 = "97e4da76de18ac7d8c254a29b690939b29be450e6a5b77ef45f15bea1548a426"
-TRAFFIC_BYTES = {"llama3_8b": 594_975_095, "fp8": 1_235_695_533, "llama3_70b_long": 1_360_392_307, "int8": 1_235_975_238,
-                 "llama3_8b_window": 1_096_168_225}
+TRAFFIC_SHA256 = "a466439f420226d74689370404d9010e8529e6405858d23f27510bd2a7669e62"
+TRAFFIC_BYTES = {"llama3_8b": 594_910_649, "fp8": 1_235_696_206, "llama3_70b_long": 1_360_124_738, "int8": 1_236_004_332,
+                 "llama3_8b_window": 1_096_349_442}
 # The same per launch of prefill_kernel and of block_copy_kernel, from
 # profiles/prefill_llama3_8b_counters.md and
 # profiles/block_copy_cow_fork_hbm_counters.md: (source, its SHA-256, bytes).
