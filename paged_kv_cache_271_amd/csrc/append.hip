@@ -255,9 +255,11 @@ __device__ inline float block_max(float v, float* red) {
 // fp8 E4M3 and int8 caches share the kernel; only the codec differs.
 // One workgroup per (token t, kv-head g); only the first token of a run (the
 // consecutive tokens of this call landing in one block) does the work, for
-// the whole run.  The run's K tile ([16][D] codes) and V tile ([D][16]) are
-// staged in LDS with one 16-byte load per thread, re-encoded and written
-// there, and the changed bytes go back with 16-byte stores.
+// the whole run.  Wave 0 reads the slots of tokens t - 1 .. t + 62 in one
+// round trip and a ballot finds the run; the first token's inputs are loaded
+// before its slot is known.  The run's K tile ([16][D] codes) and V tile
+// ([D][16]) are staged in LDS with one 16-byte load per thread, re-encoded and
+// written there, and the changed bytes go back with 16-byte stores.
 // blockDim.x = D (64 or 128); thread d owns dimension d.
 template <int D, bool INT8>
 __global__ void __launch_bounds__(D) append_q8_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
@@ -267,20 +269,43 @@ __global__ void __launch_bounds__(D) append_q8_kernel(uint8_t* __restrict__ kc, 
                                                        const int32_t* __restrict__ slots, int T, int H) {
   constexpr int TILE = kBS * D;        // bytes of one tile
   constexpr int CHUNKS = TILE / 16;    // 16-byte pieces of a tile (= D)
+  constexpr int kWin = 63;              // run tokens whose slots wave 0 reads at once
   __shared__ __attribute__((aligned(16))) uint8_t s_tile[2][TILE];  // [0] K, [1] V
   __shared__ float red[2];
+  __shared__ int32_t s_run[2];          // last token of the run (-1: not a run start), first slot
+  __shared__ int32_t s_off[kWin];       // offsets of the run's tokens t .. t + kWin - 1
   const int t = blockIdx.x;
   const int g = blockIdx.y;
   const int d = threadIdx.x;
-  const int32_t slot = slots[t];
-  if (slot < 0) return;
-  const int32_t blk = slot / kBS;
-  if (t > 0) {
-    const int32_t prev = slots[t - 1];
-    if (prev >= 0 && prev / kBS == blk) return;  // not the first token of its run
+  // the first token's inputs need no slot: in flight from the start
+  const float x0[2] = {bf16_bits_to_float(k_new[(int64_t(t) * H + g) * D + d]),
+                       bf16_bits_to_float(v_new[(int64_t(t) * H + g) * D + d])};
+  if (d < 64) {
+    // wave 0: slots of tokens t - 1 .. t + 62 in one round trip; the run is
+    // the leading lanes from 1 whose token lands in the first token's block
+    const int i = d - 1;
+    int32_t sl = -1;
+    if (t + i >= 0 && t + i < T) sl = slots[t + i];
+    const int32_t s0 = __shfl(sl, 1), sp = __shfl(sl, 0);
+    const bool start = s0 >= 0 && !(sp >= 0 && sp / kBS == s0 / kBS);
+    const bool ok = d >= 1 && s0 >= 0 && sl >= 0 && sl / kBS == s0 / kBS;
+    const uint64_t broken = ~(uint64_t(__ballot(ok)) >> 1);  // bit 63 always set
+    const int n = start ? __builtin_ctzll(broken) : 0;        // 0 .. kWin
+    if (d >= 1 && i < n) s_off[i] = sl % kBS;
+    if (d == 0) {
+      s_run[0] = start ? t + n - 1 : -1;
+      s_run[1] = s0;
+    }
   }
-  int u = t;
-  while (u + 1 < T && slots[u + 1] >= 0 && slots[u + 1] / kBS == blk) ++u;
+  __syncthreads();
+  int u = s_run[0];
+  if (u < 0) return;
+  const int32_t slot = s_run[1];
+  const int32_t blk = slot / kBS;
+  // a run past the window (only with repeated slots) continues serially
+  if (u == t + kWin - 1)
+    while (u + 1 < T && slots[u + 1] >= 0 && slots[u + 1] / kBS == blk) ++u;
+  auto off_of = [&](int r) { return r - t < kWin ? s_off[r - t] : slots[r] % kBS; };
   const int first_off = slot % kBS;
   const int64_t tile = (int64_t(blk) * H + g) * TILE;
   const int64_t sidx = int64_t(blk) * H + g;
@@ -301,15 +326,15 @@ __global__ void __launch_bounds__(D) append_q8_kernel(uint8_t* __restrict__ kc, 
   for (int which = 0; which < 2; ++which) {
     const uint16_t* src = which == 0 ? k_new : v_new;
     const float s0 = which == 0 ? sk0 : sv0;
-    float amax = 0.0f;
-    for (int r = t; r <= u; ++r)
+    float amax = fabsf(x0[which]);
+    for (int r = t + 1; r <= u; ++r)
       amax = fmaxf(amax, fabsf(bf16_bits_to_float(src[(int64_t(r) * H + g) * D + d])));
     amax = block_max(amax, red);
     const float s1 = fmaxf(s0, amax / Codec8<INT8>::kMax);
     reenc[which] = s1 != s0 && first_off > 0;
     uint8_t* st = s_tile[which];
     if (s1 == 0.0f) {
-      for (int r = t; r <= u; ++r) st[pos(which, slots[r] % kBS)] = 0;
+      for (int r = t; r <= u; ++r) st[pos(which, off_of(r))] = 0;
     } else {
       const float inv = 1.0f / s1;
       if (reenc[which])
@@ -318,8 +343,8 @@ __global__ void __launch_bounds__(D) append_q8_kernel(uint8_t* __restrict__ kc, 
           st[pos(which, o)] = uint8_t(Codec8<INT8>::encode(x * inv));
         }
       for (int r = t; r <= u; ++r) {
-        const float x = bf16_bits_to_float(src[(int64_t(r) * H + g) * D + d]);
-        st[pos(which, slots[r] % kBS)] = uint8_t(Codec8<INT8>::encode(x * inv));
+        const float x = r == t ? x0[which] : bf16_bits_to_float(src[(int64_t(r) * H + g) * D + d]);
+        st[pos(which, off_of(r))] = uint8_t(Codec8<INT8>::encode(x * inv));
       }
     }
     if (d == 0) (which == 0 ? ks : vs)[sidx] = s1;
@@ -328,7 +353,7 @@ __global__ void __launch_bounds__(D) append_q8_kernel(uint8_t* __restrict__ kc, 
 
   // write back: K rows of the run (and the re-encoded rows below it); V is
   // dim-major, so every 16-byte row changes
-  const int last_off = slots[u] % kBS;
+  const int last_off = off_of(u);
   for (int c = d; c < CHUNKS; c += D) {
     const int o = (16 * c) / D;  // token row of this K chunk
     if ((o >= first_off && o <= last_off) || (o < first_off && reenc[0]))
