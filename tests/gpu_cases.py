@@ -253,12 +253,17 @@ class Case:
             return self.q.astype(np.float64)
         return oracle.bf16_bits_to_f64(self.q)
 
-    def decode(self, partition_tokens=0, max_ctx=None, scale=None):
+    def decode(self, partition_tokens=0, max_ctx=None, scale=None, nan_out=False):
+        """nan_out: the output buffer starts as NaN, so every row the result
+        shows was written by the library."""
         max_ctx = max(self.lens_list) if max_ctx is None else max_ctx
         check_indices(self.table, self.lens, self.N, max_ctx)
         scale = scale or 1.0 / math.sqrt(self.D)
         q = self.dq if self.device_inputs else to_dev_bits(self.q, self.dtype)
-        out = self.pool.decode(0, q, self.d_table, self.d_lens, max_ctx, scale, partition_tokens)
+        out = None
+        if nan_out:
+            out = torch.full(tuple(q.shape), float("nan"), dtype=q.dtype, device=q.device)
+        out = self.pool.decode(0, q, self.d_table, self.d_lens, max_ctx, scale, partition_tokens, out=out)
         torch.cuda.synchronize()
         o = from_dev_bits(out)
         return o.astype(np.float64) if self.dtype == "f32" else oracle.bf16_bits_to_f64(o)

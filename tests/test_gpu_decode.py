@@ -167,17 +167,18 @@ def test_identical_keys_give_mean_of_values(gpu_lib, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8", "int8"])
-def test_one_token_and_empty(gpu_lib, dtype):
-    c = Case(dtype, 2, 128, 4, [1, 0, 1, 0], num_blocks=4, seed=5)
-    got = c.decode()
+@pytest.mark.parametrize("D", [128, 64])
+def test_one_token_and_empty(gpu_lib, dtype, D):
+    c = Case(dtype, 2, D, 4, [1, 0, 1, 0], num_blocks=4, seed=5)
+    got = c.decode(nan_out=True)     # empty requests' rows are written as zeros
     assert not np.any(got[1]) and not np.any(got[3])
     for b in (0, 2):
         _, V = c.seq_f64(b)
         want = np.repeat(V[0], 2, axis=0)
         assert_close(got[b], want, c.tol_key, f"ctx 1, request {b}")
     # all requests empty
-    e = Case(dtype, 2, 128, 4, [0, 0], num_blocks=2, seed=6, max_blocks=1)
-    assert not np.any(e.decode(max_ctx=0))
+    e = Case(dtype, 2, D, 4, [0, 0], num_blocks=2, seed=6, max_blocks=1)
+    assert not np.any(e.decode(max_ctx=0, nan_out=True))
 
 
 @pytest.mark.parametrize("H,h_q", [(1, 32), (4, 4), (2, 40), (1, 1)])
