@@ -604,7 +604,12 @@ def main():
     config = dict(r["config"])
     config["us_per_step"] = round(ms_per_step * 1e3, 2)
     if unit == "GB/s":
-        config["hbm_fraction"] = round(value / HBM_PEAK_GBS, 4)
+        # logical bytes count the shared prefix once per request that reads it
+        # (mostly served from cache): the HBM fraction uses the unique bytes
+        unique = config.get("unique_kv_GBs")
+        config["hbm_fraction"] = round((unique if unique is not None else value) / HBM_PEAK_GBS, 4)
+        if unique is not None:
+            config["hbm_fraction_of"] = "unique K/V bytes"
         config["kv_bytes_per_step"] = int(mean_kv)
     res = {
         "metric": r.get("metric", METRIC),
