@@ -28,23 +28,21 @@ constexpr int kBS = kBlockSize;
 // slot read and one data round trip.
 constexpr int kAppendRangeMin = 1024;  // tokens per call from which ranges are used
 
-// Bulk calls: one workgroup of 256 threads per (range of 16 tokens, kv-head g).  A run is
-// a maximal sequence of tokens of the call whose slots are consecutive within
-// one block (1 to 16 tokens).  The workgroup copies the K rows of its own
-// tokens (a row is contiguous in the tile: 16-byte pieces) and writes V for
-// the runs that start in its range, which may reach up to 15 tokens past it:
-// those tokens' V rows pass through LDS, and each thread writes one (run,
-// dimension) pair's entries into the dim-major tile at a time, a whole
-// 16-token row in 16-byte stores when the run fills the block.  The slots of tokens
-// t0 - 1 .. t0 + 31 are read in one round trip.
+// Bulk calls: one workgroup of 256 threads per (range of 16 tokens, kv-head
+// g).  A run is a maximal sequence of tokens of the call whose slots are
+// consecutive within one block (1 to 16 tokens).  The workgroup copies the K
+// rows of its own tokens (a row is contiguous in the tile: 16-byte pieces)
+// and writes V for the runs that start in its range, which may reach up to 15
+// tokens past it: those tokens' V rows pass through LDS, and each thread
+// writes one (run, dimension) pair's entries into the dim-major tile at a
+// time, a whole 16-token row in 16-byte stores when the run fills the block.
+// The slots of tokens t0 - 1 .. t0 + 31 are read in one round trip.
 constexpr int kAppendRange = 16;
 
 template <typename T, int D>
-__global__ void __launch_bounds__(256) append_copy_range_kernel(T* __restrict__ kc, T* __restrict__ vc,
-                                                          const T* __restrict__ k_new,
-                                                          const T* __restrict__ v_new,
-                                                          const int32_t* __restrict__ slots, int n_tok,
-                                                          int H) {
+__global__ void __launch_bounds__(256)
+append_copy_range_kernel(T* __restrict__ kc, T* __restrict__ vc, const T* __restrict__ k_new,
+                         const T* __restrict__ v_new, const int32_t* __restrict__ slots, int n_tok, int H) {
   constexpr int RB = D * int(sizeof(T));  // bytes of one token row
   constexpr int PR = RB / 16;             // 16-byte pieces per row
   constexpr int R = kAppendRange;
@@ -129,11 +127,9 @@ __global__ void __launch_bounds__(256) append_copy_range_kernel(T* __restrict__ 
 // thread writes its dimension's entries of the run into the dim-major tile,
 // a whole 16-token row in 16-byte stores when the run fills the block.
 template <typename T, int D>
-__global__ void __launch_bounds__(256) append_copy_run_kernel(T* __restrict__ kc, T* __restrict__ vc,
-                                                          const T* __restrict__ k_new,
-                                                          const T* __restrict__ v_new,
-                                                          const int32_t* __restrict__ slots, int n_tok,
-                                                          int H) {
+__global__ void __launch_bounds__(256)
+append_copy_run_kernel(T* __restrict__ kc, T* __restrict__ vc, const T* __restrict__ k_new,
+                       const T* __restrict__ v_new, const int32_t* __restrict__ slots, int n_tok, int H) {
   constexpr int RB = D * int(sizeof(T));  // bytes of one token row
   constexpr int PR = RB / 16;             // 16-byte pieces per row
   __shared__ __attribute__((aligned(16))) T s_v[kBS][D];
