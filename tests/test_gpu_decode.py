@@ -40,7 +40,7 @@ def _run_slots(rng, N, T):
 
 
 @pytest.mark.parametrize("pattern", ["scattered", "runs", "bulk"])
-@pytest.mark.parametrize("dtype,D", [("f32", 64), ("bf16", 128), ("bf16", 64)])
+@pytest.mark.parametrize("dtype,D", [("f32", 64), ("f32", 128), ("bf16", 128), ("bf16", 64)])
 def test_append_copy_bit_exact(gpu_lib, dtype, D, pattern):
     log(f"append {dtype} D={D} {pattern}")
     H, N = 2, {"scattered": 12, "runs": 60, "bulk": 600}[pattern]
