@@ -321,7 +321,7 @@ def decode_workload(args, torch, synth, pk, dev, spec=None, layers=0):
                 config=config, cpu=cpu, traffic=measured_traffic(name, args.two_calls), dtype={"fp8": "fp8-e4m3 K/V, bf16 q", "int8": "int8 K/V, bf16 q"}.get(dtype, "bf16"),
                 kernel=("paged_attention_decode_window" if window else
                         "paged_attention_decode" if two_calls else "paged_attention_decode_append")
-                + " call (decode_stream_kernel + stream_reduce_kernel)")
+                + " call (decode_stream_kernel + piece merge)")
 
 
 SWEEP_CTX = (512, 1024, 2048, 4096, 8192, 16384)
@@ -368,7 +368,7 @@ def ctx_sweep_workload(args, torch, synth, pk, dev):
                 dtype="bf16", value=rate, metric="paged decode call: streaming rate of the affine fit "
                 "over context length (GB/s), Llama-3-8B shape",
                 kernel="paged_attention_decode_append call at the longest context (decode_stream_kernel + "
-                       "stream_reduce_kernel)")
+                       "piece merge)")
 
 
 def churn_workload(args, torch, synth, pk, dev):
