@@ -461,11 +461,14 @@ def cow_fork_workload(args, torch, synth, pk, dev):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     dec_ms = np.array([e[0].elapsed_ms(e[1]) for e in events if e is not None])
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cow_cpu_baseline(args, rng_seed=args.seed, B=B, L=L, H=H, D=D, N=N)
     config = {"workload": "cow_fork_page_copy", "forks_per_step": B, "layers": L, "h_kv": H, "head_dim": D,
               "cache_dtype": "bf16", "page_bytes_per_layer_kv": 2 * page_bytes,
               "bytes_moved_per_step": moved}
     return dict(wall=wall, kv_total=float(total), dec_ms=dec_ms, dec_kv=np.full(len(dec_ms), float(moved)),
-                config=config, cpu=None, traffic=measured_traffic("cow_fork"),
+                config=config, cpu=cpu, traffic=measured_traffic("cow_fork"),
                 traffic_note="HBM bytes read + written per block_copy_kernel launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, "
                              "copy-calibrated); null if the kernel source changed", dtype="bf16",
                 kernel="kv_block_copy call (block_copy_kernel), bytes read + written",
@@ -747,6 +750,49 @@ def gather_probe(pool, table, lens, L, H, D, elem, torch, pk, dev, launches=64, 
     nbytes = int(offs.size) * 2 * 4 * tile
     log(f"gather probe launches: median {us:.1f} us, min {t_us.min():.1f}, max {t_us.max():.1f} over {len(t_us)}")
     return {"us": us, "bytes": nbytes, "gbs": nbytes / us / 1e3}
+
+
+def cow_cpu_baseline(args, rng_seed, B, L, H, D, N):
+    """The oracle's fork step on the same shape: the oracle allocator (same
+    seeded free order) gives 256 parents one partly filled page each, every
+    child retains its parent's page and reserves one token through the
+    oracle's copy-on-write reservation, and the oracle pool copies the 256
+    pages in every layer (K and V, bf16).  The copies are timed: 16 tasks of
+    16 pages on a thread pool as wide as the process's cores (at most 16),
+    repeated for about `cpu_seconds`.  Value: bytes read + written per second,
+    as the workload's."""
+    import oracle
+    from oracle.prefix_cache import reserve_cow
+    import synth
+    rng = synth.streams(rng_seed)
+    order = synth.permutation(rng["free_order"], N)
+    alloc = oracle.RefAllocator(N, order)
+    ptable, plen = [[] for _ in range(B)], [0] * B
+    reserve_cow(alloc, ptable, plen, rng["contexts"].integers(1, 16, B).astype(np.int32))
+    ctable, clen = [list(r) for r in ptable], list(plen)
+    for r in ctable:
+        for blk in r:
+            alloc.retain(blk)
+    _, pairs = reserve_cow(alloc, ctable, clen, [1] * B)
+    assert len(pairs) == B
+    pool = oracle.RefPool(L, N, H, D, 16, "bf16")
+    # fill the pool so that every page is real memory (untouched zero pages
+    # would make the reads nearly free)
+    pool.K.fill(0x3F80)
+    pool.V.fill(0x3F80)
+    chunks = [pairs[i:i + 16] for i in range(0, len(pairs), 16)]
+    tasks = [lambda c=c: pool.copy_pages([s_ for s_, _ in c], [d_ for _, d_ in c]) for c in chunks]
+    reps, dt, workers = _time_tasks(tasks, args.cpu_seconds)
+    moved = 2 * B * L * 2 * H * 16 * D * 2
+    return {
+        "value": round(moved * reps / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": workers,
+        "kind": "oracle",
+        "sample": f"oracle page copies of one fork step ({B} pages x {L} layers, K and V, bf16, "
+                  f"{moved / 1e9:.2f} GB read + written), pairs from the oracle's copy-on-write "
+                  f"reservation; {reps} repetitions in {dt:.1f} s, 16 pages per task on {workers} threads",
+    }
 
 
 def _time_tasks(tasks, seconds):

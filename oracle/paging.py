@@ -185,6 +185,24 @@ class RefPool:
                 self.Vs[layer, blk, g] = s1
             t = u + 1
 
+    # -- copy-on-write -------------------------------------------------------
+    def copy_pages(self, src, dst):
+        """Page dst[i] receives a copy of page src[i], in every layer, K and
+        V (and both scales for 8-bit pools).  This is the private copy a
+        request takes before writing into a page it shares ("KV Cache"
+        glossary, PagedAttention entry: blocks shared by parallel samples or
+        beams are copied when one of them writes).  Pairs with an id outside
+        the pool, or src == dst, are skipped."""
+        for s_, d_ in zip(src, dst):
+            s_, d_ = int(s_), int(d_)
+            if not (0 <= s_ < self.N and 0 <= d_ < self.N) or s_ == d_:
+                continue
+            self.K[:, d_] = self.K[:, s_]
+            self.V[:, d_] = self.V[:, s_]
+            if self.dtype in ("fp8", "int8"):
+                self.Ks[:, d_] = self.Ks[:, s_]
+                self.Vs[:, d_] = self.Vs[:, s_]
+
     # -- read path -----------------------------------------------------------
     def gather_raw(self, layer, table_row, n):
         """Raw stored K, V of the first n logical positions, [n, H, D]."""

@@ -233,3 +233,33 @@ def test_random_ops_keep_references_consistent(seed, n_ops):
             assert not set(freed) & mapped
         total = sum(alloc.refcount(b) for b in range(60))
         assert total == sum(len(r) for r in live) + cache.num_entries()
+
+
+def test_copy_pages_duplicates_and_touches_nothing_else():
+    """The oracle's page copy: each destination page ends up byte-equal to
+    its source in every layer (K, V and the 8-bit scales); every other page
+    is unchanged; out-of-range and self pairs are skipped; a request read
+    through the copy sees exactly what it saw through the shared page."""
+    rng = np.random.default_rng(11)
+    for dtype in ("bf16", "fp8"):
+        L, N, H, D = 2, 9, 2, 64
+        pool = oracle.RefPool(L, N, H, D, 16, dtype)
+        pool.K = rng.integers(0, 255, pool.K.shape).astype(pool.K.dtype)
+        pool.V = rng.integers(0, 255, pool.V.shape).astype(pool.V.dtype)
+        if dtype == "fp8":
+            pool.Ks = rng.random(pool.Ks.shape).astype(np.float32) + 0.5
+            pool.Vs = rng.random(pool.Vs.shape).astype(np.float32) + 0.5
+        before = pool.K.copy(), pool.V.copy()
+        src, dst = [3, 0, 42, 5], [7, 2, 1, 5]        # 42: out of range; 5 -> 5: itself
+        table_shared = np.array([4, 3], np.int32)     # a request whose second page is 3
+        k0, v0 = pool.gather_raw(1, table_shared, 30)
+        pool.copy_pages(src, dst)
+        for s_, d_ in ((3, 7), (0, 2)):
+            assert np.array_equal(pool.K[:, d_], pool.K[:, s_]) and np.array_equal(pool.V[:, d_], pool.V[:, s_])
+            if dtype == "fp8":
+                assert np.array_equal(pool.Ks[:, d_], pool.Ks[:, s_])
+        untouched = [b for b in range(N) if b not in (7, 2)]
+        assert np.array_equal(pool.K[:, untouched], before[0][:, untouched])
+        assert np.array_equal(pool.V[:, untouched], before[1][:, untouched])
+        k1, v1 = pool.gather_raw(1, np.array([4, 7], np.int32), 30)   # the same request on its copy
+        assert np.array_equal(k0, k1) and np.array_equal(v0, v1)
