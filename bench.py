@@ -68,7 +68,7 @@ TRAFFIC_OTHER = {
 
 def measured_traffic(workload, two_calls_asked=False):
     import hashlib
-    if two_calls_asked and workload in ("llama3_8b", "llama3_70b_long"):
+    if two_calls_asked and workload in ("llama3_8b", "llama3_70b_long", "llama3_8b_window"):
         return None  # their counters were taken on the fused kernel
     source, sha, table = TRAFFIC_SOURCE, TRAFFIC_SHA256, TRAFFIC_BYTES
     if workload in TRAFFIC_OTHER:
@@ -256,9 +256,9 @@ def decode_workload(args, torch, synth, pk, dev, spec=None, layers=0):
         state["kv"] = int(read_tokens(lens).sum()) * H * D * elem * 2
 
     # fp8 and int8 pools have no fused kernel (the append re-quantises whole
-    # tiles), nor has the windowed decode, so their step is always the two
-    # calls, with the decode alone between events
-    two_calls = args.two_calls or dtype in ("fp8", "int8") or bool(window)
+    # tiles), so their step is always the two calls, with the decode alone
+    # between events
+    two_calls = args.two_calls or dtype in ("fp8", "int8")
 
     def step(i, ev=None):
         s, r = divmod(i, L)
@@ -268,9 +268,13 @@ def decode_workload(args, torch, synth, pk, dev, spec=None, layers=0):
             pool.append(r, k_new[s, r], v_new[s, r], d_slots)
         if ev is not None:
             ev[0].record(stream)
-        if window:
+        if window and two_calls:
             pool.decode_window(r, q_all[s, r], d_table, d_lens, state["max_ctx"], scale, sink, window,
                                args.partition, out=out, workspace=ws)
+        elif window:
+            pool.decode_window_append(r, q_all[s, r], k_new[s, r], v_new[s, r], d_slots, d_table, d_lens,
+                                      state["max_ctx"], scale, sink, window, args.partition, out=out,
+                                      workspace=ws)
         elif two_calls:
             pool.decode(r, q_all[s, r], d_table, d_lens, state["max_ctx"], scale, args.partition,
                         out=out, workspace=ws)
@@ -315,13 +319,14 @@ def decode_workload(args, torch, synth, pk, dev, spec=None, layers=0):
         "contexts": (list(w["contexts"]) if "contexts" in w else {"uniform": list(w["ctx_range"])}),
         "layers_in_pool": L, "partition_tokens": args.partition,
         **({"sink_tokens": sink, "window_tokens": window} if window else {}),
-        "step": "kv_append + paged_attention_decode" if two_calls else "paged_attention_decode_append",
+        "step": ("kv_append + " if two_calls else "") + ("paged_attention_decode_window" if window else
+                                                         "paged_attention_decode")
+                + ("" if two_calls else "_append"),
     }
     return dict(wall=wall, kv_total=float(sum(per_step_kv)), dec_ms=dec_ms, dec_kv=dec_kv, probe=probe,
                 config=config, cpu=cpu, traffic=measured_traffic(name, args.two_calls), dtype={"fp8": "fp8-e4m3 K/V, bf16 q", "int8": "int8 K/V, bf16 q"}.get(dtype, "bf16"),
-                kernel=("paged_attention_decode_window" if window else
-                        "paged_attention_decode" if two_calls else "paged_attention_decode_append")
-                + " call (decode_stream_kernel + piece merge)")
+                kernel=("paged_attention_decode_window" if window else "paged_attention_decode")
+                + ("" if two_calls else "_append") + " call (decode_stream_kernel + piece merge)")
 
 
 SWEEP_CTX = (512, 1024, 2048, 4096, 8192, 16384)

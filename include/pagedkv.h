@@ -367,6 +367,27 @@ int paged_attention_decode_window(kv_pool* pool, int32_t layer, void* out, const
                                   int32_t partition_tokens, void* workspace, int64_t workspace_bytes,
                                   void* hip_stream);
 
+/* Device: one windowed decode step with the step's append: the same result as
+ *   kv_append(pool, layer, k_new, v_new, slot_mapping, B, stream);
+ *   paged_attention_decode_window(pool, layer, out, q, ...);
+ * (askaiml §1: the new token's K and V join the cache, then attention reads
+ * it; §8: through the window and the sinks).  k_new, v_new and slot_mapping
+ * are those of paged_attention_decode_append: slot_mapping[b] is the slot of
+ * position context_lens[b] - 1, or -1 when request b appends nothing.  bf16
+ * pools run one kernel, which takes the last position from k_new / v_new
+ * while the same launch stores it (outputs agree with the two calls to the
+ * bf16 rounding of the weights); fp8 and int8 pools launch the append kernel
+ * and then the windowed decode.  The other arguments, the workspace and the
+ * errors are those of paged_attention_decode_window, plus KV_E_INVALID for a
+ * NULL k_new, v_new or slot_mapping. */
+int paged_attention_decode_window_append(kv_pool* pool, int32_t layer, void* out, const void* q,
+                                         int32_t q_dtype, const void* k_new, const void* v_new,
+                                         const int32_t* slot_mapping, const int32_t* block_tables,
+                                         int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t B,
+                                         int32_t h_q, int32_t max_ctx, float scale, int32_t sink_tokens,
+                                         int32_t window_tokens, int32_t partition_tokens, void* workspace,
+                                         int64_t workspace_bytes, void* hip_stream);
+
 /* Host: give back the pages no later windowed decode of these requests reads.
  * The window only moves forward, so logical page j of a request of lens[b]
  * tokens is dead when 16 j >= sink_tokens and 16 (j + 1) <= lens[b] -

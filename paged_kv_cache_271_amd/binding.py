@@ -65,6 +65,9 @@ SIGNATURES = {
     "paged_attention_decode_window": (ctypes.c_int, [_P, _I32, _P, _P, _I32, _P, _I32, _P, _I32, _I32,
                                                      _I32, ctypes.c_float, _I32, _I32, _I32, _P, _I64,
                                                      _P]),
+    "paged_attention_decode_window_append": (ctypes.c_int, [_P, _I32, _P, _P, _I32, _P, _P, _P, _P, _I32,
+                                                            _P, _I32, _I32, _I32, ctypes.c_float, _I32, _I32,
+                                                            _I32, _P, _I64, _P]),
     "kv_window_release": (ctypes.c_int, [_P, _I32, _PI32, _I32, _PI32, _I32, _I32, _PI32]),
     "paged_attention_prefill": (ctypes.c_int, [_P, _I32, _P, _P, _I32, _P, _I32, _P, _P, _I32, _I32, _I32,
                                                _I32, ctypes.c_float, _P]),
@@ -426,6 +429,37 @@ def paged_attention_decode_window(h, desc, layer, out, q, block_tables, context_
                                               _stream_ptr(stream)))
 
 
+def paged_attention_decode_window_append(h, desc, layer, out, q, k_new, v_new, slot_mapping, block_tables,
+                                         context_lens, max_ctx, scale, sink_tokens, window_tokens,
+                                         partition_tokens=0, workspace=None, stream=None):
+    """paged_attention_decode_window with the step's append (arguments as for
+    paged_attention_decode_append)."""
+    import torch
+    if q.dim() != 3 or q.shape[2] != desc.head_dim:
+        raise ValueError("q must be [B, h_q, head_dim]")
+    B, h_q, _ = q.shape
+    want = torch.float32 if desc.cache_dtype == KV_F32 else torch.bfloat16
+    qp = _dev_ptr(q, "q", want)
+    op = _dev_ptr(out, "out", want, q.numel())
+    n = B * desc.num_kv_heads * desc.head_dim
+    kp = _dev_ptr(k_new, "k_new", want, n)
+    vp = _dev_ptr(v_new, "v_new", want, n)
+    sp = _dev_ptr(slot_mapping, "slot_mapping", torch.int32, B)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B, max_blocks]")
+    tp = _dev_ptr(block_tables, "block_tables", torch.int32)
+    cp = _dev_ptr(context_lens, "context_lens", torch.int32, B)
+    wp, wb = None, 0
+    if workspace is not None:
+        wp = _dev_ptr(workspace, "workspace")
+        wb = workspace.numel() * workspace.element_size()
+    qd = KV_F32 if want == torch.float32 else KV_BF16
+    _check(_lib.paged_attention_decode_window_append(h, int(layer), op, qp, qd, kp, vp, sp, tp,
+                                                     block_tables.shape[1], cp, B, h_q, int(max_ctx),
+                                                     float(scale), int(sink_tokens), int(window_tokens),
+                                                     int(partition_tokens), wp, wb, _stream_ptr(stream)))
+
+
 def paged_attention_prefill(h, desc, layer, out, q, block_tables, context_lens, query_start, max_q_len,
                             max_ctx, scale, stream=None):
     """q, out: bf16 [rows, h_q, d_h]; query_start: int32 [B+1] on the device."""
@@ -581,6 +615,21 @@ class Pool:
         paged_attention_decode_window(self.handle, self.desc, layer, out, q, block_tables, context_lens,
                                       max_ctx, scale, sink_tokens, window_tokens, partition_tokens,
                                       workspace, stream)
+        return out
+
+    def decode_window_append(self, layer, q, k_new, v_new, slot_mapping, block_tables, context_lens, max_ctx,
+                             scale, sink_tokens, window_tokens, partition_tokens=0, out=None, workspace=None,
+                             stream=None):
+        import torch
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            nbytes = self.workspace_bytes(q.shape[0], q.shape[1], max_ctx, partition_tokens)
+            if nbytes > 0:
+                workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+        paged_attention_decode_window_append(self.handle, self.desc, layer, out, q, k_new, v_new, slot_mapping,
+                                             block_tables, context_lens, max_ctx, scale, sink_tokens,
+                                             window_tokens, partition_tokens, workspace, stream)
         return out
 
     def prefill(self, layer, q, block_tables, context_lens, query_start, max_q_len, max_ctx, scale, out=None,

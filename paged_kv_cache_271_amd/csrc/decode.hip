@@ -361,13 +361,17 @@ __device__ inline void run_segment(WaveState<D>& st, const uint8_t* __restrict__
       }
     mx = wave_max16(mx);
     const float m_new = fmaxf(st.m, mx);  // finite: the step holds a valid token
-    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+    // WIN with a fused append: a step may hold no token read yet (a window of
+    // one whose only position is the new token); take weights against 0 then,
+    // which leaves the state as it was
+    const float m_ref = WIN && m_new == -INFINITY ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_ref);
     float psum = 0.0f;
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float e = __builtin_amdgcn_exp2f(S[j][i] - m_new);
+        const float e = __builtin_amdgcn_exp2f(S[j][i] - m_ref);
         S[j][i] = e;
         psum += e;
       }
@@ -513,7 +517,8 @@ struct StreamChunks {
 //
 // WIN: a sliding window of `window` tokens plus `sink` sink tokens; units
 // run over the pages each request reads (visited_pages), so pages outside
-// are never touched and may be free.
+// are never touched and may be free.  APPEND and WIN together: the window of
+// the grown request, its new token taken from k_new / v_new.
 template <int QT, int D, bool APPEND, bool WIN>
 __global__ void __launch_bounds__(256, 3)
 decode_stream_kernel(void* __restrict__ kc_, void* __restrict__ vc_,
@@ -622,18 +627,26 @@ decode_stream_kernel(void* __restrict__ kc_, void* __restrict__ vc_,
       const int ctx = clamp_ctx(ctx_lens, b, max_ctx);
       if constexpr (WIN) {
         // read positions [0, sink) and [ctx - window, ctx); visited pages
-        // [j, j1) map to logical [0, a) then [c, nb)
+        // [j, j1) map to logical [0, a) then [c, nb).  APPEND: the cache
+        // holds positions < ctx - 1, and the segment that ends the request
+        // takes the last one from k_new / v_new
         const VisitedPages vp = visited_pages<true>(ctx, sink, window);
         const int win_lo = max(0, ctx - window);
+        const bool app = APPEND && new_slots[b] >= 0;
+        const int ctx_c = ctx - (app ? 1 : 0);
 #pragma clang loop unroll(disable)
         for (int part = 0; part < 2; ++part) {
           const int lo = part == 0 ? j : max(j, vp.a);
           const int hi = part == 0 ? min(j1, vp.a) : j1;
           const int off = part == 0 ? 0 : vp.c - vp.a;
           if (lo < hi)
-            run_segment<QT, D, true>(st, kc, vc, kscale, vscale, tables + int64_t(b) * max_blocks, ctx, H, g,
+            run_segment<QT, D, true>(st, kc, vc, kscale, vscale, tables + int64_t(b) * max_blocks, ctx_c, H, g,
                                       lo + off, hi + off, scale_log2, qv, r, grp, sink, win_lo, u - u0 + (lo - j),
                                       ctot);
+        }
+        if (app && j1 == nb) {
+          const int64_t nrow = (int64_t(b) * H + g) * D;
+          add_token<D>(st, k_new + nrow, v_new + nrow, qv, scale_log2, grp);
         }
       } else if constexpr (APPEND) {
         // the cache holds positions < ctx - 1; a segment cut down to nothing
@@ -1114,9 +1127,14 @@ int launch_decode_d(const DecodeArgs& a, hipStream_t s) {
   using QF = std::integral_constant<int, kQFp8>;
   using QI = std::integral_constant<int, kQInt8>;
   if (d.cache_dtype == KV_BF16) {
-    if (a.new_slots) go(QB{}, T{}, F{});  // fused append (plain decode only)
-    else if (win) go(QB{}, F{}, T{});
-    else go(QB{}, F{}, F{});
+    if (a.new_slots) {  // fused append
+      if (win) go(QB{}, T{}, T{});
+      else go(QB{}, T{}, F{});
+    } else if (win) {
+      go(QB{}, F{}, T{});
+    } else {
+      go(QB{}, F{}, F{});
+    }
   } else if (d.cache_dtype == KV_FP8_E4M3) {
     if (win) go(QF{}, F{}, T{});
     else go(QF{}, F{}, F{});

@@ -391,6 +391,35 @@ int paged_attention_decode_window(kv_pool* p, int32_t layer, void* out, const vo
   return launch_decode(a, static_cast<hipStream_t>(stream));
 }
 
+int paged_attention_decode_window_append(kv_pool* p, int32_t layer, void* out, const void* q, int32_t q_dtype,
+                                         const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                                         const int32_t* tables, int32_t max_blocks, const int32_t* ctx, int32_t B,
+                                         int32_t h_q, int32_t max_ctx, float scale, int32_t sink, int32_t window,
+                                         int32_t part, void* ws, int64_t ws_bytes, void* stream) {
+  if (p && p->desc.cache_dtype == KV_F32)
+    return fail(KV_E_UNSUPPORTED, "sliding-window decode is built for bf16 and fp8 pools");
+  if (sink < 0 || window < 1)
+    return fail(KV_E_INVALID, "sink %d must be >= 0 and window %d >= 1", sink, window);
+  DecodeArgs a{};
+  const int st = prepare_decode(p, layer, out, q, q_dtype, tables, max_blocks, ctx, B, h_q, max_ctx, scale,
+                                part, ws, ws_bytes, &a);
+  if (st != KV_OK) return st;
+  if (B == 0) return ok();
+  if (!k_new || !v_new || !slot_mapping) return fail(KV_E_INVALID, "NULL device array");
+  a.sink = sink;
+  a.window = window;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p->desc.cache_dtype != KV_BF16) {  // the append kernel, then the windowed decode
+    const int e = launch_append(p, layer, k_new, v_new, slot_mapping, B, s);
+    if (e != KV_OK) return e;
+    return launch_decode(a, s);
+  }
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.new_slots = slot_mapping;
+  return launch_decode(a, s);
+}
+
 int paged_attention_prefill(kv_pool* p, int32_t layer, void* out, const void* q, int32_t q_dtype,
                             const int32_t* tables, int32_t max_blocks, const int32_t* ctx,
                             const int32_t* query_start, int32_t B, int32_t h_q, int32_t max_q_len,

@@ -56,6 +56,17 @@ def check_indices(table, lens, num_blocks, max_ctx):
     assert np.all((used >= 0) & (used < num_blocks))
 
 
+def check_window_indices(table, lens, num_blocks, max_ctx, sink, win):
+    """Every table entry a windowed decode reads (a page holding a sink or a
+    window position) names a real block; released entries are -1."""
+    assert np.all(lens >= 0) and np.all(lens <= max_ctx) and max_ctx <= table.shape[1] * 16
+    for b, n in enumerate(lens):
+        for p in range(-(-int(n) // 16)):
+            lo, hi = 16 * p, min(16 * p + 16, int(n))
+            if lo < sink or hi > int(n) - win:
+                assert 0 <= table[b, p] < num_blocks, (b, p)
+
+
 def check_slots(slots, num_blocks):
     s = np.asarray(slots)
     assert np.all((s == -1) | ((s >= 0) & (s < num_blocks * 16)))
@@ -166,9 +177,10 @@ class Case:
         self.lens_list = [n + 1 for n in self.lens_list]
         self.sync_tables()
 
-    def decode_append_step(self, seed, appends=None, partition_tokens=0):
-        """One fused step (paged_attention_decode_append): request b appends one
-        token when appends[b] (every request by default), then all decode.
+    def decode_append_step(self, seed, appends=None, partition_tokens=0, window=None):
+        """One fused step (paged_attention_decode_append, or with window =
+        (sink, window) paged_attention_decode_window_append): request b appends
+        one token when appends[b] (every request by default), then all decode.
         Checks that the call wrote exactly the new rows into the cache (bf16 /
         f32: the bits at the slots, everything else unchanged; fp8: the host
         mirror's quantiser) and returns the decode output as float64; the case
@@ -192,7 +204,10 @@ class Case:
         assert list(self.lens) == lens_after
         self.sync_tables()
         max_ctx = max(lens_after)
-        check_indices(self.table, self.lens, self.N, max_ctx)
+        if window is None:
+            check_indices(self.table, self.lens, self.N, max_ctx)
+        else:
+            check_window_indices(self.table, self.lens, self.N, max_ctx, *window)
         for b in np.nonzero(appends)[0]:  # the slot is the last position's
             pos = lens_after[b] - 1
             assert slots[b] == self.table[b, pos // 16] * 16 + pos % 16
@@ -201,8 +216,13 @@ class Case:
         vc_before = self.pool.v_cache.clone()
         q = self.dq if self.device_inputs else to_dev_bits(self.q, self.dtype)
         d_slots = torch.from_numpy(slots).to(DEV)
-        out = self.pool.decode_append(0, q, dk, dv, d_slots, self.d_table, self.d_lens, max_ctx,
-                                      1.0 / math.sqrt(self.D), partition_tokens)
+        if window is None:
+            out = self.pool.decode_append(0, q, dk, dv, d_slots, self.d_table, self.d_lens, max_ctx,
+                                          1.0 / math.sqrt(self.D), partition_tokens)
+        else:
+            out = self.pool.decode_window_append(0, q, dk, dv, d_slots, self.d_table, self.d_lens, max_ctx,
+                                                 1.0 / math.sqrt(self.D), window[0], window[1],
+                                                 partition_tokens)
         torch.cuda.synchronize()
         if self.dtype in ("fp8", "int8"):
             if self.ref_pool is not None:
