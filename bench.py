@@ -52,9 +52,9 @@ DEFAULT_SEED = {"llama3_8b": 2, "llama3_70b_long": 3, "fp8": 5, "int8": 5, "pref
 # calibration there (fetch x2, write x1).  They hold for the kernel source they
 # were taken on, identified by its SHA-256; any other source reports null.
 TRAFFIC_SOURCE = "paged_kv_cache_271_amd/csrc/decode.hip"
-TRAFFIC_SHA256 = "a466439f420226d74689370404d9010e8529e6405858d23f27510bd2a7669e62"
-TRAFFIC_BYTES = {"llama3_8b": 594_910_649, "fp8": 1_235_696_206, "llama3_70b_long": 1_360_124_738, "int8": 1_236_004_332,
-                 "llama3_8b_window": 1_096_349_442}
+TRAFFIC_SHA256 = "bc95fb00219fcc0461bba58d29a3b0e45609e963ca66b050e59724a73d4d6019"
+TRAFFIC_BYTES = {"llama3_8b": 594_930_553, "fp8": 1_235_680_312, "llama3_70b_long": 1_360_186_171, "int8": 1_235_987_294,
+                 "llama3_8b_window": 1_098_961_545}
 # The same per launch of prefill_kernel and of block_copy_kernel, from
 # profiles/prefill_llama3_8b_counters.md and
 # profiles/block_copy_cow_fork_hbm_counters.md: (source, its SHA-256, bytes).
