@@ -122,3 +122,40 @@ def test_window_append_argument_errors(gpu_lib):
     plain = c.pool.decode_window(0, q, c.d_table, c.d_lens, ml, 0.1, 4, 16)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), plain.view(torch.int16))
+
+
+def test_llama3_8b_window_full_size(gpu_lib):
+    """The benchmark's windowed step at full size: 64 requests of 8k-16k
+    tokens with Llama-3-8B heads, 4 sinks and a 4096-token window, the dead
+    pages released, then one fused step in both work splits (one token
+    appended per request by the first).  Every output of twelve sampled
+    requests against the oracle over the read positions; every output finite;
+    the cache bits at the new slots checked by the step."""
+    w = synth.WORKLOADS["llama3_8b_window"]
+    sink, win = w["sink"], w["window"]
+    rng = synth.streams(6)
+    lens = synth.uniform_contexts(rng["contexts"], w["batch"], *w["ctx_range"])
+    N = int(sum(oracle.blocks_for(int(n), 16) for n in lens))
+    log(f"llama3_8b_window: B={len(lens)} ctx {lens.min()}..{lens.max()} blocks {N}")
+    c = Case("bf16", w["h_kv"], w["head_dim"], w["h_q"], lens - 1, num_blocks=N,
+             order=synth.permutation(rng["free_order"], N), seed=6, device_inputs=True, max_blocks=1024)
+    n_rel = c.pool.window_release(c.table, c.lens, sink, win)
+    assert n_rel == sum(len(oracle.dead_pages(int(n) - 1, sink, win)) for n in lens)
+    c.sync_tables()
+    picks = sorted(int(b) for b in rng["q"].choice(len(lens), 12, replace=False))
+    for step, part in enumerate((0, w["partition_tokens"])):
+        app = np.ones(len(lens), bool) if step == 0 else np.zeros(len(lens), bool)
+        log(f"  fused windowed step, partition_tokens {part}")
+        got = c.decode_append_step(seed=61 + step, appends=app, partition_tokens=part, window=(sink, win))
+        assert c.lens_list == [int(x) for x in lens]
+        _check_sampled(c, got, sink, win, picks, f"partition {part}")
+
+
+def _check_sampled(c, got, sink, win, picks, what):
+    q = c.q_f64()
+    scale = 1.0 / math.sqrt(c.D)
+    assert np.all(np.isfinite(got)), what
+    for b in picks:
+        K, V = c.seq_f64(b)
+        ref = oracle.attention_window_fp64(q[b], K, V, scale, sink, win)
+        assert_close(got[b], ref, c.tol_key, f"{what} request {b} ctx {c.lens_list[b]}")
