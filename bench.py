@@ -237,21 +237,33 @@ def decode_workload(args, torch, synth, pk, dev, spec=None, layers=0):
     d_slots = torch.empty(B, dtype=torch.int32, device=dev)
     scale = 1.0 / math.sqrt(D)
     stream = torch.cuda.current_stream()
-    state = {"max_ctx": 0, "kv": 0}
+    state = {"max_ctx": 0, "kv": 0, "shadow": None}
 
     def host_reserve():
         slots = pool.batch_reserve(table, lens, np.ones(B, np.int32))
         if window:
             pool.window_release(table, lens, sink, window)
-        pinned = torch.empty(B * MB + 2 * B, dtype=torch.int32, pin_memory=True)
+        # the first reservation sends the whole table; later ones send only
+        # the entries that now name a block (at most one new page per
+        # request; entries released to -1 are never read again and keep
+        # their old block on the device)
+        flat = table.reshape(-1)
+        prev = state["shadow"]
+        idx = (np.arange(B * MB) if prev is None else np.flatnonzero((flat != prev) & (flat >= 0)))
+        state["shadow"] = flat.copy()
+        n = len(idx)
+        pinned = torch.empty(2 * n + 2 * B, dtype=torch.int32, pin_memory=True)
+        pidx = torch.empty(n, dtype=torch.int64, pin_memory=True)
         pn = pinned.numpy()
-        pn[:B * MB] = table.reshape(-1)
-        pn[B * MB:B * MB + B] = lens
-        pn[B * MB + B:] = slots
+        pn[:n] = flat[idx]
+        pn[n:n + B] = lens
+        pn[n + B:n + 2 * B] = slots
+        pidx.numpy()[:] = idx
         dev_buf = pinned.to(dev, non_blocking=True)
-        d_table.copy_(dev_buf[:B * MB].view(B, MB))
-        d_lens.copy_(dev_buf[B * MB:B * MB + B])
-        d_slots.copy_(dev_buf[B * MB + B:])
+        if n:
+            d_table.view(-1).index_copy_(0, pidx.to(dev, non_blocking=True), dev_buf[:n])
+        d_lens.copy_(dev_buf[n:n + B])
+        d_slots.copy_(dev_buf[n + B:n + 2 * B])
         state["max_ctx"] = int(lens.max())
         state["kv"] = int(read_tokens(lens).sum()) * H * D * elem * 2
 
@@ -303,6 +315,10 @@ def decode_workload(args, torch, synth, pk, dev, spec=None, layers=0):
         per_step_kv.append(step(args.warmup + j, events[j]))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # the device table must name the host's block at every page a decode reads
+    nb_now = (lens.astype(np.int64) + 15) // 16
+    live = (table >= 0) & (np.arange(MB)[None, :] < nb_now[:, None])
+    assert np.array_equal(d_table.cpu().numpy()[live], table[live]), "device block table out of date"
     dec_ms = np.array([e[0].elapsed_ms(e[1]) for e in events if e is not None])
     dec_kv = np.array([per_step_kv[j] for j in range(args.steps) if events[j] is not None], float)
 
@@ -465,6 +481,10 @@ def cow_fork_workload(args, torch, synth, pk, dev):
         total += step(events[j])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # the device table must name the host's block at every page a decode reads
+    nb_now = (lens.astype(np.int64) + 15) // 16
+    live = (table >= 0) & (np.arange(MB)[None, :] < nb_now[:, None])
+    assert np.array_equal(d_table.cpu().numpy()[live], table[live]), "device block table out of date"
     dec_ms = np.array([e[0].elapsed_ms(e[1]) for e in events if e is not None])
     cpu = None
     if not args.no_cpu_baseline:
@@ -526,6 +546,10 @@ def prefill_workload(args, torch, synth, pk, dev):
         step(args.warmup + j, events[j])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # the device table must name the host's block at every page a decode reads
+    nb_now = (lens.astype(np.int64) + 15) // 16
+    live = (table >= 0) & (np.arange(MB)[None, :] < nb_now[:, None])
+    assert np.array_equal(d_table.cpu().numpy()[live], table[live]), "device block table out of date"
     dec_ms = np.array([e[0].elapsed_ms(e[1]) for e in events if e is not None])
     cpu = None
     if not args.no_cpu_baseline:
