@@ -230,8 +230,7 @@ def decode_workload(args, torch, synth, pk, dev, spec=None, layers=0):
     v_new = synth.device_normal((model_steps, L, B, H, D), 8, dev, in_dt, outlier, 8.0)
     q_all = synth.device_normal((model_steps, L, B, h_q, D), 9, dev, in_dt)
     out = torch.empty((B, h_q, D), dtype=in_dt, device=dev)
-    ws_bytes = pool.workspace_bytes(B, h_q, int(final.max()), args.partition)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    ws = pool.new_workspace(B, h_q, int(final.max()), args.partition)   # counters zeroed once
     d_table = torch.empty((B, MB), dtype=torch.int32, device=dev)
     d_lens = torch.empty(B, dtype=torch.int32, device=dev)
     d_slots = torch.empty(B, dtype=torch.int32, device=dev)

@@ -260,9 +260,25 @@ int kv_append(kv_pool* pool, int32_t layer, const void* k_new, const void* v_new
 
 /* Workspace bytes paged_attention_decode needs for this batch shape, -1 on
  * invalid arguments.  fp32 caches: 0 when one partition covers max_ctx.
- * bf16, fp8 and int8 caches: always > 0 (split states plus B + 1 integers). */
+ * bf16, fp8 and int8 caches: always > 0: 256 KiB of piece-arrival counters,
+ * then the split states, then B + 1 integers.  The workspace is caller-owned
+ * device memory, 16-byte aligned.
+ * bf16 / fp8 / int8 workspaces: the first 256 KiB must be zero before the
+ * workspace's first decode call (paged_attention_workspace_init, or memory
+ * the caller zeroed); every decode call leaves them zero, so one workspace
+ * serves any number of later calls of any shape that fits it.  Two calls
+ * that run at the same time need two workspaces. */
 int64_t paged_attention_workspace_bytes(const kv_pool* pool, int32_t B, int32_t h_q,
                                         int32_t max_ctx, int32_t partition_tokens);
+
+/* Device: zero the counter region of a bf16 / fp8 / int8 decode workspace
+ * (its first 256 KiB) on hip_stream, with a fill kernel (no memset node, so
+ * it may be captured in a graph).  Nothing to do for f32 pools or
+ * workspace_bytes == 0.  KV_E_INVALID for a NULL pool or workspace, a
+ * negative size or a workspace not 16-byte aligned; KV_E_WORKSPACE when
+ * workspace_bytes is below 256 KiB. */
+int paged_attention_workspace_init(const kv_pool* pool, void* workspace, int64_t workspace_bytes,
+                                   void* hip_stream);
 
 /* Device: one decode step of attention for B requests in layer `layer`.
  * For request b and query head h (group g = h / (h_q / num_kv_heads)), with
@@ -285,7 +301,10 @@ int64_t paged_attention_workspace_bytes(const kv_pool* pool, int32_t B, int32_t 
  *  - bf16, fp8 and int8 caches (B <= 8192): 0 splits the blocks of the whole batch
  *    evenly over the kernel's waves; otherwise each piece covers at most
  *    partition_tokens tokens.  Pieces that do not cover a whole request leave
- *    states in the workspace, merged by a second kernel in piece order.
+ *    states in the workspace, merged in piece order: by the last piece of the
+ *    request to finish, inside the same kernel, when requests have few pieces
+ *    (at most 16 on average and B * num_kv_heads * ceil(h_q / num_kv_heads /
+ *    16) <= 65536), else by a second kernel.
  * Results depend on the context lengths of the batch (through the split) but
  * not on which physical blocks hold the data.  Accumulation is fp32; the
  * result is rounded to nearest even into out. */

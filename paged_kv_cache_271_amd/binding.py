@@ -50,6 +50,7 @@ SIGNATURES = {
     "kv_batch_reserve": (ctypes.c_int, [_P, _I32, _PI32, _I32, _PI32, _PI32, _PI32]),
     "kv_append": (ctypes.c_int, [_P, _I32, _P, _P, _P, _I32, _P]),
     "paged_attention_workspace_bytes": (_I64, [_P, _I32, _I32, _I32, _I32]),
+    "paged_attention_workspace_init": (ctypes.c_int, [_P, _P, _I64, _P]),
     "paged_attention_decode": (ctypes.c_int, [_P, _I32, _P, _P, _I32, _P, _I32, _P, _I32, _I32,
                                               _I32, ctypes.c_float, _I32, _P, _I64, _P]),
     "paged_attention_decode_append": (ctypes.c_int, [_P, _I32, _P, _P, _I32, _P, _P, _P, _P, _I32,
@@ -347,6 +348,27 @@ def paged_attention_workspace_bytes(h, B, h_q, max_ctx, partition_tokens=0):
     return _lib.paged_attention_workspace_bytes(h, B, h_q, max_ctx, partition_tokens)
 
 
+def paged_attention_workspace_init(h, workspace, stream=None):
+    """Zero the counter region of a decode workspace (uint8 device tensor)."""
+    wp = _dev_ptr(workspace, "workspace")
+    _check(_lib.paged_attention_workspace_init(h, wp, workspace.numel() * workspace.element_size(),
+                                               _stream_ptr(stream)))
+
+
+def new_workspace(h, nbytes, device, stream=None):
+    """A decode workspace of nbytes, allocated for `stream` (the caching
+    allocator then reuses it only after that stream's work) with its counter
+    region zeroed on that stream; None when nbytes is 0."""
+    import torch
+    if nbytes <= 0:
+        return None
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    with torch.cuda.stream(s):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    paged_attention_workspace_init(h, ws, s)
+    return ws
+
+
 def paged_attention_decode(h, desc, layer, out, q, block_tables, context_lens, max_ctx, scale,
                            partition_tokens=0, workspace=None, stream=None):
     """q, out: [B, h_q, d_h] (float32 with f32 pools, bfloat16 otherwise);
@@ -590,15 +612,19 @@ class Pool:
     def workspace_bytes(self, B, h_q, max_ctx, partition_tokens=0):
         return paged_attention_workspace_bytes(self.handle, B, h_q, max_ctx, partition_tokens)
 
+    def new_workspace(self, B, h_q, max_ctx, partition_tokens=0, device=None, stream=None):
+        """A ready decode workspace for this shape (counters zeroed), or None."""
+        nbytes = self.workspace_bytes(B, h_q, max_ctx, partition_tokens)
+        return new_workspace(self.handle, nbytes, device or self.k_cache.device, stream)
+
     def decode(self, layer, q, block_tables, context_lens, max_ctx, scale, partition_tokens=0,
                out=None, workspace=None, stream=None):
         import torch
         if out is None:
             out = torch.empty_like(q)
         if workspace is None:
-            nbytes = self.workspace_bytes(q.shape[0], q.shape[1], max_ctx, partition_tokens)
-            if nbytes > 0:
-                workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+            workspace = self.new_workspace(q.shape[0], q.shape[1], max_ctx, partition_tokens, q.device,
+                                           stream)
         paged_attention_decode(self.handle, self.desc, layer, out, q, block_tables, context_lens,
                                max_ctx, scale, partition_tokens, workspace, stream)
         return out
@@ -609,9 +635,8 @@ class Pool:
         if out is None:
             out = torch.empty_like(q)
         if workspace is None:
-            nbytes = self.workspace_bytes(q.shape[0], q.shape[1], max_ctx, partition_tokens)
-            if nbytes > 0:
-                workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+            workspace = self.new_workspace(q.shape[0], q.shape[1], max_ctx, partition_tokens, q.device,
+                                           stream)
         paged_attention_decode_window(self.handle, self.desc, layer, out, q, block_tables, context_lens,
                                       max_ctx, scale, sink_tokens, window_tokens, partition_tokens,
                                       workspace, stream)
@@ -624,9 +649,8 @@ class Pool:
         if out is None:
             out = torch.empty_like(q)
         if workspace is None:
-            nbytes = self.workspace_bytes(q.shape[0], q.shape[1], max_ctx, partition_tokens)
-            if nbytes > 0:
-                workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+            workspace = self.new_workspace(q.shape[0], q.shape[1], max_ctx, partition_tokens, q.device,
+                                           stream)
         paged_attention_decode_window_append(self.handle, self.desc, layer, out, q, k_new, v_new, slot_mapping,
                                              block_tables, context_lens, max_ctx, scale, sink_tokens,
                                              window_tokens, partition_tokens, workspace, stream)
@@ -651,9 +675,8 @@ class Pool:
         if out is None:
             out = torch.empty_like(q)
         if workspace is None:
-            nbytes = self.workspace_bytes(q.shape[0], q.shape[1], max_ctx, partition_tokens)
-            if nbytes > 0:
-                workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+            workspace = self.new_workspace(q.shape[0], q.shape[1], max_ctx, partition_tokens, q.device,
+                                           stream)
         paged_attention_decode_append(self.handle, self.desc, layer, out, q, k_new, v_new,
                                       slot_mapping, block_tables, context_lens, max_ctx, scale,
                                       partition_tokens, workspace, stream)

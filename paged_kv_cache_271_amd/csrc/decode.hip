@@ -142,6 +142,39 @@ __device__ inline float wave_sum16(float x) {
   return x + __shfl_xor(x, 32);
 }
 
+// ------------------------------------------------------------------------
+// Device-coherent accesses for the in-kernel piece merge.  Each XCD has its
+// own L2, which is not kept coherent with the others for ordinary accesses;
+// loads and stores carrying the sc1 cache-policy bit (agent scope, as the
+// compiler emits for agent-scope atomic loads and stores) bypass the
+// non-coherent levels, so a state stored by a wave on one XCD is what a
+// wave on another XCD loads after it has seen that store's arrival count.
+constexpr int kCoherent = 16;  // sc1 bit of the buffer instructions' cache policy
+
+__device__ inline __amdgpu_buffer_rsrc_t raw_rsrc(const void* base) {
+  // raw buffer (stride 0), no bounds beyond the 32-bit offset range
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, 0x00020000);
+}
+__device__ inline void store16_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCoherent);
+}
+__device__ inline void store8_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kCoherent);
+}
+__device__ inline u32x4 load16_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherent);
+}
+__device__ inline u32x2 load8_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCoherent);
+}
+// Wait until every memory access this wave issued has completed (the stores
+// above are then visible at agent scope); also a compiler barrier.
+__device__ inline void wait_all_memory() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt left alone
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
 template <typename OutT>
 __device__ inline OutT to_out(float x);
 template <>
@@ -505,6 +538,80 @@ struct StreamChunks {
   __device__ int64_t chunk_of(int64_t x) const { return C > 0 ? x / C : ((x + 1) * N - 1) / U; }
 };
 
+// Where piece k of a row lives: the row's pieces are the segments of chunks
+// c0, c0 + 1, ... that cover it; the first may be the chunk's second segment
+// (role 1), every later one is its chunk's first (role 0).  Two state sets
+// per chunk, one per wave of a workgroup chunk (coop) and HS rows each.
+__device__ inline int64_t piece_slot_base(int64_t c0, int first_role, int k, bool coop, int wv, int HS) {
+  const int64_t cr = (c0 + k) * 2 + (k == 0 ? first_role : 0);
+  return (coop ? cr * 4 + wv : cr) * HS;
+}
+
+// Merge the K pieces of one row set (request, kv-head group: nh query heads)
+// in piece order and write its nh output rows, by one whole wave: every lane
+// takes two (head, dimension quad) pairs per pass and folds the pieces with
+// a running maximum, the loads of four pieces in flight together.  The
+// states were stored with device-coherent stores and are loaded the same way.
+template <int D>
+__device__ void merge_row_pieces(uint16_t* __restrict__ out, int64_t row0, int nh, int HS,
+                                 __amdgpu_buffer_rsrc_t rml, __amdgpu_buffer_rsrc_t racc, int64_t c0,
+                                 int first_role, int K, bool coop, int wv, int lane) {
+  constexpr int DQ = D / 4;
+  constexpr int PB = 4;
+  const int quads = nh * DQ;
+  for (int q0 = 0; q0 < quads; q0 += 128) {
+    int qd[2], hh[2];
+    bool on[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      qd[i] = q0 + lane + 64 * i;
+      on[i] = qd[i] < quads;
+      hh[i] = on[i] ? qd[i] / DQ : 0;
+    }
+    float M[2] = {-INFINITY, -INFINITY}, L[2] = {0.0f, 0.0f};
+    f32x4 A[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    for (int k0 = 0; k0 < K; k0 += PB) {
+      u32x2 ml[PB][2];
+      u32x4 ac[PB][2];
+#pragma unroll
+      for (int p = 0; p < PB; ++p) {
+        const int k = k0 + p;
+        const int64_t sb = piece_slot_base(c0, first_role, k, coop, wv, HS);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          ml[p][i] = u32x2{0, 0};
+          ac[p][i] = u32x4{0, 0, 0, 0};
+          if (k < K && on[i]) {
+            const int64_t s = sb + hh[i];
+            ml[p][i] = load8_coherent(rml, uint32_t(s * 8));
+            ac[p][i] = load16_coherent(racc, uint32_t((s * D + 4 * (qd[i] - hh[i] * DQ)) * 4));
+          }
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < PB; ++p) {
+        if (k0 + p >= K) break;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const float m = __uint_as_float(ml[p][i][0]), l = __uint_as_float(ml[p][i][1]);
+          const float Mn = fmaxf(M[i], m);
+          const float eo = __builtin_amdgcn_exp2f(M[i] - Mn), en = __builtin_amdgcn_exp2f(m - Mn);
+          L[i] = L[i] * eo + l * en;
+          A[i] = A[i] * eo + __builtin_bit_cast(f32x4, ac[p][i]) * en;
+          M[i] = Mn;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (!on[i]) continue;
+      const float inv = 1.0f / L[i];
+      const u32x2 pk = {pack_bf16(A[i][0] * inv, A[i][1] * inv), pack_bf16(A[i][2] * inv, A[i][3] * inv)};
+      *reinterpret_cast<u32x2*>(out + (row0 + hh[i]) * D + 4 * (qd[i] - hh[i] * DQ)) = pk;
+    }
+  }
+}
+
 // grid = workers / 4 workgroups of 256 threads; chunk_fixed = 0 for balanced chunks.
 //
 // APPEND (bf16 caches): request b also appends one token, k_new[b] / v_new[b]
@@ -528,9 +635,9 @@ decode_stream_kernel(void* __restrict__ kc_, void* __restrict__ vc_,
                      const int32_t* __restrict__ ctx_lens, int B, int max_ctx, int H, int h_q,
                      int G, int n_hgroups, int HS, float scale_log2, int chunk_fixed,
                      float* __restrict__ ws_ml, float* __restrict__ ws_acc,
-                     int32_t* __restrict__ ws_pref, const uint16_t* __restrict__ k_new,
-                     const uint16_t* __restrict__ v_new, const int32_t* __restrict__ new_slots, int sink,
-                     int window) {
+                     int32_t* __restrict__ ws_pref, int32_t* __restrict__ ws_cnt,
+                     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+                     const int32_t* __restrict__ new_slots, int sink, int window) {
   constexpr int T8 = D / 16;
   __shared__ int32_t s_pref[kMaxStreamB + 1];
   __shared__ int32_t s_tmp[4];
@@ -571,8 +678,17 @@ decode_stream_kernel(void* __restrict__ kc_, void* __restrict__ vc_,
       }
     }
   }
-  if (blockIdx.x == 0)
-    for (int i = threadIdx.x; i <= B; i += 256) ws_pref[i] = s_pref[i];
+  if (ws_cnt == nullptr) {
+    if (blockIdx.x == 0)  // the block prefix of the reduce kernel
+      for (int i = threadIdx.x; i <= B; i += 256) ws_pref[i] = s_pref[i];
+  } else {
+    // no reduce kernel follows: requests without pages get their zero rows here
+    const int row8 = D / 4;  // 8-byte pieces of one output row (the alignment of every out store)
+    for (int b = blockIdx.x; b < B; b += gridDim.x)
+      if (s_pref[b + 1] == s_pref[b])
+        for (int i = threadIdx.x; i < h_q * row8; i += 256)
+          *reinterpret_cast<u32x2*>(out + (int64_t(b) * h_q * row8 + i) * 4) = u32x2{0, 0};
+  }
 
   const int hge = H * n_hgroups;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, uniform
@@ -591,6 +707,7 @@ decode_stream_kernel(void* __restrict__ kc_, void* __restrict__ vc_,
   const int grp = lane >> 4;
   const uint8_t* kc = static_cast<const uint8_t*>(kc_);
   const uint8_t* vc = static_cast<const uint8_t*>(vc_);
+  const __amdgpu_buffer_rsrc_t rml = raw_rsrc(ws_ml), racc = raw_rsrc(ws_acc);
 
   for (int64_t c = coop ? int64_t(blockIdx.x) : int64_t(blockIdx.x) * 4 + wv; c < ch.N; c += W) {
     int64_t u = ch.start(c);
@@ -676,14 +793,34 @@ decode_stream_kernel(void* __restrict__ kc_, void* __restrict__ vc_,
             *reinterpret_cast<u32x2*>(out + (row0 + r) * D + 16 * t + 4 * grp) = pk;
           }
         }
-      } else if (r < nh) {
-        const int64_t slot = (coop ? (c * 2 + role) * 4 + wv : c * 2 + role) * HS + r;
-        if (grp == 0) {
-          ws_ml[slot * 2] = st.m;
-          ws_ml[slot * 2 + 1] = l;
-        }
+      } else {
+        // a piece: its state goes to the workspace with device-coherent stores
+        if (r < nh) {
+          const int64_t slot = (coop ? (c * 2 + role) * 4 + wv : c * 2 + role) * HS + r;
+          if (grp == 0) store8_coherent(rml, uint32_t(slot * 8), u32x2{__float_as_uint(st.m), __float_as_uint(l)});
 #pragma unroll
-        for (int t = 0; t < T8; ++t) *reinterpret_cast<f32x4*>(ws_acc + slot * D + 16 * t + 4 * grp) = st.acc[t];
+          for (int t = 0; t < T8; ++t)
+            store16_coherent(racc, uint32_t((slot * D + 16 * t + 4 * grp) * 4), __builtin_bit_cast(u32x4, st.acc[t]));
+        }
+        if (ws_cnt != nullptr) {
+          // In-kernel merge: once its stores have completed, the wave counts
+          // its piece in the row's arrival counter; the arrival that
+          // completes the row's K pieces resets the counter to zero (every
+          // call leaves the counters as it found them) and merges the pieces.
+          const int64_t start = int64_t(hsets) * s_pref[b] + int64_t(gs) * nb;
+          const int64_t c0 = ch.chunk_of(start);
+          const int K = int(ch.chunk_of(start + nb - 1) - c0 + 1);
+          const int first_role = start > ch.start(c0) ? 1 : 0;
+          int32_t* cnt = ws_cnt + int64_t(b) * hge + gh;
+          wait_all_memory();
+          int old = 0;
+          if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          old = __builtin_amdgcn_readfirstlane(old);
+          if (old == K - 1) {
+            if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            merge_row_pieces<D>(out, row0, nh, HS, rml, racc, c0, first_role, K, coop, wv, lane);
+          }
+        }
       }
       u += j1 - j;
       if (u >= u_end) break;
@@ -1118,7 +1255,8 @@ int launch_decode_d(const DecodeArgs& a, hipStream_t s) {
     constexpr bool AP = decltype(append)::value, WN = decltype(window)::value;
     decode_stream_kernel<QT, D, AP, WN><<<grid, 256, 0, s>>>(
         kc, vc, ks, vs, q, out, a.tables, a.max_blocks, a.ctx, a.B, a.max_ctx, H, a.h_q, G, nhg, a.hs, sl,
-        a.chunk, a.ws_ml, a.ws_acc, a.ws_pref, static_cast<const uint16_t*>(a.k_new),
+        a.chunk, a.ws_ml, a.ws_acc, a.ws_pref, a.merge_inline ? a.ws_cnt : nullptr,
+        static_cast<const uint16_t*>(a.k_new),
         static_cast<const uint16_t*>(a.v_new), a.new_slots, a.sink, a.window);
   };
   using F = std::false_type;
@@ -1144,14 +1282,8 @@ int launch_decode_d(const DecodeArgs& a, hipStream_t s) {
   }
   e = hipGetLastError();
   if (e != hipSuccess) return fail(KV_E_HIP, "decode launch: %s", hipGetErrorString(e));
-  // pieces per (request, set of kv-head groups): on average the chunks of
-  // the balanced split over the batch's sets, at most the partitions of the
-  // longest request with forced chunks
-  const int64_t hge = int64_t(H) * nhg;
-  const int64_t sets = hge % 4 == 0 ? hge / 4 : hge;
-  const int64_t streams = hge % 4 == 0 ? a.workers / 4 : a.workers;
-  const int64_t pieces = a.chunk > 0 ? (int64_t(a.max_ctx) + kBS - 1) / kBS / a.chunk + 2
-                                     : streams / std::max<int64_t>(1, sets * a.B) + 1;
+  if (a.merge_inline) return ok();  // the decode kernel merged its pieces
+  const int64_t pieces = a.pieces;
   const dim3 rows_grid(unsigned((int64_t(a.B) * a.h_q + 3) / 4));
   auto reduce = [&](auto window) {
     constexpr bool WN = decltype(window)::value;
@@ -1172,7 +1304,23 @@ int launch_decode_d(const DecodeArgs& a, hipStream_t s) {
   return ok();
 }
 
+// Zero n 16-byte words (the workspace's merge counters).
+__global__ void __launch_bounds__(256) zero_words_kernel(u32x4* __restrict__ p, int64_t n) {
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256)
+    p[i] = u32x4{0, 0, 0, 0};
+}
+
 }  // namespace
+
+int launch_zero(void* p, int64_t bytes, hipStream_t s) {
+  const int64_t n = bytes / 16;
+  if (n <= 0) return ok();
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1024);
+  zero_words_kernel<<<unsigned(blocks), 256, 0, s>>>(static_cast<u32x4*>(p), n);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(KV_E_HIP, "workspace init launch: %s", hipGetErrorString(e));
+  return ok();
+}
 
 int64_t plan_decode(const kv_pool_desc& d, int32_t B, int32_t h_q, int32_t max_ctx,
                     int32_t partition_tokens, DecodeArgs* a) {
@@ -1205,7 +1353,20 @@ int64_t plan_decode(const kv_pool_desc& d, int32_t B, int32_t h_q, int32_t max_c
   a->workers = kStreamWorkers;
   a->hs = std::min(16, G);
   a->slots = 2 * chunks * a->hs;
-  return a->slots * (2 + d.head_dim) * fsz + (int64_t(B) + 1) * int64_t(sizeof(int32_t));
+  // pieces per (request, set of kv-head groups): on average the chunks of
+  // the balanced split over the batch's sets, at most the partitions of the
+  // longest request with forced chunks
+  const int64_t sets = coop ? hge / 4 : hge;
+  const int64_t streams = coop ? kStreamWorkers / 4 : kStreamWorkers;
+  a->pieces = chunk > 0 ? (int64_t(max_ctx) + kBS - 1) / kBS / chunk + 2
+                        : streams / std::max<int64_t>(1, sets * B) + 1;
+  // Rows with few pieces are merged inside the decode kernel by their last
+  // piece (arrival counters at the start of the workspace); rows with many
+  // pieces by a reduce kernel, which spreads a row's pieces over more lanes.
+  const int64_t state_bytes = a->slots * (2 + d.head_dim) * fsz;
+  a->merge_inline = a->pieces <= kNarrowPieces && int64_t(B) * hge <= kv_merge_counter_slots() &&
+                    state_bytes < (int64_t(1) << 31);
+  return kMergeCounterBytes + state_bytes + (int64_t(B) + 1) * int64_t(sizeof(int32_t));
 }
 
 int launch_decode(const DecodeArgs& a, hipStream_t s) {

@@ -140,6 +140,9 @@ struct DecodeArgs {
   int32_t workers;   // bf16/fp8: waves of the decode kernel
   int32_t hs;        // bf16/fp8: query heads per state (min(16, h_q / h_kv))
   int64_t slots;     // number of states the workspace holds
+  int64_t pieces;    // bf16/fp8: estimated pieces per row (chooses the merge)
+  bool merge_inline; // bf16/fp8: the decode kernel merges the pieces itself
+  int32_t* ws_cnt;   // bf16/fp8: [kMergeCounterBytes / 4] arrival counters, zero between calls
   float* ws_ml;      // [slots][2]  (max in log2 units, sum)
   float* ws_acc;     // [slots][head_dim]
   int32_t* ws_pref;  // bf16/fp8: [B + 1] blocks before each request
@@ -154,10 +157,18 @@ struct DecodeArgs {
   int32_t window;
 };
 
+// Arrival counters of the in-kernel piece merge: the first bytes of every
+// bf16 / fp8 / int8 decode workspace, one int32 per (request, kv-head group),
+// zero before a workspace's first use and left zero by every call.
+constexpr int64_t kMergeCounterBytes = 256 * 1024;
+constexpr int64_t kv_merge_counter_slots() { return kMergeCounterBytes / 4; }
+
 // Fills the plan for a decode of this shape (pointers excluded) and returns
 // the workspace bytes it needs, or a negative kv_status.
 int64_t plan_decode(const kv_pool_desc& d, int32_t B, int32_t h_q, int32_t max_ctx,
                     int32_t partition_tokens, DecodeArgs* plan);
 int launch_decode(const DecodeArgs& a, hipStream_t stream);
+// Zero `bytes` (a multiple of 16) of device memory with a fill kernel.
+int launch_zero(void* p, int64_t bytes, hipStream_t stream);
 
 }  // namespace pagedkv

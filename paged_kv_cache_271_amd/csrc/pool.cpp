@@ -291,6 +291,18 @@ int64_t paged_attention_workspace_bytes(const kv_pool* p, int32_t B, int32_t h_q
   return need < 0 ? -1 : need;
 }
 
+int paged_attention_workspace_init(const kv_pool* p, void* ws, int64_t ws_bytes, void* stream) {
+  if (!p) return fail(KV_E_INVALID, "NULL pool");
+  if (ws_bytes < 0) return fail(KV_E_INVALID, "negative workspace size");
+  if (p->desc.cache_dtype == KV_F32 || ws_bytes == 0) return ok();  // no counters
+  if (!ws) return fail(KV_E_INVALID, "NULL workspace");
+  if (reinterpret_cast<uintptr_t>(ws) % 16 != 0) return fail(KV_E_INVALID, "workspace not 16-byte aligned");
+  if (ws_bytes < kMergeCounterBytes)
+    return fail(KV_E_WORKSPACE, "workspace of %lld bytes, below the %lld counter bytes", (long long)ws_bytes,
+                (long long)kMergeCounterBytes);
+  return launch_zero(ws, kMergeCounterBytes, static_cast<hipStream_t>(stream));
+}
+
 namespace {
 
 // Checks shared by the decode entry points; fills the plan on success.
@@ -317,6 +329,8 @@ int prepare_decode(kv_pool* p, int32_t layer, void* out, const void* q, int32_t 
   if (need < 0) return int(need);  // plan_decode recorded the message
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(KV_E_WORKSPACE, "workspace of %lld bytes, %lld needed", (long long)ws_bytes, (long long)need);
+  if (need > 0 && reinterpret_cast<uintptr_t>(ws) % 16 != 0)
+    return fail(KV_E_INVALID, "workspace not 16-byte aligned");
   a->pool = p;
   a->layer = layer;
   a->out = out;
@@ -329,7 +343,13 @@ int prepare_decode(kv_pool* p, int32_t layer, void* out, const void* q, int32_t 
   a->max_ctx = max_ctx;
   a->scale = scale;
   if (need > 0) {
-    a->ws_ml = static_cast<float*>(ws);
+    // bf16 / fp8 / int8: the merge counters come first
+    char* base = static_cast<char*>(ws);
+    if (d.cache_dtype != KV_F32) {
+      a->ws_cnt = reinterpret_cast<int32_t*>(base);
+      base += kMergeCounterBytes;
+    }
+    a->ws_ml = reinterpret_cast<float*>(base);
     a->ws_acc = a->ws_ml + a->slots * 2;
     a->ws_pref = reinterpret_cast<int32_t*>(a->ws_acc + a->slots * d.head_dim);
   }

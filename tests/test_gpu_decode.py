@@ -282,7 +282,7 @@ def test_balanced_split_reused_workspace(gpu_lib):
     lens = [int(x) for x in np.random.default_rng(21).integers(900, 1300, 64)]
     c = Case("bf16", 8, 128, 32, lens, seed=21, device_inputs=True)
     max_ctx = max(lens)
-    ws = torch.empty(c.pool.workspace_bytes(64, 32, max_ctx), dtype=torch.uint8, device=DEV)
+    ws = c.pool.new_workspace(64, 32, max_ctx)
     outs = []
     for _ in range(3):
         out = c.pool.decode(0, c.dq, c.d_table, c.d_lens, max_ctx, 1.0 / math.sqrt(128), 0, workspace=ws)

@@ -34,7 +34,7 @@ def _declared_functions():
 
 def test_exports_every_declared_function(lib):
     names = _declared_functions()
-    assert len(names) == 31
+    assert len(names) == 32
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(pk.SIGNATURES) == names
@@ -163,10 +163,11 @@ def test_device_entry_argument_checks(lib):
             assert lib.paged_attention_workspace_bytes(h, 2, 4, 64, 0) == 0
             assert lib.paged_attention_workspace_bytes(h, 2, 4, 513, 0) == 2 * 4 * 2 * 66 * 4
         else:
-            # pieces of 1 block: 2 requests x 2 kv-heads x 4 blocks = 16 pieces, two
-            # state slots each, 2 query heads per slot; plus B + 1 prefix integers
-            assert need == 2 * 16 * 2 * (2 + 64) * 4 + 3 * 4
-            w = (lib.paged_attention_workspace_bytes(h, 2, 4, 64, 0) - 3 * 4) // (2 * 2 * 66 * 4)
+            # 256 KiB of merge counters; pieces of 1 block: 2 requests x 2 kv-heads x
+            # 4 blocks = 16 pieces, two state slots each, 2 query heads per slot;
+            # plus B + 1 prefix integers
+            assert need == 256 * 1024 + 2 * 16 * 2 * (2 + 64) * 4 + 3 * 4
+            w = (lib.paged_attention_workspace_bytes(h, 2, 4, 64, 0) - 256 * 1024 - 3 * 4) // (2 * 2 * 66 * 4)
             assert w >= 256                                  # one slot pair per wave
             assert lib.paged_attention_workspace_bytes(h, 9000, 4, 64, 0) == -1   # batch cap
         pk.kv_pool_destroy(h)

@@ -91,8 +91,7 @@ class PrefixChurn:
         self.d_lens = torch.empty(batch, dtype=torch.int32, device=dev)
         self.out = torch.empty((batch, HQ, D), dtype=torch.bfloat16, device=dev)
         max_ctx = prefix + suffix[1] + steps + 1
-        self.ws = torch.empty(max(self.pool.workspace_bytes(batch, HQ, max_ctx), 1),
-                              dtype=torch.uint8, device=dev)
+        self.ws = self.pool.new_workspace(batch, HQ, max_ctx)   # counters zeroed once
         # admit the first batch (an append pass without a decode)
         n_new = np.zeros(batch, np.int32)
         for b in range(batch):
