@@ -1,8 +1,10 @@
 """Pins of the sliding-window / attention-sink oracle: special cases with a
 known answer, brute force over explicit position lists, invariance to the
-excluded positions, the memory formula's printed example, and a brute-force
-definition of a dead page (no later request length reads it).  Planted
-off-by-one mistakes must fail them."""
+excluded positions, the memory formula's printed example, a brute-force
+definition of a dead page (no later request length reads it), and the page
+release checked against an independent model of it (refcounts, free stack,
+-1 marking, a second call, a page shared with the prefix cache, all-or-nothing
+failure).  Planted mistakes must fail them."""
 
 import math
 
@@ -96,3 +98,146 @@ def test_planted_off_by_one_fails():
             test_window_of_one_is_the_new_token()
     finally:
         W.window_positions = orig
+
+
+# ------------------------------------------------------ window_release pins --
+# An independent model of what releasing the dead pages must do, built from
+# window_positions alone (never from dead_pages or window_release): a page may
+# go back only if no position of it is read at this length or any later one,
+# and every such page must go back.  Drops happen request by request, page by
+# page; a page returns to the free stack when its last reference is dropped.
+
+def _never_read_again(n, p, sink, win, horizon=200):
+    return not any(t < n2 and 16 * p <= t < 16 * p + 16
+                   for n2 in range(n, n + horizon)
+                   for t in W.window_positions(n2, sink, win))
+
+
+def _expected_release(rc, free, table, lens, sink, win):
+    """(refcounts, free stack top-first, table, released) after the release,
+    or None when some drop would hit a page with no reference left."""
+    rc, free = dict(rc), list(free)
+    table = [list(r) for r in table]
+    n_rel = 0
+    for b, row in enumerate(table):
+        for p in range(-(-lens[b] // 16)):
+            if row[p] == -1 or not _never_read_again(lens[b], p, sink, win):
+                continue
+            blk = row[p]
+            if rc.get(blk, 0) <= 0:
+                return None
+            rc[blk] -= 1
+            if rc[blk] == 0:
+                free.insert(0, blk)
+            row[p] = -1
+            n_rel += 1
+    return rc, free, table, n_rel
+
+
+def _scenario(seed, n_req=4, shared_pages=3, cache_refs=True):
+    """A pool whose requests share their first `shared_pages` pages (the prefix,
+    also referenced once by a prefix cache when cache_refs), then private pages."""
+    rng = np.random.default_rng(seed)
+    N = 200
+    alloc = oracle.RefAllocator(N, rng.permutation(N))
+    prefix = [alloc.alloc() for _ in range(shared_pages)]
+    lens = [int(rng.integers(16 * shared_pages, 16 * shared_pages + 120)) for _ in range(n_req)]
+    table = []
+    for b in range(n_req):
+        row = list(prefix)
+        for blk in prefix:
+            alloc.retain(blk)
+        while len(row) < -(-lens[b] // 16):
+            row.append(alloc.alloc())
+        table.append(row)
+    if not cache_refs:
+        for blk in prefix:
+            alloc.release(blk)          # only the tables hold the prefix then
+    return alloc, table, lens
+
+
+def _state(alloc, blocks):
+    return {b: alloc.refcount(b) for b in blocks}, alloc.free_list_top_first()
+
+
+def check_window_release(release):
+    """Run `release` (window_release's signature) on seeded scenarios and compare
+    with the independent model; raises AssertionError on any difference."""
+    for seed in range(6):
+        for sink, win in ((0, 1), (4, 16), (3, 40), (16, 17), (20, 5), (0, 30)):
+            alloc, table, lens = _scenario(seed, cache_refs=bool(seed % 2))
+            blocks = sorted({b for r in table for b in r})
+            rc0, free0 = _state(alloc, blocks)
+            want = _expected_release(rc0, free0, table, lens, sink, win)
+            assert want is not None
+            got_n = release(alloc, table, lens, sink, win)
+            rc1, free1 = _state(alloc, blocks)
+            assert got_n == want[3], (seed, sink, win)
+            assert table == want[2], (seed, sink, win)
+            assert rc1 == want[0], (seed, sink, win)
+            assert free1 == want[1], (seed, sink, win)
+            # a second call with the same lengths finds nothing left to drop
+            assert release(alloc, table, lens, sink, win) == 0
+            assert _state(alloc, blocks) == (rc1, free1)
+            # every released page holds no position read at any later length
+            for b, row in enumerate(table):
+                for p, blk in enumerate(row):
+                    if blk == -1:
+                        assert _never_read_again(lens[b], p, sink, win)
+    # a page mapped by three tables and held by the prefix cache: dropped three
+    # times, freed only when the cache lets go as well
+    alloc = oracle.RefAllocator(10, list(range(10)))
+    blk = alloc.alloc()                       # the cache's reference
+    table = []
+    for _ in range(3):
+        alloc.retain(blk)
+        table.append([blk, alloc.alloc(), alloc.alloc()])
+    lens = [40, 40, 40]
+    assert release(alloc, table, lens, 0, 16) == 3   # page 0 is dead in every request
+    assert alloc.refcount(blk) == 1 and blk not in alloc.free_list_top_first()
+    assert [r[0] for r in table] == [-1, -1, -1]
+    alloc.release(blk)
+    assert alloc.free_list_top_first()[0] == blk
+    # a dead entry naming a free page: BadBlock, and nothing changes
+    alloc = oracle.RefAllocator(10, list(range(10)))
+    live = [alloc.alloc() for _ in range(4)]
+    alloc.release(live[2])                    # page live[2] is free now
+    table = [[live[0], live[1], live[3]], [live[2], live[3], live[1]]]
+    for blk in (live[1], live[3]):
+        alloc.retain(blk)
+    lens = [48, 48]
+    before = ([list(r) for r in table], _state(alloc, range(10)))
+    with pytest.raises(oracle.BadBlock):
+        release(alloc, table, lens, 0, 8)
+    assert ([list(r) for r in table], _state(alloc, range(10))) == before
+
+
+def test_window_release_matches_model():
+    check_window_release(W.window_release)
+
+
+def _planted(kind):
+    """window_release with one mistake planted (test of the pins above)."""
+    from oracle.allocator import BadBlock
+
+    def release(alloc, table, lens, sink, window, block_size=16):
+        n = 0
+        for b, row in enumerate(table):
+            s = 0 if kind == "sink" else sink
+            for p in W.dead_pages(lens[b], s, window, block_size):
+                if row[p] == -1:
+                    continue
+                if kind == "partial" and alloc.refcount(row[p]) == 0:
+                    raise BadBlock(row[p])
+                alloc.release(row[p])
+                if kind != "no_mark":
+                    row[p] = -1
+                n += 1
+        return n
+    return release
+
+
+@pytest.mark.parametrize("kind", ["no_mark", "sink", "partial"])
+def test_window_release_planted_mistakes_fail(kind):
+    with pytest.raises((AssertionError, oracle.BadBlock)):
+        check_window_release(_planted(kind))
