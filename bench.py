@@ -3,12 +3,14 @@
 Default workload (the one the metric is quoted on): one layer of a
 Llama-3-8B-shaped decode batch -- h_q 32, h_kv 8, d_h 128, bf16, block size 16,
 64 requests with contexts uniform on [512, 4096].  A step is one pass of the
-whole hot path for one layer: the host allocator reserves blocks and maps the
-slot of every request's new token (once per model step, i.e. every `layers`
-steps), the table/length/slot arrays go to the device, and one
-paged_attention_decode_append call writes the new token's K and V and reads
-the whole cache (for bf16 one kernel does both; --two-calls times
-kv_append + paged_attention_decode instead).  The pool
+whole hot path for one layer: one paged_attention_decode_append call writes
+the new token's K and V and reads the whole cache (for bf16 one kernel does
+both and merges its split pieces itself; --two-calls times kv_append +
+paged_attention_decode instead).  Once per model step, i.e. every `layers`
+steps, the host allocator also reserves blocks and maps the slot of every
+request's new token, and the table/length/slot arrays go to the device; a
+timed region shorter than `layers` steps that does not start a model step
+(such as --steps 20 --warmup 5 with 32 layers) holds no reservation.  The pool
 holds `layers` layers (32, as in Llama-3-8B) and the steps walk them in order,
 so each step reads a layer whose K/V was last touched `layers - 1` steps
 earlier, far beyond the 256 MB last-level cache, as in a real decode step.
@@ -41,7 +43,14 @@ sys.path.insert(0, ROOT)
 METRIC = "paged decode-attention KV GB/s (% of HBM peak) + µs/step, Llama-3-8B shape"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix peak of MI355X
-EVENT_EVERY = 8
+
+
+def event_every(steps):
+    """Bracket every timed step's call with events up to 256 steps, else every
+    (steps // 256)-th step: at least 256 bracketed calls on long runs, all of
+    them on short ones.  Events are created without the system-scope fence
+    (TimingEvent), so recording them costs the steps nothing measurable."""
+    return max(1, steps // 256)
 DEFAULT_LAYERS = {"llama3_8b": 32, "llama3_70b_long": 8, "fp8": 16, "int8": 16, "llama3_8b_window": 4}
 DEFAULT_SEED = {"llama3_8b": 2, "llama3_70b_long": 3, "fp8": 5, "int8": 5, "prefix_churn": 4, "cow_fork": 6,
                 "llama3_8b_window": 7, "prefill": 8, "ctx_sweep": 2}
@@ -303,10 +312,9 @@ def decode_workload(args, torch, synth, pk, dev, spec=None, layers=0):
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
 
-    # events bracket the decode call of every EVENT_EVERY-th timed step (an
-    # event record still idles the GPU briefly, so not every step pays it)
-    events = [(TimingEvent(), TimingEvent()) if j % EVENT_EVERY == 0 else None
-              for j in range(args.steps)]
+    # events bracket the decode call of the timed steps (event_every)
+    every = event_every(args.steps)
+    events = [(TimingEvent(), TimingEvent()) if j % every == 0 else None for j in range(args.steps)]
     per_step_kv = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -341,7 +349,8 @@ def decode_workload(args, torch, synth, pk, dev, spec=None, layers=0):
     return dict(wall=wall, kv_total=float(sum(per_step_kv)), dec_ms=dec_ms, dec_kv=dec_kv, probe=probe,
                 config=config, cpu=cpu, traffic=measured_traffic(name, args.two_calls), dtype={"fp8": "fp8-e4m3 K/V, bf16 q", "int8": "int8 K/V, bf16 q"}.get(dtype, "bf16"),
                 kernel=("paged_attention_decode_window" if window else "paged_attention_decode")
-                + ("" if two_calls else "_append") + " call (decode_stream_kernel + piece merge)")
+                + ("" if two_calls else "_append") + " call (decode_stream_kernel, merging its split pieces "
+                "itself; a reduce kernel follows only for requests split into many pieces)")
 
 
 SWEEP_CTX = (512, 1024, 2048, 4096, 8192, 16384)
@@ -473,7 +482,8 @@ def cow_fork_workload(args, torch, synth, pk, dev):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [(TimingEvent(), TimingEvent()) if j % EVENT_EVERY == 0 else None for j in range(args.steps)]
+    every = event_every(args.steps)
+    events = [(TimingEvent(), TimingEvent()) if j % every == 0 else None for j in range(args.steps)]
     t0 = time.perf_counter()
     total = 0
     for j in range(args.steps):
@@ -539,7 +549,8 @@ def prefill_workload(args, torch, synth, pk, dev):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    events = [(TimingEvent(), TimingEvent()) if j % EVENT_EVERY == 0 else None for j in range(args.steps)]
+    every = event_every(args.steps)
+    events = [(TimingEvent(), TimingEvent()) if j % every == 0 else None for j in range(args.steps)]
     t0 = time.perf_counter()
     for j in range(args.steps):
         step(args.warmup + j, events[j])
@@ -604,7 +615,9 @@ def main():
     roofline = None
     if r["dec_ms"] is not None:
         dec_mean_s = float(r["dec_ms"].mean()) / 1e3
+        dec_p50_s = float(np.median(r["dec_ms"])) / 1e3
         achieved = float(r["dec_kv"].mean()) / dec_mean_s / unit_scale
+        achieved_p50 = float(r["dec_kv"].mean()) / dec_p50_s / unit_scale
         log(f"timed call {dec_mean_s * 1e6:.1f} us mean over {len(r['dec_ms'])} calls "
             f"(p10 {np.percentile(r['dec_ms'], 10) * 1e3:.1f}, p90 {np.percentile(r['dec_ms'], 90) * 1e3:.1f}), "
             f"{achieved:.0f} {unit}")
@@ -615,6 +628,7 @@ def main():
             "peak": peak,
             "unit": unit,
             "frac": round(achieved / peak, 4),
+            "frac_median_call": round(achieved_p50 / peak, 4),
             "traffic": r.get("traffic"),
             "traffic_note": r.get("traffic_note", "HBM bytes read + written per decode_stream_kernel "
                                   "launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated); null if "

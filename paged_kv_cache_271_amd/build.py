@@ -1,6 +1,13 @@
 """Build libpagedkv.so for gfx950 with hipcc, in-tree.
 
 Usage: python -m paged_kv_cache_271_amd.build  (or call build()).
+
+build_host_sanitized() builds libpagedkv_host_san.so instead: the host
+sources alone (allocator, slot mapping, reservations, prefix cache, launch
+planning, argument checks) with g++ under AddressSanitizer and
+UndefinedBehaviorSanitizer, every device launch replaced by a stub that
+returns KV_E_HIP.  Load it with the ASan runtime preloaded
+(sanitizer_env()) and PAGEDKV_LIB pointing at it.
 """
 
 import os
@@ -13,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libpagedkv.so")
-SOURCES = ["pool.cpp", "prefix.cpp", "append.hip", "copy.hip", "decode.hip", "prefill.hip", "probe.hip"]
+SOURCES = ["pool.cpp", "prefix.cpp", "plan.cpp", "append.hip", "copy.hip", "decode.hip", "prefill.hip", "probe.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -48,6 +55,40 @@ def build(verbose=False, extra_flags=()):
         print(msg)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
+
+
+HOST_SOURCES = ["pool.cpp", "prefix.cpp", "plan.cpp", "sanitize_stubs.cpp"]
+SAN_LIB_PATH = os.path.join(LIB_DIR, "libpagedkv_host_san.so")
+
+
+def build_host_sanitized():
+    """g++ build of the host half with ASan + UBSan (no device code)."""
+    os.makedirs(LIB_DIR, exist_ok=True)
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    tmp = SAN_LIB_PATH + ".tmp"
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fPIC", "-shared", "-fno-omit-frame-pointer",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(rocm, "include"), "-I", INCLUDE, "-I", CSRC,
+           *[os.path.join(CSRC, s) for s in HOST_SOURCES], "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"g++ failed ({res.returncode}):\n{res.stdout}{res.stderr}")
+    os.replace(tmp, SAN_LIB_PATH)
+    return SAN_LIB_PATH
+
+
+def sanitizer_env(lib_path=SAN_LIB_PATH):
+    """Environment for a Python process that loads the sanitizer build: the
+    ASan runtime preloaded (Python itself is not instrumented), leak checks
+    off (the interpreter keeps memory until exit), any report fatal."""
+    libasan = subprocess.run(["g++", "-print-file-name=libasan.so"], capture_output=True,
+                             text=True).stdout.strip()
+    env = dict(os.environ)
+    env["LD_PRELOAD"] = libasan
+    env["ASAN_OPTIONS"] = "detect_leaks=0:halt_on_error=1:abort_on_error=1"
+    env["UBSAN_OPTIONS"] = "halt_on_error=1:print_stacktrace=1"
+    env["PAGEDKV_LIB"] = lib_path
+    return env
 
 
 if __name__ == "__main__":

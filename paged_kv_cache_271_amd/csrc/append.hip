@@ -14,6 +14,8 @@
 #include <cstdint>
 #include <type_traits>
 
+#include <hip/hip_runtime.h>
+
 #include "internal.h"
 
 namespace pagedkv {

@@ -11,6 +11,8 @@
 
 #include <cstdint>
 
+#include <hip/hip_runtime.h>
+
 #include "internal.h"
 
 namespace pagedkv {

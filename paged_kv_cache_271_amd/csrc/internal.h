@@ -11,7 +11,7 @@
 #include <utility>
 #include <vector>
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include "pagedkv.h"
 
@@ -65,6 +65,15 @@ namespace pagedkv {
 
 constexpr int kBlockSize = 16;
 constexpr int kDefaultPartition = 512;
+// Balanced decode (bf16, fp8, int8 caches): its waves, 256 compute units x 4
+// SIMDs x 3 resident waves, so one launch fills MI355X once; the largest
+// batch (the block prefix of the batch is kept in LDS); rows whose estimated
+// piece count is at most kNarrowPieces are merged inside the decode kernel,
+// or one wave per row by the reduce kernel when the counters do not cover
+// the batch.
+constexpr int kStreamWorkers = 256 * 4 * 3;
+constexpr int kMaxStreamB = 8192;
+constexpr int64_t kNarrowPieces = 16;
 
 // Records a message for kv_last_error() and returns `status` (never throws).
 int fail(int status, const char* fmt, ...);

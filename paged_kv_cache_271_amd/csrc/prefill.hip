@@ -37,6 +37,8 @@
 
 #include <cstdint>
 
+#include <hip/hip_runtime.h>
+
 #include "internal.h"
 
 namespace pagedkv {

@@ -8,6 +8,8 @@
 
 #include <cstdint>
 
+#include <hip/hip_runtime.h>
+
 #include "internal.h"
 #include "pagedkv_probe.h"
 
