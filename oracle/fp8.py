@@ -21,7 +21,9 @@ in the same (block, kv-head) tile; they are consecutive tokens of the call.
 
 * s0 is the tile's stored scale, except that a run whose first token lands at
   offset 0 starts a fresh tile: then s0 = 0 and nothing is re-encoded.
-* amax = max |x| over the run (fp32), s1 = max(s0, amax / 448) in fp32.
+* amax = max |x| over the run (fp32), s1 = max(s0, amax / 448) in fp32.  A NaN
+  in the run does not set the scale: both maxima skip NaN operands, as IEEE
+  maxNum does (the NaN itself is then encoded as the NaN code).
 * If s1 != s0, every slot of the tile below the run's first offset is
   re-encoded: value = decode(code) * s0 (fp32), code = encode(value * (1/s1)).
 * New codes: encode(x * (1/s1)) with the fp32 reciprocal correctly rounded;
@@ -106,8 +108,9 @@ def quantize_run(x_run, tile_codes, s0, first_offset):
     """
     x_run = np.asarray(x_run, dtype=np.float32)
     s0 = np.float32(0.0) if first_offset == 0 else np.float32(s0)
-    amax = np.float32(np.max(np.abs(x_run))) if x_run.size else np.float32(0.0)
-    s1 = np.float32(max(s0, np.float32(amax / np.float32(E4M3_MAX))))
+    # maxNum: NaN operands are skipped (the result is NaN only if all are NaN)
+    amax = np.float32(np.fmax.reduce(np.abs(x_run).ravel())) if x_run.size else np.float32(0.0)
+    s1 = np.float32(np.fmax(s0, np.float32(amax / np.float32(E4M3_MAX))))
     tile = np.array(tile_codes, dtype=np.uint8, copy=True)
     if s1 == np.float32(0.0):
         return np.zeros(x_run.shape, dtype=np.uint8), tile, s1

@@ -221,24 +221,53 @@ struct WaveState {
   float m = -INFINITY;  // running max, log2 units
   float l = 0.0f;       // running sum of 2^(s - m) (this lane group's tokens)
   f32x4 acc[D / 16];    // lane (r, q): head r, dims 16t + 4q + i
+  // int8 caches: acc holds the weighted sum divided by vs, the largest V
+  // tile scale the segment has read so far (0 before the first tile), so
+  // that the fp16 weights p * v_scale / vs fed to the MFMA stay in [0, 1]
+  // whatever the magnitude of V; the true sum is acc * vs
+  float vs = 0.0f;
 };
 
-// The lane's share of the query row as MFMA operands (bf16 bits; for int8
-// caches converted to fp16, exact for magnitudes in fp16's normal range).
+// The lane's share of the query row as MFMA operands (bf16 bits).  Returns
+// the factor the scores must be multiplied by: 1, except for int8 caches,
+// whose operands are fp16: there the group's queries are first multiplied by
+// 2^k, the power of two that puts their largest magnitude in [2^14, 2^15)
+// (exact, and every bf16 value within 2^-24 of that maximum stays an fp16
+// normal, so the conversion is exact for all of them), and 2^-k is returned.
 template <int QT, int D>
-__device__ inline void load_q(u32x4 (&qv)[D / 32], const uint16_t* q, int64_t row0, int r, int grp, int nh) {
+__device__ inline float load_q(u32x4 (&qv)[D / 32], const uint16_t* q, int64_t row0, int r, int grp, int nh) {
+  float qscale_inv = 1.0f;
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk) {
     const int dim0 = QT != kQBf16 ? (D / 4) * grp + 8 * kk : 32 * kk + 8 * grp;
     u32x4 v = {0, 0, 0, 0};
     if (r < nh) v = ld16(q + (row0 + r) * D + dim0);
-    if constexpr (QT == kQInt8) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-        v[w] = pack_op<QT>(__uint_as_float(v[w] << 16), __uint_as_float(v[w] & 0xFFFF0000u));
-    }
     qv[kk] = v;
   }
+  if constexpr (QT == kQInt8) {
+    // largest |q| of the wave's heads (bf16: the top 16 bits of an fp32)
+    uint32_t mx = 0;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) mx = max(mx, max(qv[kk][w] & 0x7FFFu, (qv[kk][w] >> 16) & 0x7FFFu));
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) mx = max(mx, uint32_t(__shfl_xor(int(mx), o)));
+    // exponent of the maximum (bf16 exponent field), 0 for an all-zero group;
+    // scale 2^k with k = 14 - (e - 127), clamped to fp32's normal range
+    const int e = int(mx >> 7);
+    const int k = e == 0 ? 0 : min(max(14 - (e - 127), -126), 127);
+    const float sq = __uint_as_float(uint32_t(127 + k) << 23);
+    qscale_inv = __uint_as_float(uint32_t(127 - k) << 23);
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t v = qv[kk][w];
+        qv[kk][w] = pack_op<QT>(__uint_as_float(v << 16) * sq, __uint_as_float(v & 0xFFFF0000u) * sq);
+      }
+  }
+  return qscale_inv;
 }
 
 // Zero the 16-bit elements e of an 8-element vector whose bit e of `keep` is clear.
@@ -284,7 +313,8 @@ __device__ inline void run_segment(WaveState<D>& st, const uint8_t* __restrict__
                                    const float* __restrict__ vscale, const int32_t* __restrict__ trow,
                                    int ctx, int H, int g, int j0, int j1, float scale_log2,
                                    const u32x4 (&qv)[D / 32], int r, int grp, int sink = 0,
-                                   int win_lo = 0, int64_t done0 = 0, int64_t total = 0) {
+                                   int win_lo = 0, int64_t done0 = 0, int64_t total = 0,
+                                   float qscale_inv = 1.0f) {
   constexpr int NB = kStreamNB;
   constexpr int KK = D / 32;
   constexpr int T8 = D / 16;
@@ -368,10 +398,23 @@ __device__ inline void run_segment(WaveState<D>& st, const uint8_t* __restrict__
     float kfac = scale_log2;
     float vfac = 1.0f;
     if constexpr (Q8) {
+      vfac = 0.0f;  // tiles past the segment: their weights are zero anyway
       if (vV) {
         kfac *= kscale[pV * H + g];
         vfac = vscale[pV * H + g];
       }
+    }
+    float vs_fold = 1.0f;  // int8: acc rescale for a larger V-scale reference
+    if constexpr (QT == kQInt8) {
+      kfac *= qscale_inv;
+      // the step's two tiles: lane groups 0-1 hold one, 2-3 the other
+      const float vs_new = fmaxf(st.vs, fmaxf(vfac, __shfl_xor(vfac, 32)));
+      if (vs_new > 0.0f) {
+        const float inv = 1.0f / vs_new;
+        vs_fold = st.vs * inv;
+        vfac *= inv;
+      }
+      st.vs = vs_new;
     }
     const int valid = vV ? min(kBS, ctx - bV * kBS) - vtok : 0;  // valid among the lane's 8
     uint32_t keep = 0;  // WIN: bit e set when token vtok + e of block bV is read
@@ -411,8 +454,9 @@ __device__ inline void run_segment(WaveState<D>& st, const uint8_t* __restrict__
       }
     st.l = st.l * alpha + psum;
     st.m = m_new;
+    const float afac = QT == kQInt8 ? alpha * vs_fold : alpha;
 #pragma unroll
-    for (int t = 0; t < T8; ++t) st.acc[t] *= alpha;
+    for (int t = 0; t < T8; ++t) st.acc[t] *= afac;
 
     // ---- weighted sum of V: k-slot e is token vtok + e of block bV
     const f32x4 lo = S[0] * vfac, hi = S[1] * vfac;
@@ -738,7 +782,7 @@ decode_stream_kernel(void* __restrict__ kc_, void* __restrict__ vc_,
       const int nh = min(16, G - hg * 16);
       const int64_t row0 = int64_t(b) * h_q + head0;
       u32x4 qv[D / 32];
-      load_q<QT, D>(qv, q, row0, r, grp, nh);
+      const float qsi = load_q<QT, D>(qv, q, row0, r, grp, nh);
       WaveState<D> st;
 #pragma unroll
       for (int t = 0; t < T8; ++t) st.acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -760,7 +804,7 @@ decode_stream_kernel(void* __restrict__ kc_, void* __restrict__ vc_,
           if (lo < hi)
             run_segment<QT, D, true>(st, kc, vc, kscale, vscale, tables + int64_t(b) * max_blocks, ctx_c, H, g,
                                       lo + off, hi + off, scale_log2, qv, r, grp, sink, win_lo, u - u0 + (lo - j),
-                                      ctot);
+                                      ctot, qsi);
         }
         if (app && j1 == nb) {
           const int64_t nrow = (int64_t(b) * H + g) * D;
@@ -781,7 +825,11 @@ decode_stream_kernel(void* __restrict__ kc_, void* __restrict__ vc_,
         }
       } else {
         run_segment<QT, D>(st, kc, vc, kscale, vscale, tables + int64_t(b) * max_blocks, ctx, H, g, j, j1,
-                            scale_log2, qv, r, grp, 0, 0, u - u0, ctot);
+                            scale_log2, qv, r, grp, 0, 0, u - u0, ctot, qsi);
+      }
+      if constexpr (QT == kQInt8) {  // back to true units (acc was relative to st.vs)
+#pragma unroll
+        for (int t = 0; t < T8; ++t) st.acc[t] *= st.vs;
       }
       const float l = wave_sum16(st.l);
       if (j == 0 && j1 == nb) {  // the whole (b, gh): finish here

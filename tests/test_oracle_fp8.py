@@ -134,3 +134,26 @@ def test_pool_fp8_append_runs():
     xin = ((bits.astype(np.uint32) << 16).view(np.float32)).astype(np.float64)
     assert np.max(np.abs(kd - xin)) <= np.max(np.abs(xin)) / 448 * 16
     assert np.array_equal(kd, vd)
+
+
+def test_nan_in_a_run_does_not_set_the_scale():
+    """A NaN among a run's values: the scale and the other codes are those of
+    the run without it (maxNum skips NaN), and the NaN takes the NaN code
+    with its sign."""
+    from oracle import fp8
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((5, 2, 8)).astype(np.float32)
+    x[1, 0, 3] = np.nan
+    x[3, 1, 0] = -np.nan
+    tile = np.zeros((16, 2, 8), np.uint8)
+    codes, _, s1 = fp8.quantize_run(x, tile, np.float32(0), 0)
+    finite = np.isfinite(x)
+    assert s1 == np.float32(np.max(np.abs(x[finite])) / np.float32(448.0))
+    clean = np.where(finite, x, np.float32(0))
+    codes_clean, _, s_clean = fp8.quantize_run(clean, tile, np.float32(0), 0)
+    assert s_clean == s1
+    assert np.array_equal(codes[finite], codes_clean[finite])
+    assert codes[1, 0, 3] == 0x7F and codes[3, 1, 0] == 0xFF
+    # the largest magnitude maps to +-448 (code 0x7E / 0xFE) at this scale
+    k = np.unravel_index(np.argmax(np.where(finite, np.abs(x), 0)), x.shape)
+    assert codes[k] & 0x7F == 0x7E
