@@ -341,6 +341,25 @@ int paged_attention_decode_append(kv_pool* pool, int32_t layer, void* out, const
                                   int32_t h_q, int32_t max_ctx, float scale, int32_t partition_tokens,
                                   void* workspace, int64_t workspace_bytes, void* hip_stream);
 
+/* Device: paged_attention_decode_append without a caller workspace, for
+ * callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Arguments,
+ * kernels and results are those of paged_attention_decode_append; the
+ * workspace is a fixed 24 MiB array inside the library, one per device,
+ * looked up on the first call on that device (the device of hip_stream) and
+ * held until the process ends.  Nothing is allocated.  KV_E_WORKSPACE when
+ * the batch needs more than 24 MiB (paged_attention_workspace_bytes tells;
+ * e.g. any Llama-3-8B or -70B shaped batch of up to 8192 requests with the
+ * default split fits).  Every call on a device shares its array: calls that
+ * overlap on one device race and must not be issued; calls in one stream
+ * order are fine. */
+int paged_attention_decode_append_noalloc(kv_pool* pool, int32_t layer, void* out, const void* q,
+                                          int32_t q_dtype, const void* k_new, const void* v_new,
+                                          const int32_t* slot_mapping, const int32_t* block_tables,
+                                          int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t B,
+                                          int32_t h_q, int32_t max_ctx, float scale, int32_t partition_tokens,
+                                          void* hip_stream);
+
 /* --------------------------------------------------------------- prefill -- */
 
 /* Device: causal attention of each request's new tokens over its paged cache

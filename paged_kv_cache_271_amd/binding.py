@@ -56,6 +56,8 @@ SIGNATURES = {
     "paged_attention_decode_append": (ctypes.c_int, [_P, _I32, _P, _P, _I32, _P, _P, _P, _P, _I32,
                                                      _P, _I32, _I32, _I32, ctypes.c_float, _I32, _P,
                                                      _I64, _P]),
+    "paged_attention_decode_append_noalloc": (ctypes.c_int, [_P, _I32, _P, _P, _I32, _P, _P, _P, _P, _I32,
+                                                             _P, _I32, _I32, _I32, ctypes.c_float, _I32, _P]),
     "kv_prefix_match": (ctypes.c_int, [_P, _I64, _PI32, _I32, _PI32, _I32, _PI32]),
     "kv_prefix_insert": (ctypes.c_int, [_P, _I64, _PI32, _I32, _PI32, _I32, _PI32]),
     "kv_prefix_evict": (ctypes.c_int, [_P, _I32, _PI32, _PI32]),
@@ -425,6 +427,31 @@ def paged_attention_decode_append(h, desc, layer, out, q, k_new, v_new, slot_map
                                               block_tables.shape[1], cp, B, h_q, int(max_ctx),
                                               float(scale), int(partition_tokens), wp, wb,
                                               _stream_ptr(stream)))
+
+
+def paged_attention_decode_append_noalloc(h, desc, layer, out, q, k_new, v_new, slot_mapping, block_tables,
+                                          context_lens, max_ctx, scale, partition_tokens=0, stream=None):
+    """paged_attention_decode_append with the library's fixed scratch as its
+    workspace (no device memory allocated by anyone)."""
+    import torch
+    if q.dim() != 3 or q.shape[2] != desc.head_dim:
+        raise ValueError("q must be [B, h_q, head_dim]")
+    B, h_q, _ = q.shape
+    want = torch.float32 if desc.cache_dtype == KV_F32 else torch.bfloat16
+    qp = _dev_ptr(q, "q", want)
+    op = _dev_ptr(out, "out", want, q.numel())
+    n = B * desc.num_kv_heads * desc.head_dim
+    kp = _dev_ptr(k_new, "k_new", want, n)
+    vp = _dev_ptr(v_new, "v_new", want, n)
+    sp = _dev_ptr(slot_mapping, "slot_mapping", torch.int32, B)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B, max_blocks]")
+    tp = _dev_ptr(block_tables, "block_tables", torch.int32)
+    cp = _dev_ptr(context_lens, "context_lens", torch.int32, B)
+    qd = KV_F32 if want == torch.float32 else KV_BF16
+    _check(_lib.paged_attention_decode_append_noalloc(h, int(layer), op, qp, qd, kp, vp, sp, tp,
+                                                      block_tables.shape[1], cp, B, h_q, int(max_ctx),
+                                                      float(scale), int(partition_tokens), _stream_ptr(stream)))
 
 
 def paged_attention_decode_window(h, desc, layer, out, q, block_tables, context_lens, max_ctx, scale,

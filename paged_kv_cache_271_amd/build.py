@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libpagedkv.so")
-SOURCES = ["pool.cpp", "prefix.cpp", "plan.cpp", "append.hip", "copy.hip", "decode.hip", "prefill.hip", "probe.hip"]
+SOURCES = ["pool.cpp", "prefix.cpp", "plan.cpp", "append.hip", "copy.hip", "decode.hip", "prefill.hip", "probe.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

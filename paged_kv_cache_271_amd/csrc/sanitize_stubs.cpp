@@ -29,6 +29,13 @@ int launch_zero(void*, int64_t, hipStream_t) { return no_device(); }
 
 }  // namespace pagedkv
 
+extern "C" int paged_attention_decode_append_noalloc(kv_pool*, int32_t, void*, const void*, int32_t, const void*,
+                                                     const void*, const int32_t*, const int32_t*, int32_t,
+                                                     const int32_t*, int32_t, int32_t, int32_t, float, int32_t,
+                                                     void*) {
+  return pagedkv::no_device();
+}
+
 extern "C" int kv_probe_gather(const void*, const void*, const int64_t*, const int64_t*, int32_t, int32_t,
                                uint32_t*, int32_t, void*) {
   return pagedkv::no_device();

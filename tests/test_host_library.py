@@ -34,7 +34,7 @@ def _declared_functions():
 
 def test_exports_every_declared_function(lib):
     names = _declared_functions()
-    assert len(names) == 32
+    assert len(names) == 33
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(pk.SIGNATURES) == names
@@ -325,3 +325,17 @@ def test_probe_argument_checks(lib):
     assert probe(rb=24) == -1 and b"run_bytes" in lib.kv_last_error()
     assert probe(wg=0) == -1 and probe(wg=65536) == -1
     assert b"workgroups" in lib.kv_last_error()
+
+
+def test_noalloc_argument_checks(lib):
+    """The no-allocation step refuses a missing pool and a batch whose
+    workspace would not fit its fixed 24 MiB scratch before touching a device."""
+    h, desc = _pool(lib, 64, H=8, D=128)
+    call = lambda **kw: lib.paged_attention_decode_append_noalloc(
+        kw.get("h", h), 0, FAKE, FAKE, pk.KV_BF16, FAKE, FAKE, FAKE, FAKE, 1, FAKE, kw.get("B", 8192),
+        kw.get("hq", 128), 16, ctypes.c_float(0.1), 0, None)
+    assert call(h=None) == -1
+    assert lib.paged_attention_workspace_bytes(h, 8192, 128, 16, 0) > 24 << 20
+    assert call() == -6 and b"scratch" in lib.kv_last_error()
+    assert call(hq=3) == -1                                  # not a multiple of the kv heads
+    pk.kv_pool_destroy(h)
