@@ -275,10 +275,10 @@ def decode_workload(args, torch, synth, pk, dev, spec=None, layers=0):
         state["max_ctx"] = int(lens.max())
         state["kv"] = int(read_tokens(lens).sum()) * H * D * elem * 2
 
-    # fp8 and int8 pools have no fused kernel (the append re-quantises whole
-    # tiles), so their step is always the two calls, with the decode alone
-    # between events
-    two_calls = args.two_calls or dtype in ("fp8", "int8")
+    # every pool type runs the fused step unless --two-calls (fp8 / int8: the
+    # decode kernel re-quantises the new token's tile itself); windowed
+    # 8-bit steps run the append kernel and the windowed decode in one call
+    two_calls = args.two_calls
 
     def step(i, ev=None):
         s, r = divmod(i, L)

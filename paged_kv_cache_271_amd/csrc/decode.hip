@@ -32,6 +32,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include "codec8.h"
 #include "internal.h"
 
 namespace pagedkv {
@@ -169,8 +170,10 @@ __device__ inline u32x4 load16_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off) 
 __device__ inline u32x2 load8_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCoherent);
 }
-// Wait until every memory access this wave issued has completed (the stores
-// above are then visible at agent scope); also a compiler barrier.
+// Wait until every memory access this wave issued has completed, between a
+// workgroup-scope release and acquire: the wave's earlier stores are then
+// visible to its own later loads (and device-coherent stores at agent
+// scope); also a compiler barrier.
 __device__ inline void wait_all_memory() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt left alone
@@ -308,7 +311,7 @@ __device__ inline void progress_prio(int64_t done, int64_t total) {
 // Positions at or past ctx are masked.  WIN: so are positions in
 // [sink, win_lo) (a sliding window with attention sinks).
 template <int QT, int D, bool WIN = false>
-__device__ inline void run_segment(WaveState<D>& st, const uint8_t* __restrict__ kc,
+__device__ __forceinline__ void run_segment(WaveState<D>& st, const uint8_t* __restrict__ kc,
                                    const uint8_t* __restrict__ vc, const float* __restrict__ kscale,
                                    const float* __restrict__ vscale, const int32_t* __restrict__ trow,
                                    int ctx, int H, int g, int j0, int j1, float scale_log2,
@@ -483,6 +486,116 @@ __device__ inline void run_segment(WaveState<D>& st, const uint8_t* __restrict__
   }
 }
 
+// The step's append for an 8-bit cache, inside the decode: the wave that
+// owns tile (block, kv head) `sidx` writes the new token at offset o of it
+// ("KV cache and PagedAttention", askaiml §7: the cache holds codes with a
+// scale).  The rule and the arithmetic are append_q8_kernel's for a run of
+// one token: s1 = max(s0, max |x| / largest code) with s0 = 0 when o == 0;
+// when the scale grows the tile's older codes are re-encoded from
+// decode(code) * s0; the new codes are encode(x * (1 / s1)), 0 when s1 == 0.
+// Plain loads and stores: only this wave touches the tile in this launch,
+// and the workgroup-scope release / acquire that follows (wait_all_memory)
+// orders them before the wave's reads of it.
+template <int D, bool INT8>
+__device__ __forceinline__ void append8_token(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
+                                              float* __restrict__ ksc, float* __restrict__ vsc, int64_t sidx, int o,
+                                              const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vn,
+                                              int lane) {
+  using C = Codec8<INT8>;
+  constexpr int TILE = kBS * D;
+  constexpr int KP = TILE / 16 / 64;  // K pieces per lane
+  constexpr int VR = D / 64;          // V rows per lane
+  auto bf = [](uint16_t b) { return __uint_as_float(uint32_t(b) << 16); };
+  uint8_t* ktile = kc + sidx * TILE;
+  uint8_t* vtile = vc + sidx * TILE;
+  // everything the rule reads, in flight together: both old scales, the new
+  // rows, the old K pieces below the token and the V rows
+  const float sk0 = o == 0 ? 0.0f : ksc[sidx];
+  const float sv0 = o == 0 ? 0.0f : vsc[sidx];
+  float kx[VR], vx[VR];
+#pragma unroll
+  for (int i = 0; i < VR; ++i) {
+    kx[i] = bf(kn[lane + 64 * i]);
+    vx[i] = bf(vn[lane + 64 * i]);
+  }
+  u32x4 kp[KP], vr[VR];
+#pragma unroll
+  for (int i = 0; i < KP; ++i) {
+    const int row = (lane + 64 * i) / (D / 16);
+    kp[i] = row < o ? ld16(ktile + 16 * (lane + 64 * i)) : u32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int i = 0; i < VR; ++i) vr[i] = ld16(vtile + 16 * (lane + 64 * i));
+  float ka = fabsf(kx[0]), va = fabsf(vx[0]);
+#pragma unroll
+  for (int i = 1; i < VR; ++i) {
+    ka = fmaxf(ka, fabsf(kx[i]));
+    va = fmaxf(va, fabsf(vx[i]));
+  }
+#pragma unroll
+  for (int w = 32; w > 0; w >>= 1) {
+    ka = fmaxf(ka, __shfl_xor(ka, w));
+    va = fmaxf(va, __shfl_xor(va, w));
+  }
+  const float sk1 = fmaxf(sk0, ka / C::kMax), sv1 = fmaxf(sv0, va / C::kMax);
+  const bool rek = sk1 != sk0 && o > 0, rev = sv1 != sv0 && o > 0;
+  const float ik = sk1 == 0.0f ? 0.0f : 1.0f / sk1, iv = sv1 == 0.0f ? 0.0f : 1.0f / sv1;
+  auto reenc = [](uint32_t c, float s0, float inv) -> uint32_t {
+    const float x = C::decode(c) * s0;
+    return C::encode(x * inv) & 0xFFu;
+  };
+  // K tile [16][D]: 16-byte pieces lane, lane + 64, ...; the new row's codes
+  // come from the token's values, the rows below it are re-encoded
+#pragma unroll
+  for (int i = 0; i < KP; ++i) {
+    const int pc = lane + 64 * i;
+    const int row = pc / (D / 16), col0 = (pc % (D / 16)) * 16;
+    if (row > o || (row < o && !rek)) continue;
+    u32x4 w = {0, 0, 0, 0};
+    if (row < o) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[k] |= reenc((kp[i][k] >> (8 * e)) & 0xFFu, sk0, ik) << (8 * e);
+    } else if (sk1 != 0.0f) {
+      const u32x4 a = ld16(kn + col0), b = ld16(kn + col0 + 8);  // the row's 16 values
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int idx = 4 * k + e;
+          const u32x4& src = idx < 8 ? a : b;
+          const uint32_t word = src[(idx & 7) >> 1];
+          const float x = __uint_as_float((idx & 1) ? (word & 0xFFFF0000u) : (word << 16));
+          w[k] |= (C::encode(x * ik) & 0xFFu) << (8 * e);
+        }
+    }
+    *reinterpret_cast<u32x4*>(ktile + 16 * pc) = w;
+  }
+  // V tile [D][16]: dimension rows lane, lane + 64, ...; byte o is the new
+  // token, the bytes below it are re-encoded, the ones above stay
+#pragma unroll
+  for (int i = 0; i < VR; ++i) {
+    const uint32_t cnew = sv1 == 0.0f ? 0u : (C::encode(vx[i] * iv) & 0xFFu);
+    u32x4 w = vr[i];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 4 * k + e;
+        if (t > o) continue;
+        const uint32_t c = (w[k] >> (8 * e)) & 0xFFu;
+        const uint32_t v = t == o ? cnew : rev ? reenc(c, sv0, iv) : c;
+        w[k] = (w[k] & ~(0xFFu << (8 * e))) | (v << (8 * e));
+      }
+    *reinterpret_cast<u32x4*>(vtile + 16 * (lane + 64 * i)) = w;
+  }
+  if (lane == 0) {
+    ksc[sidx] = sk1;
+    vsc[sidx] = sv1;
+  }
+}
+
 // Fold one more token, whose K and V rows (head_dim values each, this kv
 // head) are given directly, into the wave state: the score of head r is the
 // dot product of the lane group's quarter of q and of the key, summed over
@@ -574,13 +687,13 @@ __device__ inline void block_prefix_blocks(int32_t* s_pref, int32_t* s_tmp, cons
 // the unit order, so the chunks holding one (b, gh) are consecutive.
 struct StreamChunks {
   int64_t U, C, N;
-  __device__ StreamChunks(int64_t U_, int W, int chunk_fixed) : U(U_), C(chunk_fixed) {
+  __device__ __forceinline__ StreamChunks(int64_t U_, int W, int chunk_fixed) : U(U_), C(chunk_fixed) {
     N = C > 0 ? (U + C - 1) / C : min<int64_t>(W, U);
   }
-  __device__ int64_t start(int64_t c) const { return C > 0 ? c * C : c * U / N; }
-  __device__ int64_t end(int64_t c) const { return C > 0 ? min(U, c * C + C) : (c + 1) * U / N; }
+  __device__ __forceinline__ int64_t start(int64_t c) const { return C > 0 ? c * C : c * U / N; }
+  __device__ __forceinline__ int64_t end(int64_t c) const { return C > 0 ? min(U, c * C + C) : (c + 1) * U / N; }
   // chunk holding unit x (0 <= x < U)
-  __device__ int64_t chunk_of(int64_t x) const { return C > 0 ? x / C : ((x + 1) * N - 1) / U; }
+  __device__ __forceinline__ int64_t chunk_of(int64_t x) const { return C > 0 ? x / C : ((x + 1) * N - 1) / U; }
 };
 
 // Where piece k of a row lives: the row's pieces are the segments of chunks
@@ -598,7 +711,7 @@ __device__ inline int64_t piece_slot_base(int64_t c0, int first_role, int k, boo
 // a running maximum, the loads of four pieces in flight together.  The
 // states were stored with device-coherent stores and are loaded the same way.
 template <int D>
-__device__ void merge_row_pieces(uint16_t* __restrict__ out, int64_t row0, int nh, int HS,
+__device__ __forceinline__ void merge_row_pieces(uint16_t* __restrict__ out, int64_t row0, int nh, int HS,
                                  __amdgpu_buffer_rsrc_t rml, __amdgpu_buffer_rsrc_t racc, int64_t c0,
                                  int first_role, int K, bool coop, int wv, int lane) {
   constexpr int DQ = D / 4;
@@ -674,7 +787,7 @@ __device__ void merge_row_pieces(uint16_t* __restrict__ out, int64_t row0, int n
 template <int QT, int D, bool APPEND, bool WIN>
 __global__ void __launch_bounds__(256, 3)
 decode_stream_kernel(void* __restrict__ kc_, void* __restrict__ vc_,
-                     const float* __restrict__ kscale, const float* __restrict__ vscale,
+                     float* __restrict__ kscale, float* __restrict__ vscale,
                      const uint16_t* __restrict__ q, uint16_t* __restrict__ out,
                      const int32_t* __restrict__ tables, int max_blocks,
                      const int32_t* __restrict__ ctx_lens, int B, int max_ctx, int H, int h_q,
@@ -689,18 +802,19 @@ decode_stream_kernel(void* __restrict__ kc_, void* __restrict__ vc_,
   // APPEND: 16-byte pieces (8 dims) of the new rows; thread i of the grid
   // takes piece i (and i + grid, ... on big batches).  The first piece's
   // loads are issued before the block counts are summed, its stores after.
-  const int pieces = APPEND ? B * H * (D / 8) : 0;
+  constexpr bool APPEND16 = APPEND && QT == kQBf16;  // 8-bit caches append inside their segments
+  const int pieces = APPEND16 ? B * H * (D / 8) : 0;
   const int gthreads = gridDim.x * 256;
   int piece = blockIdx.x * 256 + threadIdx.x;
   u32x4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
   int32_t pslot = -1;
-  if (APPEND && piece < pieces) {
+  if (APPEND16 && piece < pieces) {
     pslot = new_slots[piece / (H * (D / 8))];
     kx = ld16(k_new + int64_t(piece) * 8);
     vx = ld16(v_new + int64_t(piece) * 8);
   }
   block_prefix_blocks<WIN>(s_pref, s_tmp, ctx_lens, B, max_ctx, sink, window);
-  if constexpr (APPEND) {
+  if constexpr (APPEND16) {
     uint16_t* kw = static_cast<uint16_t*>(kc_);
     uint16_t* vw = static_cast<uint16_t*>(vc_);
     while (piece < pieces) {
@@ -809,6 +923,32 @@ decode_stream_kernel(void* __restrict__ kc_, void* __restrict__ vc_,
         if (app && j1 == nb) {
           const int64_t nrow = (int64_t(b) * H + g) * D;
           add_token<D>(st, k_new + nrow, v_new + nrow, qv, scale_log2, grp);
+        }
+      } else if constexpr (APPEND && QT != kQBf16) {
+        // 8-bit cache: the wave whose segment ends the request writes the
+        // new token into the request's last tile (re-encoding it when its
+        // scale grows) before the segment's last step, then runs that step;
+        // every position, the new one included,
+        // comes from the cache, and the steps are those of the plain decode,
+        // so the result is bit for bit that of kv_append followed by
+        // paged_attention_decode.  Only this wave reads the tile (one kv-head
+        // group per kv head).
+        const int32_t slot = __builtin_amdgcn_readfirstlane(new_slots[b]);
+        const int64_t trow_off = int64_t(b) * max_blocks;
+        if (slot >= 0 && j1 == nb) {
+          const int last = j + kStreamNB * ((nb - 1 - j) / kStreamNB);  // first block of the last step
+          if (j < last)
+            run_segment<QT, D>(st, kc, vc, kscale, vscale, tables + trow_off, ctx, H, g, j, last, scale_log2,
+                               qv, r, grp, 0, 0, u - u0, ctot, qsi);
+          append8_token<D, QT == kQInt8>(static_cast<uint8_t*>(kc_), static_cast<uint8_t*>(vc_), kscale, vscale,
+                                         int64_t(slot / kBS) * H + g, slot % kBS,
+                                         k_new + (int64_t(b) * H + g) * D, v_new + (int64_t(b) * H + g) * D, lane);
+          wait_all_memory();
+          run_segment<QT, D>(st, kc, vc, kscale, vscale, tables + trow_off, ctx, H, g, last, nb, scale_log2, qv, r,
+                             grp, 0, 0, u - u0 + (last - j), ctot, qsi);
+        } else {
+          run_segment<QT, D>(st, kc, vc, kscale, vscale, tables + trow_off, ctx, H, g, j, j1, scale_log2, qv, r,
+                             grp, 0, 0, u - u0, ctot, qsi);
         }
       } else if constexpr (APPEND) {
         // the cache holds positions < ctx - 1; a segment cut down to nothing
@@ -1291,8 +1431,8 @@ int launch_decode_d(const DecodeArgs& a, hipStream_t s) {
   auto* q = static_cast<const uint16_t*>(a.q);
   auto* out = static_cast<uint16_t*>(a.out);
   const bool q8 = d.cache_dtype == KV_FP8_E4M3 || d.cache_dtype == KV_INT8;
-  const float* ks = q8 ? a.pool->k_scale + so : nullptr;
-  const float* vs = q8 ? a.pool->v_scale + so : nullptr;
+  float* ks = q8 ? a.pool->k_scale + so : nullptr;
+  float* vs = q8 ? a.pool->v_scale + so : nullptr;
   const bool win = a.window > 0;
   auto go = [&](auto qt, auto append, auto window) {
     constexpr int QT = decltype(qt)::value;
@@ -1319,9 +1459,11 @@ int launch_decode_d(const DecodeArgs& a, hipStream_t s) {
     }
   } else if (d.cache_dtype == KV_FP8_E4M3) {
     if (win) go(QF{}, F{}, T{});
+    else if (a.new_slots) go(QF{}, T{}, F{});  // fused append
     else go(QF{}, F{}, F{});
   } else {
     if (win) go(QI{}, F{}, T{});
+    else if (a.new_slots) go(QI{}, T{}, F{});  // fused append
     else go(QI{}, F{}, F{});
   }
   e = hipGetLastError();

@@ -382,7 +382,11 @@ int paged_attention_decode_append(kv_pool* p, int32_t layer, void* out, const vo
   if (B == 0) return ok();
   if (!k_new || !v_new || !slot_mapping) return fail(KV_E_INVALID, "NULL device array");
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (p->desc.cache_dtype != KV_BF16) {  // the append kernel, then the decode
+  // one kernel for bf16 pools, and for fp8 / int8 pools whose kv heads have
+  // at most 16 query heads (one wave owns each tile it appends to); f32 and
+  // the other 8-bit shapes run the append kernel, then the decode
+  const bool q8 = scaled_dtype(p->desc.cache_dtype);
+  if (p->desc.cache_dtype != KV_BF16 && !(q8 && h_q / p->desc.num_kv_heads <= 16)) {
     const int e = launch_append(p, layer, k_new, v_new, slot_mapping, B, s);
     if (e != KV_OK) return e;
     return launch_decode(a, s);

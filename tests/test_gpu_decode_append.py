@@ -91,6 +91,52 @@ def test_decode_append_equals_two_calls(gpu_lib):
     assert_close(got, two, "bf16", "fused vs two calls")
 
 
+@pytest.mark.parametrize("dtype", ["fp8", "int8"])
+@pytest.mark.parametrize("grow,part", [(1.0, 0), (8.0, 0), (8.0, 32), (1e-3, 0)])
+def test_decode_append_8bit_equals_two_calls(gpu_lib, dtype, grow, part):
+    """fp8 / int8: the fused step writes the new token inside the decode
+    launch (the wave owning the request's last tile) and must leave exactly
+    the codes and scales of kv_append, and give exactly the output of
+    kv_append + paged_attention_decode.  New tokens scaled by `grow`: x8
+    makes most tiles' scales grow, so their older codes are re-encoded; x1e-3
+    keeps every scale."""
+    import synth
+    fused, appends = _case(dtype, 8, 128, 32, seed=38)
+    twin, _ = _case(dtype, 8, 128, 32, seed=38)
+    B = len(FINAL)
+    slots_f = fused.pool.batch_reserve(fused.table, fused.lens, appends.astype(np.int32))
+    slots_t = twin.pool.batch_reserve(twin.table, twin.lens, appends.astype(np.int32))
+    assert np.array_equal(slots_f, slots_t) and np.array_equal(fused.table, twin.table)
+    slots = np.full(B, -1, np.int32)
+    slots[appends] = slots_f
+    rng = synth.streams(71)
+    k = synth.normal_bf16_bits(rng["append"], (B, 8, 128))
+    v = synth.normal_bf16_bits(rng["append"], (B, 8, 128))
+    if grow != 1.0:
+        scale_bits = lambda b: synth.f32_to_bf16_bits(
+            ((b.astype(np.uint32) << 16).view(np.float32) * np.float32(grow)).astype(np.float32))
+        k, v = scale_bits(k), scale_bits(v)
+    dk, dv, ds = to_dev_bits(k, "bf16"), to_dev_bits(v, "bf16"), torch.from_numpy(slots).to(DEV)
+    for c in (fused, twin):
+        c.sync_tables()
+    max_ctx = int(fused.lens.max())
+    q = to_dev_bits(fused.q, "bf16")
+    out_f = fused.pool.decode_append(0, q, dk, dv, ds, fused.d_table, fused.d_lens, max_ctx,
+                                     1.0 / math.sqrt(128), part)
+    twin.pool.append(0, dk[torch.from_numpy(np.nonzero(appends)[0]).to(DEV)],
+                     dv[torch.from_numpy(np.nonzero(appends)[0]).to(DEV)],
+                     torch.from_numpy(slots_t).to(DEV))
+    out_t = twin.pool.decode(0, q, twin.d_table, twin.d_lens, max_ctx, 1.0 / math.sqrt(128), part)
+    torch.cuda.synchronize()
+    for name in ("k_cache", "v_cache", "k_scale", "v_scale"):
+        a, b = getattr(fused.pool, name), getattr(twin.pool, name)
+        assert torch.equal(a.view(torch.uint8) if a.dtype != torch.float32 else a.view(torch.int32),
+                           b.view(torch.uint8) if b.dtype != torch.float32 else b.view(torch.int32)), name
+    assert torch.equal(out_f.view(torch.int16), out_t.view(torch.int16)), "fused output differs from two calls"
+    grew = int(np.sum(fused.pool.k_scale.cpu().numpy() != 0))
+    log(f"{dtype} x{grow:g} part {part}: fused step equals kv_append + decode bit for bit ({grew} K scales set)")
+
+
 def test_decode_append_argument_errors(gpu_lib):
     import paged_kv_cache_271_amd as pk
     c, _ = _case("bf16", 2, 64, 4, seed=39)
