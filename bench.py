@@ -46,11 +46,61 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix peak of MI355X
 
 
 def event_every(steps):
-    """Bracket every timed step's call with events up to 256 steps, else every
-    (steps // 256)-th step: at least 256 bracketed calls on long runs, all of
-    them on short ones.  Events are created without the system-scope fence
-    (TimingEvent), so recording them costs the steps nothing measurable."""
+    """Per-call brackets (CallTimer(every=...)): every timed call up to 256
+    steps, else every (steps // 256)-th."""
     return max(1, steps // 256)
+
+
+class CallTimer:
+    """HIP events on the launch stream around the timed calls.
+
+    Runs of back-to-back calls (nothing else on the stream between them) are
+    bracketed as a whole, two events per run, so no event sits between two
+    calls: each event is a packet the command processor handles between
+    kernels, a few microseconds per pair, which per-call brackets would add to
+    every step.  A run's time per call is its elapsed time over its calls,
+    launch gaps included.  `new_run(j)` is true for a step whose call follows
+    other work on the stream (a host upload); it starts a new run.  With
+    `every`, every `every`-th call is bracketed alone instead (for steps with
+    another kernel before the timed call)."""
+
+    def __init__(self, stream, steps, new_run=None, every=None):
+        self.stream = stream
+        self.begin = [None] * steps
+        self.end = [None] * steps
+        self.runs = []
+        if every is not None:
+            groups = [[j] for j in range(0, steps, every)]
+        else:
+            groups, j = [], 0
+            while j < steps:
+                k = j + 1
+                while k < steps and not (new_run is not None and new_run(k)):
+                    k += 1
+                groups.append(list(range(j, k)))
+                j = k
+        for g in groups:
+            b, e = TimingEvent(), TimingEvent()
+            self.begin[g[0]] = b
+            self.end[g[-1]] = e
+            self.runs.append((b, e, g))
+
+    def before(self, j):
+        if self.begin[j] is not None:
+            self.begin[j].record(self.stream)
+
+    def after(self, j):
+        if self.end[j] is not None:
+            self.end[j].record(self.stream)
+
+    def results(self, per_step_work):
+        """(ms per call, work per call, calls) for every bracket."""
+        ms = np.array([b.elapsed_ms(e) / len(g) for b, e, g in self.runs])
+        work = np.array([float(np.mean([per_step_work[j] for j in g])) for _, _, g in self.runs])
+        n = np.array([len(g) for _, _, g in self.runs])
+        return ms, work, n
+
+
 DEFAULT_LAYERS = {"llama3_8b": 32, "llama3_70b_long": 8, "fp8": 16, "int8": 16, "llama3_8b_window": 4}
 DEFAULT_SEED = {"llama3_8b": 2, "llama3_70b_long": 3, "fp8": 5, "int8": 5, "prefix_churn": 4, "cow_fork": 6,
                 "llama3_8b_window": 7, "prefill": 8, "ctx_sweep": 2}
@@ -61,7 +111,7 @@ DEFAULT_SEED = {"llama3_8b": 2, "llama3_70b_long": 3, "fp8": 5, "int8": 5, "pref
 # calibration there (fetch x2, write x1).  They hold for the kernel source they
 # were taken on, identified by its SHA-256; any other source reports null.
 TRAFFIC_SOURCE = "paged_kv_cache_271_amd/csrc/decode.hip"
-TRAFFIC_SHA256 = "400ecce857db5e97c2caa3d9726547a5879fbed2b1e4c786e2fc54025cf5c4a5"
+TRAFFIC_SHA256 = "f22574467dc1829e4398cd0e8e2652ad6f267159c91bc911c9112009a5e16d31"
 TRAFFIC_BYTES = {"llama3_8b": 603_151_152, "fp8": 1_254_006_063, "llama3_70b_long": 1_359_456_336,
                  "int8": 1_252_225_612, "llama3_8b_window": 1_106_833_558}
 # The same per launch of prefill_kernel and of block_copy_kernel, from
@@ -280,14 +330,14 @@ def decode_workload(args, torch, synth, pk, dev, spec=None, layers=0):
     # 8-bit steps run the append kernel and the windowed decode in one call
     two_calls = args.two_calls
 
-    def step(i, ev=None):
+    def step(i, timer=None, j=0):
         s, r = divmod(i, L)
         if r == 0:
             host_reserve()
         if two_calls:
             pool.append(r, k_new[s, r], v_new[s, r], d_slots)
-        if ev is not None:
-            ev[0].record(stream)
+        if timer is not None:
+            timer.before(j)
         if window and two_calls:
             pool.decode_window(r, q_all[s, r], d_table, d_lens, state["max_ctx"], scale, sink, window,
                                args.partition, out=out, workspace=ws)
@@ -301,8 +351,8 @@ def decode_workload(args, torch, synth, pk, dev, spec=None, layers=0):
         else:
             pool.decode_append(r, q_all[s, r], k_new[s, r], v_new[s, r], d_slots, d_table, d_lens,
                                state["max_ctx"], scale, args.partition, out=out, workspace=ws)
-        if ev is not None:
-            ev[1].record(stream)
+        if timer is not None:
+            timer.after(j)
         return state["kv"]
 
     if args.copy_calibration:
@@ -312,22 +362,24 @@ def decode_workload(args, torch, synth, pk, dev, spec=None, layers=0):
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
 
-    # events bracket the decode call of the timed steps (event_every)
-    every = event_every(args.steps)
-    events = [(TimingEvent(), TimingEvent()) if j % every == 0 else None for j in range(args.steps)]
+    # events bracket the timed calls: runs of fused calls between host
+    # uploads, or (two calls per step) the decode call alone
+    if two_calls:
+        timer = CallTimer(stream, args.steps, every=event_every(args.steps))
+    else:
+        timer = CallTimer(stream, args.steps, new_run=lambda j: (args.warmup + j) % L == 0)
     per_step_kv = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for j in range(args.steps):
-        per_step_kv.append(step(args.warmup + j, events[j]))
+        per_step_kv.append(step(args.warmup + j, timer, j))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     # the device table must name the host's block at every page a decode reads
     nb_now = (lens.astype(np.int64) + 15) // 16
     live = (table >= 0) & (np.arange(MB)[None, :] < nb_now[:, None])
     assert np.array_equal(d_table.cpu().numpy()[live], table[live]), "device block table out of date"
-    dec_ms = np.array([e[0].elapsed_ms(e[1]) for e in events if e is not None])
-    dec_kv = np.array([per_step_kv[j] for j in range(args.steps) if events[j] is not None], float)
+    dec_ms, dec_kv, dec_n = timer.results(per_step_kv)
 
     probe = None
     if spec is None and not window and (H % 4) == 0 and h_q // H <= 16:
@@ -346,7 +398,8 @@ def decode_workload(args, torch, synth, pk, dev, spec=None, layers=0):
                                                          "paged_attention_decode")
                 + ("" if two_calls else "_append"),
     }
-    return dict(wall=wall, kv_total=float(sum(per_step_kv)), dec_ms=dec_ms, dec_kv=dec_kv, probe=probe,
+    return dict(wall=wall, kv_total=float(sum(per_step_kv)), dec_ms=dec_ms, dec_kv=dec_kv, dec_n=dec_n,
+                probe=probe,
                 config=config, cpu=cpu, traffic=measured_traffic(name, args.two_calls), dtype={"fp8": "fp8-e4m3 K/V, bf16 q", "int8": "int8 K/V, bf16 q"}.get(dtype, "bf16"),
                 kernel=("paged_attention_decode_window" if window else "paged_attention_decode")
                 + ("" if two_calls else "_append") + " call (decode_stream_kernel, merging its split pieces "
@@ -371,8 +424,8 @@ def ctx_sweep_workload(args, torch, synth, pk, dev):
         per_layer = B * c * H * D * 2 * 2
         layers = max(2, -(-4 * 10 ** 9 // per_layer))  # >= 4 GB of pool: every step reads cold lines
         r = decode_workload(args, torch, synth, pk, dev, spec=spec, layers=layers)
-        call_us = float(r["dec_ms"].mean()) * 1e3
-        kv = float(r["dec_kv"].mean())
+        call_us = float(np.average(r["dec_ms"], weights=r["dec_n"])) * 1e3
+        kv = float(np.average(r["dec_kv"], weights=r["dec_n"]))
         pts.append((c, kv, call_us, r["wall"] / args.steps * 1e6))
         log(f"ctx {c}: {kv / 1e6:.1f} MB, call {call_us:.1f} us ({kv / call_us / 1e3:.0f} GB/s), "
             f"step {pts[-1][3]:.1f} us")
@@ -393,7 +446,7 @@ def ctx_sweep_workload(args, torch, synth, pk, dev):
               "us_per_step_points": [round(p[3], 2) for p in pts],
               "fit_fixed_us": round(float(icept), 2), "fit_rate_gbs": round(rate, 1), "fit_r2": round(r2, 6)}
     return dict(wall=last["wall"], kv_total=last["kv_total"], dec_ms=last["dec_ms"], dec_kv=last["dec_kv"],
-                config=config, cpu=None, traffic=None, traffic_note="HBM counters not taken for this sweep",
+                dec_n=last["dec_n"], config=config, cpu=None, traffic=None, traffic_note="HBM counters not taken for this sweep",
                 dtype="bf16", value=rate, metric="paged decode call: streaming rate of the affine fit "
                 "over context length (GB/s), Llama-3-8B shape",
                 kernel="paged_attention_decode_append call at the longest context (decode_stream_kernel + "
@@ -461,7 +514,7 @@ def cow_fork_workload(args, torch, synth, pk, dev):
     stream = torch.cuda.current_stream()
     ones = np.ones(B, np.int32)
 
-    def step(ev=None):
+    def step(timer=None, j=0):
         ctable, clen = ptable.copy(), plen.copy()
         pool.retain_n(ctable.reshape(-1))           # the fork
         _, src, dst = pool.batch_reserve_cow(ctable, clen, ones)
@@ -469,11 +522,11 @@ def cow_fork_workload(args, torch, synth, pk, dev):
         pn = pinned.numpy()
         pn[:B], pn[B:] = src, dst
         d_pairs.copy_(pinned, non_blocking=True)
-        if ev is not None:
-            ev[0].record(stream)
+        if timer is not None:
+            timer.before(j)
         pool.block_copy(d_pairs[:B], d_pairs[B:])
-        if ev is not None:
-            ev[1].record(stream)
+        if timer is not None:
+            timer.after(j)
         pool.release_n(ctable.reshape(-1))          # the children retire
         return moved
 
@@ -482,26 +535,22 @@ def cow_fork_workload(args, torch, synth, pk, dev):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    every = event_every(args.steps)
-    events = [(TimingEvent(), TimingEvent()) if j % every == 0 else None for j in range(args.steps)]
+    # every copy follows its step's upload of the page pairs: bracketed alone
+    timer = CallTimer(stream, args.steps, every=event_every(args.steps))
     t0 = time.perf_counter()
     total = 0
     for j in range(args.steps):
-        total += step(events[j])
+        total += step(timer, j)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # the device table must name the host's block at every page a decode reads
-    nb_now = (lens.astype(np.int64) + 15) // 16
-    live = (table >= 0) & (np.arange(MB)[None, :] < nb_now[:, None])
-    assert np.array_equal(d_table.cpu().numpy()[live], table[live]), "device block table out of date"
-    dec_ms = np.array([e[0].elapsed_ms(e[1]) for e in events if e is not None])
+    dec_ms, dec_kv, dec_n = timer.results([moved] * args.steps)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cow_cpu_baseline(args, rng_seed=args.seed, B=B, L=L, H=H, D=D, N=N)
     config = {"workload": "cow_fork_page_copy", "forks_per_step": B, "layers": L, "h_kv": H, "head_dim": D,
               "cache_dtype": "bf16", "page_bytes_per_layer_kv": 2 * page_bytes,
               "bytes_moved_per_step": moved}
-    return dict(wall=wall, kv_total=float(total), dec_ms=dec_ms, dec_kv=np.full(len(dec_ms), float(moved)),
+    return dict(wall=wall, kv_total=float(total), dec_ms=dec_ms, dec_kv=dec_kv, dec_n=dec_n,
                 config=config, cpu=cpu, traffic=measured_traffic("cow_fork"),
                 traffic_note="HBM bytes read + written per block_copy_kernel launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, "
                              "copy-calibrated); null if the kernel source changed", dtype="bf16",
@@ -537,30 +586,26 @@ def prefill_workload(args, torch, synth, pk, dev):
     scale = 1.0 / math.sqrt(D)
     stream = torch.cuda.current_stream()
 
-    def step(i, ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def step(i, timer=None, j=0):
+        if timer is not None:
+            timer.before(j)
         pool.prefill(i % L, q_all[i % L], d_table, d_lens, d_qs, P, P, scale, out=out)
-        if ev is not None:
-            ev[1].record(stream)
+        if timer is not None:
+            timer.after(j)
 
     if args.copy_calibration:
         copy_calibration(torch, dev)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    every = event_every(args.steps)
-    events = [(TimingEvent(), TimingEvent()) if j % every == 0 else None for j in range(args.steps)]
+    # back-to-back prefill calls: one run
+    timer = CallTimer(stream, args.steps)
     t0 = time.perf_counter()
     for j in range(args.steps):
-        step(args.warmup + j, events[j])
+        step(args.warmup + j, timer, j)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # the device table must name the host's block at every page a decode reads
-    nb_now = (lens.astype(np.int64) + 15) // 16
-    live = (table >= 0) & (np.arange(MB)[None, :] < nb_now[:, None])
-    assert np.array_equal(d_table.cpu().numpy()[live], table[live]), "device block table out of date"
-    dec_ms = np.array([e[0].elapsed_ms(e[1]) for e in events if e is not None])
+    dec_ms, dec_kv, dec_n = timer.results([flops] * args.steps)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = prefill_cpu_baseline(args, torch, synth, dev, q_all[(args.warmup + args.steps - 1) % L],
@@ -568,7 +613,7 @@ def prefill_workload(args, torch, synth, pk, dev):
     config = {"workload": "llama3_8b_prefill_layer", "batch": B, "new_tokens": P, "h_q": h_q, "h_kv": H,
               "head_dim": D, "cache_dtype": "bf16", "layers_in_pool": L, "flop_per_step": flops}
     return dict(wall=wall, kv_total=float(flops) * args.steps, dec_ms=dec_ms,
-                dec_kv=np.full(len(dec_ms), float(flops)), config=config, cpu=cpu, traffic=measured_traffic("prefill"),
+                dec_kv=dec_kv, dec_n=dec_n, config=config, cpu=cpu, traffic=measured_traffic("prefill"),
                 traffic_note="HBM bytes read + written per prefill_kernel launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, "
                              "copy-calibrated); null if the kernel source changed", dtype="bf16",
                 kernel="paged_attention_prefill call (prefill_kernel)",
@@ -614,13 +659,15 @@ def main():
     log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step, {value:.0f} {unit}")
     roofline = None
     if r["dec_ms"] is not None:
-        dec_mean_s = float(r["dec_ms"].mean()) / 1e3
+        w_n = r["dec_n"]
+        dec_mean_s = float(np.average(r["dec_ms"], weights=w_n)) / 1e3
         dec_p50_s = float(np.median(r["dec_ms"])) / 1e3
-        achieved = float(r["dec_kv"].mean()) / dec_mean_s / unit_scale
-        achieved_p50 = float(r["dec_kv"].mean()) / dec_p50_s / unit_scale
-        log(f"timed call {dec_mean_s * 1e6:.1f} us mean over {len(r['dec_ms'])} calls "
-            f"(p10 {np.percentile(r['dec_ms'], 10) * 1e3:.1f}, p90 {np.percentile(r['dec_ms'], 90) * 1e3:.1f}), "
-            f"{achieved:.0f} {unit}")
+        kv_call = float(np.average(r["dec_kv"], weights=w_n))
+        achieved = kv_call / dec_mean_s / unit_scale
+        achieved_p50 = kv_call / dec_p50_s / unit_scale
+        log(f"timed call {dec_mean_s * 1e6:.1f} us mean over {int(w_n.sum())} calls in {len(w_n)} brackets "
+            f"(bracket p10 {np.percentile(r['dec_ms'], 10) * 1e3:.1f}, "
+            f"p90 {np.percentile(r['dec_ms'], 90) * 1e3:.1f}), {achieved:.0f} {unit}")
         roofline = {
             "bound": r.get("bound", "hbm"),
             "kernel": r["kernel"],
@@ -628,15 +675,20 @@ def main():
             "peak": peak,
             "unit": unit,
             "frac": round(achieved / peak, 4),
-            "frac_median_call": round(achieved_p50 / peak, 4),
+            "frac_median_bracket": round(achieved_p50 / peak, 4),
             "traffic": r.get("traffic"),
             "traffic_note": r.get("traffic_note", "HBM bytes read + written per decode_stream_kernel "
                                   "launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated); null if "
                                   "the kernel source changed"),
             "stream_copy_gbs": stream_copy_gbs(torch, dev),
             "us_per_call": round(dec_mean_s * 1e6, 2),
-            "us_per_call_p10_p50_p90": [round(float(np.percentile(r["dec_ms"], x)) * 1e3, 2) for x in (10, 50, 90)],
-            "calls_timed": int(len(r["dec_ms"])),
+            "us_per_call_p10_p50_p90_bracket": [round(float(np.percentile(r["dec_ms"], x)) * 1e3, 2)
+                                                for x in (10, 50, 90)],
+            "calls_timed": int(w_n.sum()),
+            "brackets": int(len(w_n)),
+            "bracket_note": "HIP events on the launch stream around runs of back-to-back calls (a run ends at a "
+                            "host upload or, for two calls per step, each decode call alone); time per call = "
+                            "run time / calls, launch gaps included",
         }
         if r.get("probe"):
             pr = r["probe"]

@@ -776,9 +776,11 @@ __device__ __forceinline__ void merge_row_pieces(uint16_t* __restrict__ out, int
 // ([H][D] each), at new_slots[b] (-1: none), which is the slot of its
 // position ctx - 1.  The attention then reads positions < ctx - 1 from the
 // cache and takes the last one from k_new / v_new (add_token, in the segment
-// that ends the request), so no wave reads the slot being written; threads of
-// the same launch store the token into the cache while the block counts are
-// summed.
+// that ends the request); threads of the same launch store the token into
+// the cache while the block counts are summed.  The slot's bytes may still be
+// loaded with the rest of its tile while those stores land, unordered, but
+// that lane is past the cached range and masked, so neither the old nor the
+// new bytes reach the result.  8-bit caches: see the Q8 append branch.
 //
 // WIN: a sliding window of `window` tokens plus `sink` sink tokens; units
 // run over the pages each request reads (visited_pages), so pages outside
