@@ -9,7 +9,11 @@ as fp8 or int8 with a scale):
   the scale is exactly 1, carrying every finite bf16 value in range (and NaN
   for fp8): each code must equal the oracle's encoder byte for byte;
 * fp8 end to end: the fp8 workload's batch without outliers against the
-  oracle on the inputs before quantisation, the 6e-2 bound."""
+  oracle on the inputs before quantisation, the 6e-2 bound;
+* decode steps: the last 48 tokens of every request written one per fused
+  step, so a tile's scale grows several times and its older codes are
+  re-encoded each time; cache bit-exact against the oracle's pool every step,
+  and the final decode within the same bounds as above."""
 
 import math
 
@@ -142,3 +146,36 @@ def test_fp8_end_to_end_without_outliers(gpu_lib):
             log(f"  request {b} (ctx {int(lens[b])}) partition {part}: max|kernel - oracle(inputs)| {err:.3e}")
             assert np.all(np.isfinite(o[b])) and err <= 6e-2
     log(f"fp8 end to end, no outliers: worst {worst:.3e} (bound 6e-2)")
+
+
+@pytest.mark.parametrize("dtype", ["fp8", "int8"])
+def test_end_to_end_after_decode_steps(gpu_lib, dtype):
+    """Requests of the fp8 workload's shape (h_q 32, h_kv 8, d 128; 1k-2k
+    tokens), N(0,1) values without outliers, whose last 48 tokens arrive one
+    per fused decode step.  Each single-token append may grow its tile's scale
+    and re-encode the tile's older codes from their decoded values, so those
+    codes are rounded more than once.  Every step the cache must equal the
+    oracle pool's bit for bit (checked inside decode_append_step); after the
+    last step the output must match the oracle on the stored codes (the
+    dtype's tolerance) and stay within 6e-2 of the oracle on the inputs before
+    quantisation."""
+    w = synth.WORKLOADS[dtype]
+    rng = synth.streams(71)
+    B, steps = 12, 48
+    lens = synth.uniform_contexts(rng["contexts"], B, 1024, 2048)
+    N = int(sum(oracle.blocks_for(int(n) + steps, 16) for n in lens))
+    c = Case(dtype, w["h_kv"], w["head_dim"], w["h_q"], lens, num_blocks=N,
+             order=synth.permutation(rng["free_order"], N), seed=72, max_blocks=oracle.blocks_for(2048 + steps, 16),
+             mirror=True)
+    o = None
+    for i in range(steps):
+        o = c.decode_append_step(seed=1000 + i)
+    ref_codes = c.oracle(dequant=True)
+    ref_inputs = c.oracle(dequant=False)
+    worst = 0.0
+    for b in range(B):
+        assert_close(o[b], ref_codes[b], c.tol_key, f"request {b} against the stored codes")
+        err = float(np.max(np.abs(o[b] - ref_inputs[b])))
+        worst = max(worst, err)
+        assert np.all(np.isfinite(o[b])) and err <= 6e-2, f"request {b}: {err:.3e} against the inputs"
+    log(f"{dtype} after {steps} decode steps: worst |kernel - oracle(inputs)| {worst:.3e} (bound 6e-2)")
