@@ -40,12 +40,14 @@ namespace {
 
 constexpr int kBS = kBlockSize;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazyLog2 = 8.0f;  // headroom of the decode's lazy running maximum (log2 units)
 
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef _Float16 f16x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
 typedef _Float16 f16x2 __attribute__((__vector_size__(2 * sizeof(_Float16))));
 typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef float f32x2 __attribute__((__vector_size__(2 * sizeof(float))));
 typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
 typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
 
@@ -56,7 +58,11 @@ __device__ inline uint32_t f2bf_bits(float x) {
   return uint32_t(__builtin_bit_cast(uint16_t, h));
 }
 
-__device__ inline uint32_t pack_bf16(float lo, float hi) { return f2bf_bits(lo) | (f2bf_bits(hi) << 16); }
+// Two floats -> two bf16 (round to nearest even) in one dword: one
+// v_cvt_pk_bf16_f32.
+__device__ inline uint32_t pack_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
 
 // Four E4M3 codes (one dword) -> four bf16 (two dwords), exact.
 __device__ inline u32x2 fp8x4_to_bf16x4(uint32_t w) {
@@ -332,9 +338,7 @@ __device__ __forceinline__ void run_segment(WaveState<D>& st, const uint8_t* __r
   int32_t tV = trow[min(j0 + vb_rel, jlast)];
   for (int cb = j0; cb < j1; cb += NB) {
     progress_prio(done0 + (cb - j0), total);
-    const int bK = cb + kb_rel;
     const int bV = cb + vb_rel;
-    const bool vK = bK < j1;
     const bool vV = bV < j1;
     const int64_t pK = tK;
     const int64_t pV = tV;
@@ -344,7 +348,10 @@ __device__ __forceinline__ void run_segment(WaveState<D>& st, const uint8_t* __r
     const uint8_t* ktile = kc + (pK * H + g) * tile_bytes;
     const uint8_t* vtile = vc + (pV * H + g) * tile_bytes;
 
-    // ---- loads: K rows for the score MFMAs, this lane's V slice
+    // ---- loads: K rows for the score MFMAs, this lane's V slice.  A block
+    // past the segment (an odd last step) is loaded from the clamped table
+    // entry like any other: its scores are masked to -inf and its V zeroed
+    // below, so its bytes never count, and no load needs a lane mask.
     u32x4 kop[NB][KK];
     u32x4 vraw[T8];
 #pragma unroll
@@ -352,19 +359,12 @@ __device__ __forceinline__ void run_segment(WaveState<D>& st, const uint8_t* __r
       const int ktok = 8 * ((r >> 2) & 1) + 4 * j + (r & 3);
       if constexpr (!Q8) {
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          u32x4 v = {0, 0, 0, 0};
-          if (vK) v = ld16(ktile + (ktok * D + 32 * kk + 8 * grp) * 2);
-          kop[j][kk] = v;
-        }
+        for (int kk = 0; kk < KK; ++kk) kop[j][kk] = ld16(ktile + (ktok * D + 32 * kk + 8 * grp) * 2);
       } else {
         constexpr int NSEG = D / 64;  // 16-byte pieces of a lane's D/4 codes
         u32x4 seg[NSEG];
 #pragma unroll
-        for (int s = 0; s < NSEG; ++s) {
-          seg[s] = u32x4{0, 0, 0, 0};
-          if (vK) seg[s] = ld16(ktile + ktok * D + (D / 4) * grp + 16 * s);
-        }
+        for (int s = 0; s < NSEG; ++s) seg[s] = ld16(ktile + ktok * D + (D / 4) * grp + 16 * s);
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           const u32x4& sv = seg[kk / 2];
@@ -377,12 +377,9 @@ __device__ __forceinline__ void run_segment(WaveState<D>& st, const uint8_t* __r
 #pragma unroll
     for (int t = 0; t < T8; ++t) {
       if constexpr (!Q8) {
-        u32x4 v = {0, 0, 0, 0};
-        if (vV) v = ld16(vtile + ((16 * t + r) * kBS + vtok) * 2);
-        vraw[t] = v;
+        vraw[t] = ld16(vtile + ((16 * t + r) * kBS + vtok) * 2);
       } else {
-        u32x2 v = {0, 0};
-        if (vV) v = *reinterpret_cast<const u32x2*>(vtile + (16 * t + r) * kBS + vtok);
+        const u32x2 v = *reinterpret_cast<const u32x2*>(vtile + (16 * t + r) * kBS + vtok);
         vraw[t] = u32x4{v[0], v[1], 0, 0};
       }
     }
@@ -401,13 +398,11 @@ __device__ __forceinline__ void run_segment(WaveState<D>& st, const uint8_t* __r
     float kfac = scale_log2;
     float vfac = 1.0f;
     if constexpr (Q8) {
-      vfac = 0.0f;  // tiles past the segment: their weights are zero anyway
-      if (vV) {
-        kfac *= kscale[pV * H + g];
-        vfac = vscale[pV * H + g];
-      }
+      kfac *= kscale[pV * H + g];
+      vfac = vV ? vscale[pV * H + g] : 0.0f;  // tiles past the segment: zero weights anyway
     }
     float vs_fold = 1.0f;  // int8: acc rescale for a larger V-scale reference
+    bool vs_grew = false;
     if constexpr (QT == kQInt8) {
       kfac *= qscale_inv;
       // the step's two tiles: lane groups 0-1 hold one, 2-3 the other
@@ -417,72 +412,120 @@ __device__ __forceinline__ void run_segment(WaveState<D>& st, const uint8_t* __r
         vs_fold = st.vs * inv;
         vfac *= inv;
       }
+      vs_grew = vs_new != st.vs;
       st.vs = vs_new;
     }
-    const int valid = vV ? min(kBS, ctx - bV * kBS) - vtok : 0;  // valid among the lane's 8
-    uint32_t keep = 0;  // WIN: bit e set when token vtok + e of block bV is read
-    if constexpr (WIN) {
-      const int p0 = bV * kBS + vtok;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int p = p0 + e;
-        keep |= uint32_t(vV && p < ctx && (p < sink || p >= win_lo)) << e;
-      }
-    }
+    // A step whose two blocks lie inside the segment and whose 32 positions
+    // are all read (below ctx; WIN: all sinks or all inside the window)
+    // needs no mask: the common case, one wave-uniform test.
+    bool full = cb + 1 < j1 && (cb + NB) * kBS <= ctx;
+    if constexpr (WIN) full = full && ((cb + NB) * kBS <= sink || cb * kBS >= win_lo);
+    int valid = 8;      // valid among the lane's 8 tokens (not WIN)
+    uint32_t keep = 0xFFu;  // WIN: bit e set when token vtok + e of block bV is read
     float mx = -INFINITY;
+    if (full) {
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
+      for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool ok = WIN ? ((keep >> (4 * j + i)) & 1u) != 0 : 4 * j + i < valid;
-        const float s = ok ? S[j][i] * kfac : -INFINITY;
-        S[j][i] = s;
-        mx = fmaxf(mx, s);
+        for (int i = 0; i < 4; ++i) {
+          S[j][i] *= kfac;
+          mx = fmaxf(mx, S[j][i]);
+        }
+    } else {
+      valid = vV ? min(kBS, ctx - bV * kBS) - vtok : 0;
+      if constexpr (WIN) {
+        keep = 0;
+        const int p0 = bV * kBS + vtok;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int p = p0 + e;
+          keep |= uint32_t(vV && p < ctx && (p < sink || p >= win_lo)) << e;
+        }
       }
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool ok = WIN ? ((keep >> (4 * j + i)) & 1u) != 0 : 4 * j + i < valid;
+          const float sv = ok ? S[j][i] * kfac : -INFINITY;
+          S[j][i] = sv;
+          mx = fmaxf(mx, sv);
+        }
+    }
     mx = wave_max16(mx);
-    const float m_new = fmaxf(st.m, mx);  // finite: the step holds a valid token
-    // WIN with a fused append: a step may hold no token read yet (a window of
-    // one whose only position is the new token); take weights against 0 then,
-    // which leaves the state as it was
-    const float m_ref = WIN && m_new == -INFINITY ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(st.m - m_ref);
+    // Lazy maximum: the running maximum moves (and the accumulators are
+    // rescaled) only when a step's maximum exceeds it by more than 2^8 in a
+    // lane of the wave; otherwise the weights are formed against the stale
+    // maximum and stay below 2^8.  The state (m, l, acc) is the same softmax
+    // for any m, which is all the finish and the piece merge assume.
+    if (__builtin_amdgcn_ballot_w64(mx > st.m + kLazyLog2 || vs_grew) != 0) {
+      const float m_new = fmaxf(st.m, mx);
+      // WIN with a fused append: a row may have read no token yet (a window
+      // of one whose only position is the new token); its state stays empty
+      const float m_ref = WIN && m_new == -INFINITY ? 0.0f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(st.m - m_ref);
+      st.l *= alpha;
+      st.m = m_new;
+      const float afac = QT == kQInt8 ? alpha * vs_fold : alpha;
+#pragma unroll
+      for (int t = 0; t < T8; ++t) st.acc[t] *= afac;
+    }
+    const float m_use = WIN && st.m == -INFINITY ? 0.0f : st.m;
     float psum = 0.0f;
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float e = __builtin_amdgcn_exp2f(S[j][i] - m_ref);
+        const float e = __builtin_amdgcn_exp2f(S[j][i] - m_use);
         S[j][i] = e;
         psum += e;
       }
-    st.l = st.l * alpha + psum;
-    st.m = m_new;
-    const float afac = QT == kQInt8 ? alpha * vs_fold : alpha;
-#pragma unroll
-    for (int t = 0; t < T8; ++t) st.acc[t] *= afac;
+    st.l += psum;
 
     // ---- weighted sum of V: k-slot e is token vtok + e of block bV
     const f32x4 lo = S[0] * vfac, hi = S[1] * vfac;
     const u32x4 pop = {pack_op<QT>(lo[0], lo[1]), pack_op<QT>(lo[2], lo[3]), pack_op<QT>(hi[0], hi[1]),
                        pack_op<QT>(hi[2], hi[3])};
-    const int vh = min(max(valid, 0), 8);
-#pragma unroll
-    for (int t = 0; t < T8; ++t) {
-      u32x4 v;
+    auto v_op = [&](int t) -> u32x4 {  // this lane's V slice t as MFMA operand pairs
       if constexpr (Q8) {
         const u32x2 a = q8x4_to_op<QT>(vraw[t][0]);
         const u32x2 c2 = q8x4_to_op<QT>(vraw[t][1]);
-        v = u32x4{a[0], a[1], c2[0], c2[1]};
+        return u32x4{a[0], a[1], c2[0], c2[1]};
       } else {
-        v = vraw[t];
+        return vraw[t];
       }
-      if constexpr (WIN) {
-        if (keep != 0xFFu) v = mask_bits(v, keep);  // stale slots, or outside the window
+    };
+    // Stale or poisoned slots past the context (WIN: outside the window)
+    // are zeroed before their weight-zero product: one mask for the step,
+    // applied to the raw registers (8-bit codes: per byte, code 0 is +0);
+    // a full step skips it.
+    if (!full) {
+      const int vh = min(max(valid, 0), 8);
+      const uint32_t k8 = WIN ? keep : (1u << vh) - 1u;
+      if constexpr (Q8) {
+        uint32_t bm[2];
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          bm[w] = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) bm[w] |= ((k8 >> (4 * w + e)) & 1u ? 0xFFu : 0u) << (8 * e);
+        }
+#pragma unroll
+        for (int t = 0; t < T8; ++t) {
+          vraw[t][0] &= bm[0];
+          vraw[t][1] &= bm[1];
+        }
       } else {
-        if (vh < 8) v = mask_tail(v, vh);  // stale or poisoned slots past the context
+        u32x4 vm;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          vm[w] = ((k8 >> (2 * w)) & 1u ? 0x0000FFFFu : 0u) | ((k8 >> (2 * w + 1)) & 1u ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int t = 0; t < T8; ++t) vraw[t] &= vm;
       }
-      st.acc[t] = mfma_op<QT>(v, pop, st.acc[t]);
     }
+#pragma unroll
+    for (int t = 0; t < T8; ++t) st.acc[t] = mfma_op<QT>(v_op(t), pop, st.acc[t]);
   }
 }
 
