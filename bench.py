@@ -111,9 +111,9 @@ DEFAULT_SEED = {"llama3_8b": 2, "llama3_70b_long": 3, "fp8": 5, "int8": 5, "pref
 # calibration there (fetch x2, write x1).  They hold for the kernel source they
 # were taken on, identified by its SHA-256; any other source reports null.
 TRAFFIC_SOURCE = "paged_kv_cache_271_amd/csrc/decode.hip"
-TRAFFIC_SHA256 = "f22574467dc1829e4398cd0e8e2652ad6f267159c91bc911c9112009a5e16d31"
-TRAFFIC_BYTES = {"llama3_8b": 603_151_152, "fp8": 1_254_006_063, "llama3_70b_long": 1_359_456_336,
-                 "int8": 1_252_225_612, "llama3_8b_window": 1_106_833_558}
+TRAFFIC_SHA256 = "2be2b88d0aa4bff65b3186bf952d4e7cc5d9f42f8ada30a3f0345894e17fdf1f"
+TRAFFIC_BYTES = {"llama3_8b": 608_928_646, "fp8": 1_255_802_116, "llama3_70b_long": 1_371_137_507,
+                 "int8": 1_252_429_640, "llama3_8b_window": 1_106_530_099}
 # The same per launch of prefill_kernel and of block_copy_kernel, from
 # profiles/prefill_llama3_8b_counters.md and
 # profiles/block_copy_cow_fork_hbm_counters.md: (source, its SHA-256, bytes).
