@@ -119,7 +119,7 @@ TRAFFIC_BYTES = {"llama3_8b": 608_928_646, "fp8": 1_255_802_116, "llama3_70b_lon
 # profiles/block_copy_cow_fork_hbm_counters.md: (source, its SHA-256, bytes).
 TRAFFIC_OTHER = {
     "prefill": ("paged_kv_cache_271_amd/csrc/prefill.hip",
-                "40d38543edea2e06f68c0d6da0127566fc6313d02540da9c7573ea14264047d7", 433_608_499),
+                "b945496209c1d008c3440b9416689f144f3706c8279255c5525e13a420050de5", 400_594_330),
     "cow_fork": ("paged_kv_cache_271_amd/csrc/copy.hip",
                  "06367c5bcbf1b2856b1a3729463a1093d9928cc8dab6c0ca5b114bb07073ec79", 1_073_901_158),
 }

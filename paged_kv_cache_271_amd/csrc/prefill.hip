@@ -20,17 +20,20 @@
 // Lane group q of a 32-key block owns keys 8q..8q+7, which are exactly its 8
 // scores of each row, so the softmax needs no data movement.
 //
-// Keys stream in chunks of 64 (four pages).  Wave w copies page w of the next
-// chunk from HBM straight into LDS (global_load_lds_dwordx4, no registers)
-// while the workgroup computes on the current one: two LDS buffers, one
+// Keys stream in chunks of 32 (two pages), three workgroups per CU (three
+// waves per SIMD: 166 VGPRs, 40 KiB of LDS each).  Waves 0-1 copy the K
+// pages of a chunk, waves 2-3 its V pages, from HBM straight into LDS
+// (global_load_lds_dwordx4, no registers) while the workgroup computes on
+// the current chunk: three K buffers (K staged two chunks ahead, its copy
+// kept in flight across the barrier) and two V buffers (one ahead), one
 // barrier per chunk.  The copies place 16-byte granules with an XOR swizzle
 // so that the MFMA operand reads of every 16 lanes touch 16 different bank
-// groups.  Softmax per chunk (64 keys): the running row maximum only moves
-// when a chunk's maximum exceeds it by more than 2^8 (then the accumulators
-// are rescaled), otherwise the weights are formed against the stale maximum
-// and stay below 256, which changes no result beyond rounding.  The causal
-// mask is applied only on the chunks that reach a row's own position, and
-// the V rows past the context are zeroed in LDS on the request's last chunk
+// groups.  Softmax per chunk: the running row maximum only moves when a
+// chunk's maximum exceeds it by more than 2^8 (then the accumulators are
+// rescaled), otherwise the weights are formed against the stale maximum and
+// stay below 256, which changes no result beyond rounding.  The causal mask
+// is applied only on the chunks that reach a row's own position, and the V
+// rows past the context are zeroed in LDS on the request's last chunk
 // (unwritten slots may hold any bits).  Tiles with the most keys launch
 // first; the tiles of one (request, kv head) share an XCD when B * H is a
 // multiple of 8, so its K/V stays in that XCD's L2.
@@ -48,11 +51,14 @@ constexpr int kBS = kBlockSize;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kRT = 2;                 // 16-row MFMA tiles per wave
 constexpr int kRows = 4 * 16 * kRT;    // query rows per workgroup
-constexpr int kChunk = 64;             // keys per chunk: four pages, one per wave
+constexpr int kChunk = 32;             // keys per chunk: two pages; waves 0-1 copy K, 2-3 copy V
+constexpr int kKB = kChunk / 32;       // 32-key MFMA blocks per chunk
 constexpr float kSlack = 8.0f;         // log2 headroom of the running maximum
 // s_waitcnt immediates (vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 constexpr int kWaitAll = 0x0070;       // vmcnt(0) lgkmcnt(0)
 constexpr int kWaitLds = 0xC07F;       // lgkmcnt(0)
+template <int N>
+constexpr int kWaitVm = 0x0070 | N;     // vmcnt(N) lgkmcnt(0), N < 16
 constexpr int kXcds = 8;               // workgroup ids go round-robin over the XCDs
 constexpr int kPairGroup = 4;          // (request, kv head) pairs an XCD streams at a time
 
@@ -123,7 +129,7 @@ struct Tile {
   float m[kRT], l[kRT];
   int pos[kRT];
   uint32_t kaddr[KK], vaddr;  // LDS read offsets (elements) of this lane's operands
-  uint32_t ksrc[NI], vsrc[NI];  // element offsets within a page tile of this lane's copies
+  uint32_t csrc[NI];  // element offsets within a page tile of this lane's copies (K for waves 0-1, V for 2-3)
 };
 
 // Copy the K (or V) tiles of chunk `ci` (keys 64 ci .. 64 ci + 63): wave w
@@ -131,19 +137,19 @@ struct Tile {
 // context are masked and, for V, zeroed before use).
 template <int D>
 __device__ __forceinline__ void issue_tiles(uint16_t* buf, const uint16_t* cache, const uint32_t (&src)[Tile<D>::NI],
-                                            int ci, int nb, const int32_t* trow, int H, int g, int w) {
+                                            int ci, int nb, const int32_t* trow, int H, int g, int pg) {
   constexpr int PG = Tile<D>::PG;
-  const int page = min(ci * (kChunk / kBS) + w, nb - 1);
+  const int page = min(ci * (kChunk / kBS) + pg, nb - 1);
   const int64_t tile = (int64_t(trow[page]) * H + g) * kBS * D;
 #pragma unroll
-  for (int m = 0; m < Tile<D>::NI; ++m) copy_to_lds(cache + tile + src[m], buf + (w * PG + 64 * m) * 8);
+  for (int m = 0; m < Tile<D>::NI; ++m) copy_to_lds(cache + tile + src[m], buf + (pg * PG + 64 * m) * 8);
 }
 
 // Zero the V entries of keys >= ctx in a chunk buffer.
 template <int D>
 __device__ __forceinline__ void zero_tail(uint16_t* vbuf, int k0, int ctx, int tid) {
 #pragma unroll
-  for (int u = 0; u < D / 32; ++u) {
+  for (int u = 0; u < (kChunk / kBS) * 2 * D / 256; ++u) {
     const int s = tid + 256 * u;
     const int p = s / (2 * D), rem = s % (2 * D);
     const int d = rem >> 1, h = (rem & 1) ^ vswz(d);
@@ -165,17 +171,17 @@ __device__ __forceinline__ void zero_tail(uint16_t* vbuf, int k0, int ctx, int t
 // chunk against row 16 (kRT w + rt) + c (A operand row c is key
 // 8 (c / 4) + 4 j + c % 4 of the block, so lane group qg gets keys 8 qg ..).
 template <int D>
-__device__ __forceinline__ void chunk_scores(f32x4 (&S)[kRT][2][2], const uint16_t* kbuf, const Tile<D>& t) {
+__device__ __forceinline__ void chunk_scores(f32x4 (&S)[kRT][kKB][2], const uint16_t* kbuf, const Tile<D>& t) {
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
       for (int j = 0; j < 2; ++j) S[rt][kb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < Tile<D>::KK; ++kk)  // eight independent accumulators per k-step
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const u32x4 kv = *reinterpret_cast<const u32x4*>(kbuf + (32 * kb + 4 * j) * D + t.kaddr[kk]);
@@ -184,34 +190,39 @@ __device__ __forceinline__ void chunk_scores(f32x4 (&S)[kRT][2][2], const uint16
       }
 }
 
-// Step ci of the pipeline.  On entry S holds the raw scores of chunk ci,
-// K of chunk ci + 1 and V of chunk ci are on their way into k_next / v_cur,
-// and k_free / v_free (K of ci, V of ci - 1) are being read no more once
-// everyone passes the barrier.  The step starts the copies of K(ci + 2) and
-// V(ci + 1), issues the score MFMAs of chunk ci + 1 (into S for the next
-// step) among the softmax instructions of chunk ci, then the weighted sum of
-// V(ci).  On the last step the next scores come from stale LDS and are
-// dropped.
+// Step ci of the pipeline.  K of chunk ci is in k_cur (copied two steps
+// ago), V of chunk ci in v_cur (one step ago).  Waves 0-1 copy K pages and
+// keep the copy of K(ci + 1) in flight across the barrier; waves 2-3 copy V
+// pages.  After the barrier the buffers of K(ci - 1) and V(ci - 1) are read
+// no more, and the step starts the copies of K(ci + 2) and V(ci + 1) into
+// them, then computes chunk ci: scores, softmax, the weighted sum of V.
 template <int D>
-__device__ __forceinline__ void chunk_step(Tile<D>& t, f32x4 (&S)[kRT][2][2], uint16_t* k_next, uint16_t* k_free,
-                                           uint16_t* v_cur, uint16_t* v_free, int ci, int nch, int nb, int ctx,
-                                           int pos_min, const int32_t* trow, const uint16_t* kc,
-                                           const uint16_t* vc, int H, int g, int w, int tid, int qg, float sl) {
+__device__ __forceinline__ void chunk_step(Tile<D>& t, const uint16_t* k_cur, uint16_t* k_free, uint16_t* v_cur,
+                                           uint16_t* v_free, int ci, int nch, int nb, int ctx, int pos_min,
+                                           const int32_t* trow, const uint16_t* kc, const uint16_t* vc, int H,
+                                           int g, int w, int tid, int qg, float sl) {
   constexpr int T8 = Tile<D>::T8;
-  barrier<kWaitAll>();  // K(ci + 1) and V(ci) are in LDS; the free buffers are free
-  if (ci + 2 < nch) issue_tiles<D>(k_free, kc, t.ksrc, ci + 2, nb, trow, H, g, w);
-  if (ci + 1 < nch) issue_tiles<D>(v_free, vc, t.vsrc, ci + 1, nb, trow, H, g, w);
+  constexpr int NI = Tile<D>::NI;
+  if (w < 2 && ci + 1 < nch) barrier<kWaitVm<NI>>();  // K(ci) landed; K(ci + 1) stays in flight
+  else barrier<kWaitAll>();                          // K(ci) or V(ci) landed
+  if (w < 2) {
+    if (ci + 2 < nch) issue_tiles<D>(k_free, kc, t.csrc, ci + 2, nb, trow, H, g, w);
+  } else {
+    if (ci + 1 < nch) issue_tiles<D>(v_free, vc, t.csrc, ci + 1, nb, trow, H, g, w - 2);
+  }
   const int k0 = ci * kChunk;
   if (k0 + kChunk > ctx) {  // the request's last chunk: no V copy is in flight
     zero_tail<D>(v_cur, k0, ctx, tid);
     barrier<kWaitLds>();
   }
+  f32x4 S[kRT][kKB][2];
+  chunk_scores<D>(S, k_cur, t);
   // raw scores; sl > 0 is folded into the exponent below
   if (k0 + kChunk - 1 > pos_min) {  // some key of the chunk lies after some row of this wave
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -227,7 +238,7 @@ __device__ __forceinline__ void chunk_step(Tile<D>& t, f32x4 (&S)[kRT][2][2], ui
   for (int rt = 0; rt < kRT; ++rt) {
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         mx = __builtin_elementwise_maximum(mx, max4(S[rt][kb][j][0], S[rt][kb][j][1], S[rt][kb][j][2],
@@ -250,15 +261,12 @@ __device__ __forceinline__ void chunk_step(Tile<D>& t, f32x4 (&S)[kRT][2][2], ui
     }
   }
 
-  // weights of chunk ci, with the score MFMAs of chunk ci + 1 in flight
-  f32x4 Sn[kRT][2][2];
-  chunk_scores<D>(Sn, k_next, t);
-  u32x4 pop[kRT][2];
+  u32x4 pop[kRT][kKB];
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
     float ps = 0.0f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < kKB; ++kb) {
       float e[2][4];
 #pragma unroll
       for (int j = 0; j < 2; ++j)
@@ -272,40 +280,20 @@ __device__ __forceinline__ void chunk_step(Tile<D>& t, f32x4 (&S)[kRT][2][2], ui
     }
     t.l[rt] += ps;
   }
-  // PV: the eight V operands of key block 0 are read up front, and each
-  // block-1 read is issued beside two block-0 MFMAs, so eight LDS reads stay
-  // in flight (left alone, the compiler waited on every read after two).
-  u32x4 vv[2][T8];
+  // PV: each V operand read feeds the kRT row tiles.
 #pragma unroll
-  for (int t8 = 0; t8 < T8; ++t8) vv[0][t8] = *reinterpret_cast<const u32x4*>(v_cur + t.vaddr + 8 * (32 * t8));
-  __builtin_amdgcn_sched_barrier(0);
+  for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
-  for (int t8 = 0; t8 < T8; ++t8) {
-    vv[1][t8] = *reinterpret_cast<const u32x4*>(v_cur + t.vaddr + 8 * (4 * D + 32 * t8));
+    for (int t8 = 0; t8 < T8; ++t8) {
+      const u32x4 vv = *reinterpret_cast<const u32x4*>(v_cur + t.vaddr + 8 * (4 * D * kb + 32 * t8));
 #pragma unroll
-    for (int rt = 0; rt < kRT; ++rt) t.acc[rt][t8] = mfma(vv[0][t8], pop[rt][0], t.acc[rt][t8]);
-  }
-#pragma unroll
-  for (int t8 = 0; t8 < T8; ++t8) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-    __builtin_amdgcn_sched_group_barrier(0x008, kRT, 0);  // then kRT MFMAs
-  }
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int t8 = 0; t8 < T8; ++t8)
-#pragma unroll
-    for (int rt = 0; rt < kRT; ++rt) t.acc[rt][t8] = mfma(vv[1][t8], pop[rt][1], t.acc[rt][t8]);
-#pragma unroll
-  for (int rt = 0; rt < kRT; ++rt)
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) S[rt][kb][j] = Sn[rt][kb][j];
+      for (int rt = 0; rt < kRT; ++rt) t.acc[rt][t8] = mfma(vv, pop[rt][kb], t.acc[rt][t8]);
+    }
 }
 
 // grid: tiles * B * H workgroups of 256 threads, latest tiles first.
 template <int D>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(256, 3) __attribute__((amdgpu_waves_per_eu(3, 3)))
 prefill_kernel(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc, const uint16_t* __restrict__ q,
                uint16_t* __restrict__ out, const int32_t* __restrict__ tables, int max_blocks,
                const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ qstart, int B, int tiles,
@@ -316,6 +304,7 @@ prefill_kernel(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
   __shared__ __attribute__((aligned(16))) uint16_t v_a[kChunk * D];
   __shared__ __attribute__((aligned(16))) uint16_t k_b[kChunk * D];
   __shared__ __attribute__((aligned(16))) uint16_t v_b[kChunk * D];
+  __shared__ __attribute__((aligned(16))) uint16_t k_c[kChunk * D];
 
   // Which tile: the XCD running this workgroup (id % 8) takes the (request,
   // kv head) pairs x, x + 8, ... in groups of kPairGroup, each group's tiles
@@ -346,21 +335,26 @@ prefill_kernel(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
   const int tok_end = min(tok0 + tpt, n_q);
 
   T t;
-  bool valid[kRT];
-  int64_t qrow[kRT];
-#pragma unroll
-  for (int rt = 0; rt < kRT; ++rt) {
+  // row rt of this lane: q / out row (q0 + tok) * h_q + head, recomputed
+  // where needed rather than held through the key loop
+  auto row_of = [&](int rt, bool& ok) -> int64_t {
     const int row = 16 * (kRT * w + rt) + c;
     const int tl = row / G;
-    valid[rt] = tl < tpt && tok0 + tl < tok_end;
-    const int tok = tok0 + (valid[rt] ? tl : 0);
-    const int head = g * G + row % G;
+    ok = tl < tpt && tok0 + tl < tok_end;
+    const int tok = tok0 + (ok ? tl : 0);
+    return int64_t(q0 + tok) * h_q + g * G + row % G;
+  };
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) {
+    bool ok;
+    const int64_t qr = row_of(rt, ok);
+    const int row = 16 * (kRT * w + rt) + c;
+    const int tok = tok0 + (ok ? row / G : 0);
     t.pos[rt] = max(ctx - n_q + tok, 0);  // last key this row reads
-    qrow[rt] = int64_t(q0 + tok) * h_q + head;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       u32x4 v = {0, 0, 0, 0};
-      if (valid[rt]) v = *reinterpret_cast<const u32x4*>(q + qrow[rt] * D + 32 * kk + 8 * qg);
+      if (ok) v = *reinterpret_cast<const u32x4*>(q + qr * D + 32 * kk + 8 * qg);
       t.qv[rt][kk] = v ^ q_sign;  // negated for negative scales (exact)
     }
     t.m[rt] = -INFINITY;
@@ -384,10 +378,13 @@ prefill_kernel(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
 #pragma unroll
   for (int m = 0; m < NI; ++m) {
     const int s = 64 * m + lane;  // granule of the page tile, in LDS order
-    const int rl = s / (D / 8), slot = s % (D / 8);
-    t.ksrc[m] = rl * D + 8 * (slot ^ kswz<D>(kBS * w + rl));
-    const int d = s >> 1;
-    t.vsrc[m] = d * kBS + 8 * ((s & 1) ^ vswz(d));
+    if (w < 2) {  // K page w of a chunk: key row rl, dimension granule slot
+      const int rl = s / (D / 8), slot = s % (D / 8);
+      t.csrc[m] = rl * D + 8 * (slot ^ kswz<D>(kBS * w + rl));
+    } else {  // V page w - 2: dimension d, key half s & 1
+      const int d = s >> 1;
+      t.csrc[m] = d * kBS + 8 * ((s & 1) ^ vswz(d));
+    }
   }
 
   const int n_keys = min(ctx, max(ctx - n_q + tok_end, 0));  // keys the tile reads
@@ -395,33 +392,44 @@ prefill_kernel(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
   const int nb = (ctx + kBS - 1) / kBS;
   const int32_t* trow = tables + int64_t(b) * max_blocks;
   if (nch > 0) {
-    issue_tiles<D>(k_a, kc, t.ksrc, 0, nb, trow, H, g, w);
-    issue_tiles<D>(v_a, vc, t.vsrc, 0, nb, trow, H, g, w);
-    if (nch > 1) issue_tiles<D>(k_b, kc, t.ksrc, 1, nb, trow, H, g, w);
-    barrier<kWaitAll>();
-    f32x4 S[kRT][2][2];
-    chunk_scores<D>(S, k_a, t);
-    for (int ci = 0; ci < nch; ci += 2) {
-      chunk_step<D>(t, S, k_b, k_a, v_a, v_b, ci, nch, nb, ctx, pos_min, trow, kc, vc, H, g, w, tid, qg,
-                    scale_log2);
-      if (ci + 1 < nch)
-        chunk_step<D>(t, S, k_a, k_b, v_b, v_a, ci + 1, nch, nb, ctx, pos_min, trow, kc, vc, H, g, w, tid, qg,
-                      scale_log2);
+    // K(0), K(1) (waves 0-1) and V(0) (waves 2-3) first; then steps in
+    // groups of six, the period of the three K and two V buffers
+    if (w < 2) {
+      issue_tiles<D>(k_a, kc, t.csrc, 0, nb, trow, H, g, w);
+      if (nch > 1) issue_tiles<D>(k_b, kc, t.csrc, 1, nb, trow, H, g, w);
+    } else {
+      issue_tiles<D>(v_a, vc, t.csrc, 0, nb, trow, H, g, w - 2);
+    }
+    for (int c6 = 0; c6 < nch; c6 += 6) {
+#define PF_STEP(u, kcur, kfree, vcur, vfree)                                                                 \
+  if (c6 + u < nch)                                                                                          \
+    chunk_step<D>(t, kcur, kfree, vcur, vfree, c6 + u, nch, nb, ctx, pos_min, trow, kc, vc, H, g, w, tid, qg, \
+                  scale_log2);
+      PF_STEP(0, k_a, k_c, v_a, v_b)
+      PF_STEP(1, k_b, k_a, v_b, v_a)
+      PF_STEP(2, k_c, k_b, v_a, v_b)
+      PF_STEP(3, k_a, k_c, v_b, v_a)
+      PF_STEP(4, k_b, k_a, v_a, v_b)
+      PF_STEP(5, k_c, k_b, v_b, v_a)
+#undef PF_STEP
     }
   }
+
 
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
     float lt = t.l[rt];
     lt += __shfl_xor(lt, 16);
     lt += __shfl_xor(lt, 32);
-    if (valid[rt]) {
+    bool ok;
+    const int64_t qr = row_of(rt, ok);
+    if (ok) {
       const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
 #pragma unroll
       for (int t8 = 0; t8 < T8; ++t8) {
         const f32x4 o = t.acc[rt][t8] * inv;
         const u32x2 pk = {pack2(o[0], o[1]), pack2(o[2], o[3])};
-        *reinterpret_cast<u32x2*>(out + qrow[rt] * D + 16 * t8 + 4 * qg) = pk;
+        *reinterpret_cast<u32x2*>(out + qr * D + 16 * t8 + 4 * qg) = pk;
       }
     }
   }
