@@ -235,6 +235,7 @@ struct WaveState {
   // that the fp16 weights p * v_scale / vs fed to the MFMA stay in [0, 1]
   // whatever the magnitude of V; the true sum is acc * vs
   float vs = 0.0f;
+  float vs_inv = 0.0f;  // 1 / vs once vs > 0, recomputed only when vs grows
 };
 
 // The lane's share of the query row as MFMA operands (bf16 bits).  Returns
@@ -347,6 +348,16 @@ __device__ __forceinline__ void run_segment(WaveState<D>& st, const uint8_t* __r
     tV = trow[min(cb + NB + vb_rel, jlast)];
     const uint8_t* ktile = kc + (pK * H + g) * tile_bytes;
     const uint8_t* vtile = vc + (pV * H + g) * tile_bytes;
+    // fp8: the tile scales go out before the K/V loads, so that waiting for
+    // them (loads complete in order) never waits for V (same box, fp8 calls
+    // 1% faster; int8, whose extra state makes registers tight, lost as much
+    // and loads them after)
+    float ksc = 1.0f, vsc = 1.0f;
+    if constexpr (QT == kQFp8) {
+      ksc = kscale[pV * H + g];
+      vsc = vscale[pV * H + g];
+      __builtin_amdgcn_sched_barrier(0);
+    }
 
     // ---- loads: K rows for the score MFMAs, this lane's V slice.  A block
     // past the segment (an odd last step) is loaded from the clamped table
@@ -398,22 +409,27 @@ __device__ __forceinline__ void run_segment(WaveState<D>& st, const uint8_t* __r
     float kfac = scale_log2;
     float vfac = 1.0f;
     if constexpr (Q8) {
-      kfac *= kscale[pV * H + g];
-      vfac = vV ? vscale[pV * H + g] : 0.0f;  // tiles past the segment: zero weights anyway
+      if constexpr (QT == kQInt8) {
+        ksc = kscale[pV * H + g];
+        vsc = vscale[pV * H + g];
+      }
+      kfac *= ksc;
+      vfac = vV ? vsc : 0.0f;  // tiles past the segment: zero weights anyway
     }
     float vs_fold = 1.0f;  // int8: acc rescale for a larger V-scale reference
     bool vs_grew = false;
     if constexpr (QT == kQInt8) {
       kfac *= qscale_inv;
       // the step's two tiles: lane groups 0-1 hold one, 2-3 the other
+      // (wave-uniform: both halves of the wave see both tiles' scales)
       const float vs_new = fmaxf(st.vs, fmaxf(vfac, __shfl_xor(vfac, 32)));
-      if (vs_new > 0.0f) {
-        const float inv = 1.0f / vs_new;
-        vs_fold = st.vs * inv;
-        vfac *= inv;
-      }
       vs_grew = vs_new != st.vs;
-      st.vs = vs_new;
+      if (vs_grew) {  // a larger reference: fold the old one into acc
+        st.vs_inv = 1.0f / vs_new;
+        vs_fold = st.vs * st.vs_inv;
+        st.vs = vs_new;
+      }
+      vfac *= st.vs_inv;
     }
     // A step whose two blocks lie inside the segment and whose 32 positions
     // are all read (below ctx; WIN: all sinks or all inside the window)
