@@ -111,9 +111,9 @@ DEFAULT_SEED = {"llama3_8b": 2, "llama3_70b_long": 3, "fp8": 5, "int8": 5, "pref
 # calibration there (fetch x2, write x1).  They hold for the kernel source they
 # were taken on, identified by its SHA-256; any other source reports null.
 TRAFFIC_SOURCE = "paged_kv_cache_271_amd/csrc/decode.hip"
-TRAFFIC_SHA256 = "2be2b88d0aa4bff65b3186bf952d4e7cc5d9f42f8ada30a3f0345894e17fdf1f"
-TRAFFIC_BYTES = {"llama3_8b": 608_928_646, "fp8": 1_255_802_116, "llama3_70b_long": 1_371_137_507,
-                 "int8": 1_252_429_640, "llama3_8b_window": 1_106_530_099}
+TRAFFIC_SHA256 = "4c7b53a2109f260d2e7230505c30a65b1b2c3d653769ae38697f3681ede1950a"
+TRAFFIC_BYTES = {"llama3_8b": 608_924_608, "fp8": 1_254_177_324, "llama3_70b_long": 1_371_129_251,
+                 "int8": 1_255_365_825, "llama3_8b_window": 1_106_550_928}
 # The same per launch of prefill_kernel and of block_copy_kernel, from
 # profiles/prefill_llama3_8b_counters.md and
 # profiles/block_copy_cow_fork_hbm_counters.md: (source, its SHA-256, bytes).
