@@ -111,7 +111,7 @@ DEFAULT_SEED = {"llama3_8b": 2, "llama3_70b_long": 3, "fp8": 5, "int8": 5, "pref
 # calibration there (fetch x2, write x1).  They hold for the kernel source they
 # were taken on, identified by its SHA-256; any other source reports null.
 TRAFFIC_SOURCE = "paged_kv_cache_271_amd/csrc/decode.hip"
-TRAFFIC_SHA256 = "4c7b53a2109f260d2e7230505c30a65b1b2c3d653769ae38697f3681ede1950a"
+TRAFFIC_SHA256 = "24c4ccb7420d606e05812e6663a8afbcb5936d5b504cab912fe3c5786c0a9c56"
 TRAFFIC_BYTES = {"llama3_8b": 608_924_608, "fp8": 1_254_177_324, "llama3_70b_long": 1_371_129_251,
                  "int8": 1_255_365_825, "llama3_8b_window": 1_106_550_928}
 # The same per launch of prefill_kernel and of block_copy_kernel, from

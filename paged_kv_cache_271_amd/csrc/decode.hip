@@ -126,15 +126,6 @@ __device__ inline f32x4 mfma_op(u32x4 a, u32x4 b, f32x4 c) {
                                                    c, 0, 0, 0);
 }
 
-// Zero the 16-bit elements e >= valid (0 <= valid <= 8) of an 8-element vector.
-__device__ inline u32x4 mask_tail(u32x4 v, int valid) {
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    if (2 * w >= valid) v[w] = 0;
-    else if (2 * w + 1 >= valid) v[w] &= 0xFFFFu;
-  }
-  return v;
-}
 
 // Context length of request b, clamped to [0, max_ctx] so that no kernel can
 // index past the table row or the workspace sized from max_ctx.
@@ -280,16 +271,6 @@ __device__ inline float load_q(u32x4 (&qv)[D / 32], const uint16_t* q, int64_t r
   return qscale_inv;
 }
 
-// Zero the 16-bit elements e of an 8-element vector whose bit e of `keep` is clear.
-__device__ inline u32x4 mask_bits(u32x4 v, uint32_t keep) {
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const uint32_t lo = (keep >> (2 * w)) & 1u ? 0x0000FFFFu : 0u;
-    const uint32_t hi = (keep >> (2 * w + 1)) & 1u ? 0xFFFF0000u : 0u;
-    v[w] &= lo | hi;
-  }
-  return v;
-}
 
 // Wave issue priority from the progress of the wave's chunk: `done` of `total`
 // units streamed.  Waves of the three workgroups that share a CU would
