@@ -300,18 +300,21 @@ def test_balanced_split_reused_workspace(gpu_lib):
     assert np.max(np.abs(fixed - got)) <= 2e-2
 
 
-def test_largest_batch(gpu_lib):
-    """8192 requests (the largest batch of the balanced decode) of 0-40
-    tokens: the block prefix is scanned in 32 passes, chunks hold many whole
-    requests, empty requests give zeros.  Plain decode, then the fused step
-    (which also appends 8192 rows); a sample of requests is checked against
-    the oracle, and every output is finite."""
+@pytest.mark.parametrize("B,D", [(8192, 64), (8192, 128), (4096, 128)])
+def test_largest_batch(gpu_lib, B, D):
+    """The largest batches, of 0-40 tokens per request: 8192 (the bound of
+    the balanced decode) and 4096 (the bound of the LDS-ring decode, which
+    bf16 pools with head_dim 128 take up to that size; larger batches fall
+    back to the register-streaming decode).  The block prefix is scanned in
+    many passes, chunks hold many whole requests, empty requests give zeros.
+    Plain decode, then the fused step (which also appends B rows); a sample
+    of requests is checked against the oracle, and every output is finite."""
     rng = np.random.default_rng(81)
-    lens = rng.integers(0, 41, 8192)
-    lens[rng.choice(8192, 200, replace=False)] = 0
+    lens = rng.integers(0, 41, B)
+    lens[rng.choice(B, 200, replace=False)] = 0
     need = int(sum(oracle.blocks_for(int(n), 16) for n in lens))
-    c = Case("bf16", 2, 64, 8, lens, num_blocks=need + 8192, max_blocks=4, seed=81)
-    sample = sorted(set(rng.choice(8192, 48, replace=False).tolist()) | {0, 8191, int(np.argmax(lens))})
+    c = Case("bf16", 2, D, 8, lens, num_blocks=need + B, max_blocks=4, seed=81)
+    sample = sorted(set(rng.choice(B, 48, replace=False).tolist()) | {0, B - 1, int(np.argmax(lens))})
     got = c.decode()
     assert np.all(np.isfinite(got))
     ref = c.oracle(batch=sample)
