@@ -105,15 +105,15 @@ DEFAULT_LAYERS = {"llama3_8b": 32, "llama3_70b_long": 8, "fp8": 16, "int8": 16, 
 DEFAULT_SEED = {"llama3_8b": 2, "llama3_70b_long": 3, "fp8": 5, "int8": 5, "prefix_churn": 4, "cow_fork": 6,
                 "llama3_8b_window": 7, "prefill": 8, "ctx_sweep": 2}
 
-# HBM bytes (read + written) per launch of decode_stream_kernel in the default
+# HBM bytes (read + written) per launch of the decode kernel in the default
 # step of each workload, from the rocprofv3 FETCH_SIZE and WRITE_SIZE runs in
-# profiles/decode_stream_workloads_hbm_counters.md, scaled by the plain-copy
+# profiles/decode_workloads_hbm_counters.md, scaled by the plain-copy
 # calibration there (fetch x2, write x1).  They hold for the kernel source they
 # were taken on, identified by its SHA-256; any other source reports null.
 TRAFFIC_SOURCE = "paged_kv_cache_271_amd/csrc/decode.hip"
-TRAFFIC_SHA256 = "24c4ccb7420d606e05812e6663a8afbcb5936d5b504cab912fe3c5786c0a9c56"
-TRAFFIC_BYTES = {"llama3_8b": 608_924_608, "fp8": 1_254_177_324, "llama3_70b_long": 1_371_129_251,
-                 "int8": 1_255_365_825, "llama3_8b_window": 1_106_550_928}
+TRAFFIC_SHA256 = "bf06a74dff4d516b4a904b4658e26dc9b02fb20b4149653578254ad90435c9ec"
+TRAFFIC_BYTES = {"llama3_8b": 591_523_510, "fp8": 1_254_203_745, "llama3_70b_long": 1_348_120_377,
+                 "int8": 1_256_149_566, "llama3_8b_window": 1_106_600_272}
 # The same per launch of prefill_kernel and of block_copy_kernel, from
 # profiles/prefill_llama3_8b_counters.md and
 # profiles/block_copy_cow_fork_hbm_counters.md: (source, its SHA-256, bytes).
@@ -123,6 +123,14 @@ TRAFFIC_OTHER = {
     "cow_fork": ("paged_kv_cache_271_amd/csrc/copy.hip",
                  "06367c5bcbf1b2856b1a3729463a1093d9928cc8dab6c0ca5b114bb07073ec79", 1_073_901_158),
 }
+
+
+def decode_kernel_name(dtype, head_dim, window, batch):
+    """The decode kernel the library launches for such a step: the LDS-ring
+    kernel for unwindowed bf16 batches with head_dim 128 of up to 4096
+    requests, the register-streaming kernel otherwise."""
+    ring = dtype == "bf16" and head_dim == 128 and not window and batch <= 4096
+    return "decode_ring_kernel" if ring else "decode_stream_kernel"
 
 
 def measured_traffic(workload, two_calls_asked=False):
@@ -402,8 +410,10 @@ def decode_workload(args, torch, synth, pk, dev, spec=None, layers=0):
                 probe=probe,
                 config=config, cpu=cpu, traffic=measured_traffic(name, args.two_calls), dtype={"fp8": "fp8-e4m3 K/V, bf16 q", "int8": "int8 K/V, bf16 q"}.get(dtype, "bf16"),
                 kernel=("paged_attention_decode_window" if window else "paged_attention_decode")
-                + ("" if two_calls else "_append") + " call (decode_stream_kernel, merging its split pieces "
-                "itself; a reduce kernel follows only for requests split into many pieces)")
+                + ("" if two_calls else "_append") + f" call ({decode_kernel_name(dtype, D, window, B)}, merging "
+                "its split pieces itself; a reduce kernel follows only for requests split into many pieces)",
+                traffic_note=f"HBM bytes read + written per {decode_kernel_name(dtype, D, window, B)} launch "
+                             "(rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated); null if the kernel source changed")
 
 
 SWEEP_CTX = (512, 1024, 2048, 4096, 8192, 16384)
@@ -449,7 +459,7 @@ def ctx_sweep_workload(args, torch, synth, pk, dev):
                 dec_n=last["dec_n"], config=config, cpu=None, traffic=None, traffic_note="HBM counters not taken for this sweep",
                 dtype="bf16", value=rate, metric="paged decode call: streaming rate of the affine fit "
                 "over context length (GB/s), Llama-3-8B shape",
-                kernel="paged_attention_decode_append call at the longest context (decode_stream_kernel + "
+                kernel="paged_attention_decode_append call at the longest context (decode_ring_kernel + "
                        "piece merge)")
 
 
@@ -677,8 +687,8 @@ def main():
             "frac": round(achieved / peak, 4),
             "frac_median_bracket": round(achieved_p50 / peak, 4),
             "traffic": r.get("traffic"),
-            "traffic_note": r.get("traffic_note", "HBM bytes read + written per decode_stream_kernel "
-                                  "launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated); null if "
+            "traffic_note": r.get("traffic_note", "HBM bytes read + written per launch of the dominant "
+                                  "kernel (rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated); null if "
                                   "the kernel source changed"),
             "stream_copy_gbs": stream_copy_gbs(torch, dev),
             "us_per_call": round(dec_mean_s * 1e6, 2),
