@@ -148,6 +148,13 @@ int kv_block_refcount(const kv_pool* pool, int32_t block, int32_t* rc);
 /* Number of free blocks. */
 int kv_num_free_blocks(const kv_pool* pool, int32_t* n);
 
+/* Number of blocks whose reference count is at least 2: pages that several
+ * block tables, or a table and the prefix cache, map (askaiml page, §4 and
+ * §6: shared prefix pages).  The decode reads K/V with the non-temporal cache
+ * hint while this is 0, and with plain loads otherwise, so that the caches
+ * serve the repeated reads of a shared page. */
+int kv_num_shared_blocks(const kv_pool* pool, int32_t* n);
+
 /* --------------------------------------------------------- slot mapping -- */
 
 /* Host: slots_out[i] = table_row[positions[i] / block_size] * block_size
@@ -306,8 +313,9 @@ int paged_attention_workspace_init(const kv_pool* pool, void* workspace, int64_t
  *    (at most 16 on average and B * num_kv_heads * ceil(h_q / num_kv_heads /
  *    16) <= 65536), else by a second kernel.
  * Results depend on the context lengths of the batch (through the split) but
- * not on which physical blocks hold the data.  Accumulation is fp32; the
- * result is rounded to nearest even into out. */
+ * not on which physical blocks hold the data, nor on the cache hint of the
+ * K/V loads (non-temporal while kv_num_shared_blocks is 0).  Accumulation is
+ * fp32; the result is rounded to nearest even into out. */
 int paged_attention_decode(kv_pool* pool, int32_t layer, void* out, const void* q, int32_t q_dtype,
                            const int32_t* block_tables, int32_t max_blocks_per_seq,
                            const int32_t* context_lens, int32_t B, int32_t h_q, int32_t max_ctx,
@@ -330,9 +338,11 @@ int paged_attention_decode(kv_pool* pool, int32_t layer, void* out, const void* 
  * bf16 pools run it as one kernel: the attention takes the last position from
  * k_new / v_new while the same launch stores them into the slot, so the step
  * costs no separate append launch (outputs agree with the two calls to the
- * bf16 rounding of the weights).  f32, fp8 and int8 pools launch the append
- * kernel and then the decode (fp8 and int8 re-quantise the tile, which the attention must
- * read).  Errors and workspace are those of paged_attention_decode, plus
+ * bf16 rounding of the weights).  fp8 and int8 pools with at most 16 query
+ * heads per kv head also run one kernel: the wave that owns a request's last
+ * tile re-quantises it as kv_append does (cache bytes identical) before it
+ * reads it.  f32 pools, and 8-bit pools with more query heads per kv head,
+ * launch the append kernel and then the decode.  Errors and workspace are those of paged_attention_decode, plus
  * KV_E_INVALID for a NULL k_new, v_new or slot_mapping. */
 int paged_attention_decode_append(kv_pool* pool, int32_t layer, void* out, const void* q,
                                   int32_t q_dtype, const void* k_new, const void* v_new,

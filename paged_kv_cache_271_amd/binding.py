@@ -46,6 +46,7 @@ SIGNATURES = {
     "kv_block_release_n": (ctypes.c_int, [_P, _PI32, _I32]),
     "kv_block_refcount": (ctypes.c_int, [_P, _I32, _PI32]),
     "kv_num_free_blocks": (ctypes.c_int, [_P, _PI32]),
+    "kv_num_shared_blocks": (ctypes.c_int, [_P, _PI32]),
     "kv_slot_mapping": (ctypes.c_int, [_P, _PI32, _I32, _PI32, _I32, _PI32]),
     "kv_batch_reserve": (ctypes.c_int, [_P, _I32, _PI32, _I32, _PI32, _PI32, _PI32]),
     "kv_append": (ctypes.c_int, [_P, _I32, _P, _P, _P, _I32, _P]),
@@ -235,6 +236,12 @@ def kv_block_refcount(h, block):
 def kv_num_free_blocks(h):
     n = ctypes.c_int32()
     _check(_lib.kv_num_free_blocks(h, ctypes.byref(n)))
+    return n.value
+
+
+def kv_num_shared_blocks(h):
+    n = ctypes.c_int32()
+    _check(_lib.kv_num_shared_blocks(h, ctypes.byref(n)))
     return n.value
 
 
@@ -610,6 +617,9 @@ class Pool:
 
     def num_free(self):
         return kv_num_free_blocks(self.handle)
+
+    def num_shared(self):
+        return kv_num_shared_blocks(self.handle)
 
     def slot_mapping(self, table_row, positions):
         return kv_slot_mapping(self.handle, table_row, positions)

@@ -7,7 +7,11 @@
 //
 // A page of one layer is contiguous in K and in V (all kv heads' tiles), so
 // each workgroup streams one (pair, layer, K or V) run with 16-byte loads and
-// stores.  HBM-bound: 2 x page bytes moved per (pair, layer, K or V).
+// stores.  HBM-bound: 2 x page bytes moved per (pair, layer, K or V).  Loads
+// and stores carry the non-temporal hint: the copy is read next by a later
+// decode step of its layer, long after the caches have turned over (same box,
+// the 256-fork step took 212.6 us with plain loads and stores, 200.2 with
+// non-temporal stores, 186.5 with both).
 
 #include <cstdint>
 
@@ -17,6 +21,8 @@
 
 namespace pagedkv {
 namespace {
+
+typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
 
 // grid (n pairs, layers, 2); 256 threads.  Pairs with an id out of range, or
 // src == dst, are skipped (device ids are a caller contract; this keeps a bad
@@ -37,10 +43,12 @@ __global__ void __launch_bounds__(256) block_copy_kernel(uint8_t* __restrict__ k
     uint4 v[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      if (k + u * 256 < n16) v[u] = from[k + u * 256];
+      if (k + u * 256 < n16)
+        v[u] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(from + k + u * 256)));
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      if (k + u * 256 < n16) to[k + u * 256] = v[u];
+      if (k + u * 256 < n16)
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v[u]), reinterpret_cast<u32x4*>(to + k + u * 256));
   }
   if (ks && threadIdx.x < H) {
     float* sc = (which ? vs : ks) + int64_t(l) * N * H;

@@ -48,6 +48,50 @@ struct PrefixCache {
   int64_t clock = 0;
 };
 
+// Reference counts of the pool's blocks (0 = free), which also keep the
+// number of blocks counted at least twice: blocks that several tables, or a
+// table and the prefix cache, map.  Every change goes through an element
+// reference, so the number stays exact whichever entry point changed a count.
+class RefCounts {
+ public:
+  class Ref {
+   public:
+    Ref(int32_t& v, int32_t& shared) : v_(v), shared_(shared) {}
+    operator int32_t() const { return v_; }
+    Ref& operator=(int32_t x) {
+      set(x);
+      return *this;
+    }
+    int32_t operator++() {
+      set(v_ + 1);
+      return v_;
+    }
+    int32_t operator--() {
+      set(v_ - 1);
+      return v_;
+    }
+
+   private:
+    void set(int32_t x) {
+      shared_ += int32_t(x >= 2) - int32_t(v_ >= 2);
+      v_ = x;
+    }
+    int32_t& v_;
+    int32_t& shared_;
+  };
+  void assign(size_t n, int32_t x) {
+    v_.assign(n, x);
+    shared_ = x >= 2 ? int32_t(n) : 0;
+  }
+  Ref operator[](size_t i) { return Ref(v_[i], shared_); }
+  int32_t operator[](size_t i) const { return v_[i]; }
+  int32_t shared() const { return shared_; }
+
+ private:
+  std::vector<int32_t> v_;
+  int32_t shared_ = 0;
+};
+
 }  // namespace pagedkv
 
 struct kv_pool {
@@ -57,7 +101,7 @@ struct kv_pool {
   float* k_scale;
   float* v_scale;
   std::vector<int32_t> stack;  // free blocks; the back is the top
-  std::vector<int32_t> rc;     // reference count per block, 0 = free
+  pagedkv::RefCounts rc;      // reference count per block, 0 = free
   pagedkv::PrefixCache prefix;
 };
 

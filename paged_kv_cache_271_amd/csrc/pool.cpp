@@ -161,6 +161,12 @@ int kv_block_release_n(kv_pool* p, const int32_t* blocks, int32_t n) {
   return ok();
 }
 
+int kv_num_shared_blocks(const kv_pool* p, int32_t* n) {
+  if (!p || !n) return fail(KV_E_INVALID, "NULL argument");
+  *n = p->rc.shared();
+  return ok();
+}
+
 int kv_block_refcount(const kv_pool* p, int32_t b, int32_t* rc) {
   if (!p || !rc) return fail(KV_E_INVALID, "NULL argument");
   if (b < 0 || b >= p->desc.num_blocks) return fail(KV_E_BAD_BLOCK, "block %d out of range", b);
@@ -187,7 +193,8 @@ int kv_slot_mapping(const kv_pool* p, const int32_t* table_row, int32_t n_table,
       return fail(KV_E_INVALID, "position %d (index %d) outside a table of %d blocks", pos, i, n_table);
     const int32_t b = table_row[pos / bs];
     if (!block_live(p, b)) return fail(KV_E_BAD_BLOCK, "position %d maps to block %d that is out of range or free", pos, b);
-    if (p->rc[b] > 1) return fail(KV_E_SHARED, "position %d maps to block %d shared by %d tables", pos, b, p->rc[b]);
+    if (p->rc[b] > 1) return fail(KV_E_SHARED, "position %d maps to block %d shared by %d tables", pos, b,
+                                  int32_t(p->rc[b]));
     slots_out[i] = b * bs + pos % bs;
   }
   return ok();

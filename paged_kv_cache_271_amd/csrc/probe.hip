@@ -18,6 +18,9 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
 
+// The runs are read with the non-temporal hint, as the decode reads K/V.
+__device__ inline u32x4 ldnt(const u32x4* p) { return __builtin_nontemporal_load(p); }
+
 // grid = workgroups, 256 threads; unit u reads run16 16-byte pieces at
 // kb + k_off[u] and at vb + v_off[u]; workgroup c takes units
 // [c n / W, (c + 1) n / W) and writes the XOR of its words to sink[c].  The
@@ -52,13 +55,13 @@ __global__ void __launch_bounds__(256) gather_probe_kernel(const uint8_t* __rest
       const u32x4* k1 = reinterpret_cast<const u32x4*>(kb + s_k[q + 1]);
       const u32x4* v1 = reinterpret_cast<const u32x4*>(vb + s_v[q + 1]);
 #pragma unroll 4
-      for (int i = tid; i < run16; i += 256) x ^= k0[i] ^ v0[i] ^ k1[i] ^ v1[i];
+      for (int i = tid; i < run16; i += 256) x ^= ldnt(k0 + i) ^ ldnt(v0 + i) ^ ldnt(k1 + i) ^ ldnt(v1 + i);
     }
     if (q < nb) {
       const u32x4* k0 = reinterpret_cast<const u32x4*>(kb + s_k[q]);
       const u32x4* v0 = reinterpret_cast<const u32x4*>(vb + s_v[q]);
 #pragma unroll 4
-      for (int i = tid; i < run16; i += 256) x ^= k0[i] ^ v0[i];
+      for (int i = tid; i < run16; i += 256) x ^= ldnt(k0 + i) ^ ldnt(v0 + i);
     }
   }
   uint32_t w = x[0] ^ x[1] ^ x[2] ^ x[3];

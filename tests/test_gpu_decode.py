@@ -270,6 +270,25 @@ def test_shared_prefix_equals_duplicated(gpu_lib, dtype):
     assert np.array_equal(outs[0], outs[1])
 
 
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("fp8", 128), ("int8", 128)])
+def test_cache_hint_bit_identical(gpu_lib, dtype, D):
+    """The decode reads K/V with the non-temporal hint while no block is
+    mapped twice and with plain loads otherwise (kv_num_shared_blocks).  A
+    block that no table lists is retained to switch the pool over: the
+    outputs stay bit-identical, balanced and fixed splits alike."""
+    lens = [int(x) for x in np.random.default_rng(31).integers(1, 3000, 24)]
+    need = sum(oracle.blocks_for(n, 16) for n in lens)
+    c = Case(dtype, 2, D, 8, lens, num_blocks=need + 1, seed=31)
+    assert c.pool.num_shared() == 0
+    plain = [c.decode(partition_tokens=p) for p in (0, 64)]
+    spare = c.pool.alloc()
+    c.pool.retain(spare)
+    assert c.pool.num_shared() == 1
+    assert all(np.array_equal(a, c.decode(partition_tokens=p)) for a, p in zip(plain, (0, 64)))
+    c.pool.release(spare)
+    assert c.pool.num_shared() == 0
+
+
 def test_deterministic_repeats(gpu_lib):
     c = Case("bf16", 8, 128, 32, [700, 2000, 33, 4096], num_blocks=600, seed=13)
     a = c.decode()

@@ -34,7 +34,7 @@ def _declared_functions():
 
 def test_exports_every_declared_function(lib):
     names = _declared_functions()
-    assert len(names) == 33
+    assert len(names) == 34
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(pk.SIGNATURES) == names
@@ -203,6 +203,8 @@ def test_allocator_bit_exact_against_oracle(n, seed, ops):
                 continue
             getattr(pk, f"kv_block_{op}")(h, x)
         assert pk.kv_num_free_blocks(h) == ref.num_free()
+        # blocks counted at least twice (the decode's cache-hint switch)
+        assert pk.kv_num_shared_blocks(h) == sum(ref.refcount(i) >= 2 for i in range(n))
     pk.kv_pool_destroy(h)
 
 
@@ -264,6 +266,7 @@ def test_batch_reserve_matches_oracle_composition(seed, B, steps):
             for i in range(N):
                 assert pk.kv_block_refcount(h, i) == ref.refcount(i)
             assert pk.kv_num_free_blocks(h) == ref.num_free()
+            assert pk.kv_num_shared_blocks(h) == sum(ref.refcount(i) >= 2 for i in range(N))
             break
     pk.kv_pool_destroy(h)
 
@@ -299,15 +302,18 @@ def test_retain_release_n_and_rollback(lib):
     for b in range(10):
         assert pk.kv_block_refcount(h, b) == ref.refcount(b)
     assert pk.kv_num_free_blocks(h) == ref.num_free()
+    assert pk.kv_num_shared_blocks(h) == sum(ref.refcount(b) >= 2 for b in range(10)) > 0
     # a failing entry undoes the whole call: counts and free order unchanged
     before = [pk.kv_block_refcount(h, b) for b in range(10)]
     free_before = pk.kv_num_free_blocks(h)
+    shared_before = pk.kv_num_shared_blocks(h)
     with pytest.raises(pk.KVError, match="BAD_BLOCK"):
         pk.kv_block_release_n(h, [blocks[0], blocks[0], blocks[0], blocks[0], 9])
     with pytest.raises(pk.KVError, match="BAD_BLOCK"):
         pk.kv_block_retain_n(h, [blocks[0], blocks[1], 8])
     assert [pk.kv_block_refcount(h, b) for b in range(10)] == before
     assert pk.kv_num_free_blocks(h) == free_before
+    assert pk.kv_num_shared_blocks(h) == shared_before
     assert [pk.kv_block_alloc(h) for _ in range(free_before)] == \
         [ref.alloc() for _ in range(free_before)]
     pk.kv_pool_destroy(h)

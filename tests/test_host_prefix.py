@@ -34,6 +34,7 @@ def lib():
 
 def same_state(h, alloc, n):
     assert pk.kv_num_free_blocks(h) == alloc.num_free()
+    assert pk.kv_num_shared_blocks(h) == sum(alloc.refcount(b) >= 2 for b in range(n))
     for b in range(n):
         assert pk.kv_block_refcount(h, b) == alloc.refcount(b)
 
