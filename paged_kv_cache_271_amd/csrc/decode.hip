@@ -1282,6 +1282,35 @@ __device__ __forceinline__ void ring_next(RingSeg& s, const int32_t* s_pref, int
   }
 }
 
+// The fused append's V slot, written as whole rows: the step's V slices are
+// in registers (lane (r, grp): dimension 16 t + r, key half grp & 1 of the
+// step's block grp >> 1), so the lanes holding block `be` (the token's block)
+// put the new token's value at offset o of their half rows and store them.
+// Every row of the tile is rewritten with the bytes the step copied, which
+// are the tile's current ones: no other wave of the launch reads or writes
+// this tile.  trw.v[t] holds dimensions 16 t + 4 grp .. + 3 in every lane
+// of group grp, so dimension 16 t + r comes from lane r + 16 (r >> 2).
+__device__ __forceinline__ void patch_token_v(const u32x4 (&vraw)[8], const TokenRows<128>& trw, uint8_t* vtile,
+                                              int be, int o, int r, int grp) {
+  const int src = r + 16 * (r >> 2);
+  const int e = r & 3;
+  const int h = grp & 1;
+  const int p = o & 7;
+  const uint32_t sh = 16u * uint32_t(p & 1);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const uint32_t w0 = __shfl(trw.v[t][0], src), w1 = __shfl(trw.v[t][1], src);
+    const uint32_t val = (((e >> 1) ? w1 : w0) >> (16 * (e & 1))) & 0xFFFFu;
+    u32x4 row = vraw[t];
+    if (h == (o >> 3)) {
+#pragma unroll
+      for (int wi = 0; wi < 4; ++wi)
+        if (wi == (p >> 1)) row[wi] = (row[wi] & ~(0xFFFFu << sh)) | (val << sh);
+    }
+    if ((grp >> 1) == be) *reinterpret_cast<u32x4*>(vtile + ((16 * t + r) * kBS + 8 * h) * 2) = row;
+  }
+}
+
 // grid: one workgroup per CU (at most kStreamWorkers / 4), 256 threads,
 // kRingLds bytes of dynamic LDS; B <= kRingMaxB.  Arguments and results as
 // decode_stream_kernel<kQBf16, 128, APPEND, false, NT>.
@@ -1322,9 +1351,16 @@ decode_ring_kernel(void* __restrict__ kc_, void* __restrict__ vc_, const uint16_
         const int64_t tile = (int64_t(pslot / kBS) * H + g) * kBS * D;
         const int off = pslot % kBS;
         *reinterpret_cast<u32x4*>(kw + tile + off * D + d0) = kx;
+        // V is dimension-major, so the slot is 2 bytes in each 32-byte row:
+        // such scattered partial writes cost 6 us per Llama-3-8B call.  The
+        // wave that reads the request's last block writes its V rows whole
+        // instead (below); only a block that holds nothing but the new token
+        // (offset 0), which no wave reads, gets them here.
+        if (off == 0) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          vw[tile + int64_t(d0 + e) * kBS + off] = uint16_t(vx[e / 2] >> (16 * (e & 1)));
+          for (int e = 0; e < 8; ++e)
+            vw[tile + int64_t(d0 + e) * kBS + off] = uint16_t(vx[e / 2] >> (16 * (e & 1)));
+        }
       }
       piece += gthreads;
       if (piece < pieces) {
@@ -1437,6 +1473,13 @@ decode_ring_kernel(void* __restrict__ kc_, void* __restrict__ vc_, const uint16_
         const int64_t nrow = (int64_t(b) * H + g) * D;
         load_token<D>(trw, k_new + nrow, v_new + nrow, grp);
       }
+      // ... and, unless the token starts its block, this wave writes that
+      // block's V rows with the token's values in place (patch_token_v)
+      const int tb = cs.nb - 1;
+      const bool vpatch = tok && ((ctx - 1) & (kBS - 1)) != 0;
+      uint8_t* vtile = nullptr;
+      if (vpatch)
+        vtile = static_cast<uint8_t*>(vc_) + (int64_t(tables[int64_t(b) * max_blocks + tb]) * H + g) * (kBS * D * 2);
       for (int cb = cs.j; cb < cs.jr1; cb += 2, ++consumed) {
         uint8_t* stage = ring + (consumed % kRingStages) * kRingStage;
         // this stage's 16 copies have landed once at most the next stage's
@@ -1447,6 +1490,9 @@ decode_ring_kernel(void* __restrict__ kc_, void* __restrict__ vc_, const uint16_
         u32x4 vraw[T8];
         ring_read(kop, vraw, stage, Lr);
         issue_next(stage);  // the stage is read: the copies two stages on refill it
+        if constexpr (APPEND) {
+          if (vpatch && unsigned(tb - cb) < 2u) patch_token_v(vraw, trw, vtile, tb - cb, (ctx - 1) & (kBS - 1), r, grp);
+        }
         stream_step<kQBf16, D, false>(st, kop, vraw, qv, cb, cs.jr1, ctx_c, scale_log2, 1.0f, 1.0f, grp, 0, 0, 1.0f,
                                       noscale);
       }
