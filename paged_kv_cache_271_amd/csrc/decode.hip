@@ -486,6 +486,71 @@ __device__ __forceinline__ void stream_step(WaveState<D>& st, const u32x4 (&kop)
 // Stream blocks [j0, j1) of one (request, kv-head) into the wave state.
 // Positions at or past ctx are masked.  WIN: so are positions in
 // [sink, win_lo) (a sliding window with attention sinks).
+// The new token's K row and this lane's part of its V row (dimensions
+// 16 t + 4 grp .. + 3), for a fused append.
+template <int D>
+struct TokenRows {
+  u32x4 k[D / 32];
+  u32x2 v[D / 16];
+};
+
+// The fused append's V slot, written as whole rows: the step's V slices are
+// in registers (lane (r, grp): dimension 16 t + r, key half grp & 1 of the
+// step's block grp >> 1), so the lanes holding block `be` (the token's block)
+// put the new token's value at offset o of their half rows and store them.
+// Every row of the tile is rewritten with the bytes the step copied, which
+// are the tile's current ones: no other wave of the launch reads or writes
+// this tile.  val[t] is the token's value of dimension 16 t + r (bf16 bits).
+template <int D>
+__device__ __forceinline__ void patch_token_v(const u32x4 (&vraw)[D / 16], const uint32_t (&val)[D / 16],
+                                              uint8_t* vtile, int be, int o, int r, int grp) {
+  const int h = grp & 1;
+  const int p = o & 7;
+  const uint32_t sh = 16u * uint32_t(p & 1);
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    u32x4 row = vraw[t];
+    if (h == (o >> 3)) {
+#pragma unroll
+      for (int wi = 0; wi < 4; ++wi)
+        if (wi == (p >> 1)) row[wi] = (row[wi] & ~(0xFFFFu << sh)) | (val[t] << sh);
+    }
+    if ((grp >> 1) == be) *reinterpret_cast<u32x4*>(vtile + ((16 * t + r) * kBS + 8 * h) * 2) = row;
+  }
+}
+
+// The same after the segment, for the register-streaming kernel (whose step
+// has no registers to spare): the tile's V rows are loaded again (lanes of
+// groups 0 and 1: dimension 16 t + r, half grp), the token's values with
+// them, and the rows go back with the token in place.
+template <int D>
+__device__ __forceinline__ void reload_patch_token_v(uint8_t* vtile, const uint16_t* __restrict__ vn, int o, int r,
+                                                     int grp) {
+  if (grp >= 2) return;
+  u32x4 rows[D / 16];
+  uint32_t val[D / 16];
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    rows[t] = ld16(vtile + ((16 * t + r) * kBS + 8 * grp) * 2);
+    val[t] = vn[16 * t + r];
+  }
+  patch_token_v<D>(rows, val, vtile, 0, o, r, grp);
+}
+
+// The values patch_token_v needs, from TokenRows: trw.v[t] holds dimensions
+// 16 t + 4 grp .. + 3 in every lane of group grp, so dimension 16 t + r comes
+// from lane r + 16 (r >> 2).  Every lane of the wave must take part.
+template <int D>
+__device__ __forceinline__ void token_v_values(uint32_t (&val)[D / 16], const TokenRows<D>& trw, int r) {
+  const int src = r + 16 * (r >> 2);
+  const int e = r & 3;
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    const uint32_t w0 = __shfl(trw.v[t][0], src), w1 = __shfl(trw.v[t][1], src);
+    val[t] = (((e >> 1) ? w1 : w0) >> (16 * (e & 1))) & 0xFFFFu;
+  }
+}
+
 template <int QT, int D, bool NT, bool WIN = false>
 __device__ __forceinline__ void run_segment(WaveState<D>& st, const uint8_t* __restrict__ kc,
                                    const uint8_t* __restrict__ vc, const float* __restrict__ kscale,
@@ -682,11 +747,6 @@ __device__ __forceinline__ void append8_token(uint8_t* __restrict__ kc, uint8_t*
 
 // One token's K and V rows (head_dim values each, one kv head), this lane's
 // share: K dims 32 kk + 8 grp .. + 7, V dims 16 t + 4 grp .. + 3.
-template <int D>
-struct TokenRows {
-  u32x4 k[D / 32];
-  u32x2 v[D / 16];
-};
 
 template <int D>
 __device__ inline void load_token(TokenRows<D>& t, const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vn,
@@ -725,16 +785,6 @@ __device__ inline void fold_token(WaveState<D>& st, const TokenRows<D>& tr, cons
                      __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xFFFF0000u)};
     st.acc[t] = st.acc[t] * alpha + v * p;
   }
-}
-
-// The same for a token whose rows are loaded here.
-template <int D>
-__device__ inline void add_token(WaveState<D>& st, const uint16_t* __restrict__ kn,
-                                 const uint16_t* __restrict__ vn, const u32x4 (&qv)[D / 32],
-                                 float scale_log2, int grp) {
-  TokenRows<D> tr;
-  load_token<D>(tr, kn, vn, grp);
-  fold_token<D>(st, tr, qv, scale_log2, grp);
 }
 
 // Pages a decode reads for a request of n tokens: logical pages [0, a) and
@@ -884,12 +934,16 @@ __device__ __forceinline__ void merge_row_pieces(uint16_t* __restrict__ out, int
 // APPEND (bf16 caches): request b also appends one token, k_new[b] / v_new[b]
 // ([H][D] each), at new_slots[b] (-1: none), which is the slot of its
 // position ctx - 1.  The attention then reads positions < ctx - 1 from the
-// cache and takes the last one from k_new / v_new (add_token, in the segment
-// that ends the request); threads of the same launch store the token into
-// the cache while the block counts are summed.  The slot's bytes may still be
-// loaded with the rest of its tile while those stores land, unordered, but
-// that lane is past the cached range and masked, so neither the old nor the
-// new bytes reach the result.  8-bit caches: see the Q8 append branch.
+// cache and takes the last one from k_new / v_new (fold_token, in the segment
+// that ends the request).  The token goes into the cache in the same launch:
+// threads store its K row while the block counts are summed (and its V slot
+// when it starts a block, which no wave then reads), and the wave whose
+// segment ends the request writes the V rows of the token's block whole,
+// from the copy it read, with the token in place (patch_token_v).  The K
+// slot's bytes may be loaded with the rest of its tile while the K stores
+// land, unordered, but that lane is past the cached range and masked, so
+// neither the old nor the new bytes reach the result.  8-bit caches: see the
+// Q8 append branch.
 //
 // WIN: a sliding window of `window` tokens plus `sink` sink tokens; units
 // run over the pages each request reads (visited_pages), so pages outside
@@ -936,9 +990,14 @@ decode_stream_kernel(void* __restrict__ kc_, void* __restrict__ vc_,
         const int64_t tile = (int64_t(pslot / kBS) * H + g) * kBS * D;
         const int off = pslot % kBS;
         *reinterpret_cast<u32x4*>(kw + tile + off * D + d0) = kx;
+        // the V slot is 2 bytes in each 32-byte row: the wave that reads the
+        // block writes its rows whole (patch_token_v); only a block holding
+        // nothing but the token gets the scattered stores
+        if (off == 0) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          vw[tile + int64_t(d0 + e) * kBS + off] = uint16_t(vx[e / 2] >> (16 * (e & 1)));
+          for (int e = 0; e < 8; ++e)
+            vw[tile + int64_t(d0 + e) * kBS + off] = uint16_t(vx[e / 2] >> (16 * (e & 1)));
+        }
       }
       piece += gthreads;
       if (piece < pieces) {
@@ -1031,9 +1090,18 @@ decode_stream_kernel(void* __restrict__ kc_, void* __restrict__ vc_,
                                       lo + off, hi + off, scale_log2, qv, r, grp, sink, win_lo, u - u0 + (lo - j),
                                       ctot, qsi);
         }
+        // the segment that ends the request folds in the new token and, unless
+        // it starts its block, writes that block's V rows (patch_token_v)
         if (app && j1 == nb) {
           const int64_t nrow = (int64_t(b) * H + g) * D;
-          add_token<D>(st, k_new + nrow, v_new + nrow, qv, scale_log2, grp);
+          TokenRows<D> trw;
+          load_token<D>(trw, k_new + nrow, v_new + nrow, grp);
+          fold_token<D>(st, trw, qv, scale_log2, grp);
+          const int o = (ctx - 1) & (kBS - 1);
+          if (APPEND16 && o != 0)
+            reload_patch_token_v<D>(static_cast<uint8_t*>(vc_) +
+                                        (int64_t(tables[int64_t(b) * max_blocks + vp.nb - 1]) * H + g) * (kBS * D * 2),
+                                    v_new + nrow, o, r, grp);
         }
       } else if constexpr (APPEND && QT != kQBf16) {
         // 8-bit cache: the wave whose segment ends the request writes the
@@ -1070,9 +1138,18 @@ decode_stream_kernel(void* __restrict__ kc_, void* __restrict__ vc_,
         if (j < jc1)
           run_segment<QT, D, NT>(st, kc, vc, kscale, vscale, tables + int64_t(b) * max_blocks, ctx_c, H, g,
                               j, jc1, scale_log2, qv, r, grp, 0, 0, u - u0, ctot);
+        // the segment that ends the request folds in the new token and, unless
+        // it starts its block, writes that block's V rows (patch_token_v)
         if (app && j1 == nb) {
           const int64_t nrow = (int64_t(b) * H + g) * D;
-          add_token<D>(st, k_new + nrow, v_new + nrow, qv, scale_log2, grp);
+          TokenRows<D> trw;
+          load_token<D>(trw, k_new + nrow, v_new + nrow, grp);
+          fold_token<D>(st, trw, qv, scale_log2, grp);
+          const int o = (ctx - 1) & (kBS - 1);
+          if (o != 0)
+            reload_patch_token_v<D>(static_cast<uint8_t*>(vc_) +
+                                        (int64_t(tables[int64_t(b) * max_blocks + nb - 1]) * H + g) * (kBS * D * 2),
+                                    v_new + nrow, o, r, grp);
         }
       } else {
         run_segment<QT, D, NT>(st, kc, vc, kscale, vscale, tables + int64_t(b) * max_blocks, ctx, H, g, j, j1,
@@ -1282,35 +1359,6 @@ __device__ __forceinline__ void ring_next(RingSeg& s, const int32_t* s_pref, int
   }
 }
 
-// The fused append's V slot, written as whole rows: the step's V slices are
-// in registers (lane (r, grp): dimension 16 t + r, key half grp & 1 of the
-// step's block grp >> 1), so the lanes holding block `be` (the token's block)
-// put the new token's value at offset o of their half rows and store them.
-// Every row of the tile is rewritten with the bytes the step copied, which
-// are the tile's current ones: no other wave of the launch reads or writes
-// this tile.  trw.v[t] holds dimensions 16 t + 4 grp .. + 3 in every lane
-// of group grp, so dimension 16 t + r comes from lane r + 16 (r >> 2).
-__device__ __forceinline__ void patch_token_v(const u32x4 (&vraw)[8], const TokenRows<128>& trw, uint8_t* vtile,
-                                              int be, int o, int r, int grp) {
-  const int src = r + 16 * (r >> 2);
-  const int e = r & 3;
-  const int h = grp & 1;
-  const int p = o & 7;
-  const uint32_t sh = 16u * uint32_t(p & 1);
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const uint32_t w0 = __shfl(trw.v[t][0], src), w1 = __shfl(trw.v[t][1], src);
-    const uint32_t val = (((e >> 1) ? w1 : w0) >> (16 * (e & 1))) & 0xFFFFu;
-    u32x4 row = vraw[t];
-    if (h == (o >> 3)) {
-#pragma unroll
-      for (int wi = 0; wi < 4; ++wi)
-        if (wi == (p >> 1)) row[wi] = (row[wi] & ~(0xFFFFu << sh)) | (val << sh);
-    }
-    if ((grp >> 1) == be) *reinterpret_cast<u32x4*>(vtile + ((16 * t + r) * kBS + 8 * h) * 2) = row;
-  }
-}
-
 // grid: one workgroup per CU (at most kStreamWorkers / 4), 256 threads,
 // kRingLds bytes of dynamic LDS; B <= kRingMaxB.  Arguments and results as
 // decode_stream_kernel<kQBf16, 128, APPEND, false, NT>.
@@ -1491,7 +1539,11 @@ decode_ring_kernel(void* __restrict__ kc_, void* __restrict__ vc_, const uint16_
         ring_read(kop, vraw, stage, Lr);
         issue_next(stage);  // the stage is read: the copies two stages on refill it
         if constexpr (APPEND) {
-          if (vpatch && unsigned(tb - cb) < 2u) patch_token_v(vraw, trw, vtile, tb - cb, (ctx - 1) & (kBS - 1), r, grp);
+          if (vpatch && unsigned(tb - cb) < 2u) {
+            uint32_t val[T8];
+            token_v_values<D>(val, trw, r);
+            patch_token_v<D>(vraw, val, vtile, tb - cb, (ctx - 1) & (kBS - 1), r, grp);
+          }
         }
         stream_step<kQBf16, D, false>(st, kop, vraw, qv, cb, cs.jr1, ctx_c, scale_log2, 1.0f, 1.0f, grp, 0, 0, 1.0f,
                                       noscale);
