@@ -645,8 +645,11 @@ __device__ __forceinline__ void run_segment(WaveState<D>& st, const uint8_t* __r
 // Plain loads and stores: only this wave touches the tile in this launch,
 // and the workgroup-scope release / acquire that follows (wait_all_memory)
 // orders them before the wave's reads of it.
+// Not inlined: its fp8 codec is large, and inlined into the ring decode's
+// step loop (where it runs once per request and kv head) the code grew the
+// fused fp8 step from 210 to 251 us.
 template <int D, bool INT8>
-__device__ __forceinline__ void append8_token(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
+__device__ __attribute__((noinline)) void append8_token(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
                                               float* __restrict__ ksc, float* __restrict__ vsc, int64_t sidx, int o,
                                               const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vn,
                                               int lane) {
@@ -1321,6 +1324,108 @@ __device__ __forceinline__ void ring_read(u32x4 (&kop)[2][4], u32x4 (&vr)[8], co
       : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(av));
 }
 
+// ---- 8-bit caches (fp8, int8) on the ring.  A tile is 2 KiB of K (16 token
+// rows of 128 codes) and 2 KiB of V (128 dimension rows of 16 codes), so a
+// step's two blocks fill 8 KiB and a wave keeps four stages (the bytes in
+// flight of the bf16 ring's two).  Stage layout: K of block 0 and 1 at 0 and
+// 2048, V at 4096 and 6144, then the two blocks' (K, V) scale pairs at 8192.
+// K row R of block be holds code granule c (16 codes) at slot c ^ h(R, be),
+// h = ((R >> 1) & 1) | ((R >> 3) & 1) << 1 | be << 2, so that the 16 lanes of
+// each operand read (rows 8 ((r >> 2) & 1) + 4 j + (r & 3) of block r >> 3)
+// fall in 16 different bank quads; V reads are conflict-free as laid out.
+// Copies per stage: 4 of K and 4 of V (1 KiB each), 1 of the four scales.
+constexpr int kRing8Stage = 8320;                 // bytes per stage (8 KiB + scales, 128-byte aligned)
+constexpr int kRing8Stages = 4;                   // stages per wave
+constexpr int kRing8Lds = 4 * kRing8Stages * kRing8Stage;
+constexpr int kRing8Copies = 9;                   // copy instructions per stage
+
+struct RingLane8 {
+  uint32_t koff[2][2];  // K copy source offset in a tile: [block][copy]
+  uint32_t krd[2][2];   // LDS offset of the lane's K granules: [j][s] (block r >> 3)
+  uint32_t vrd;         // LDS offset of the lane's V half row of dimension r (t adds 256)
+  uint32_t srd;         // LDS offset of the (K, V) scales of block grp >> 1
+};
+
+__device__ inline int ring8_h(int R, int be) { return ((R >> 1) & 1) | (((R >> 3) & 1) << 1) | (be << 2); }
+
+__device__ inline RingLane8 ring_lane8(int lane) {
+  RingLane8 L;
+  // copy c of block be writes rows 8 c + (lane >> 3), slot lane & 7, linearly
+#pragma unroll
+  for (int be = 0; be < 2; ++be)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int R = 8 * c + (lane >> 3);
+      L.koff[be][c] = 128 * R + 16 * ((lane & 7) ^ ring8_h(R, be));
+    }
+  const int r = lane & 15, grp = lane >> 4;
+  const int be = r >> 3;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int R = 8 * ((r >> 2) & 1) + 4 * j + (r & 3);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) L.krd[j][s] = 2048 * be + 128 * R + 16 * ((2 * grp + s) ^ ring8_h(R, be));
+  }
+  L.vrd = 4096 + 2048 * (grp >> 1) + 16 * r + 8 * (grp & 1);
+  L.srd = 8192 + 8 * (grp >> 1);
+  return L;
+}
+
+// One direct-to-LDS copy of 4 bytes per active lane.
+template <bool NT>
+__device__ __forceinline__ void copy4_kv(const float* src, uint8_t* dst) {
+  if constexpr (NT) __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 2);
+  else __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+}
+
+// Copy the K and V tiles of kv head g in physical pages p0, p1 into a stage,
+// and their scales (lanes 0-3: K and V of p0, then of p1).
+template <bool NT>
+__device__ __forceinline__ void ring_issue8(uint8_t* stage, const uint8_t* kc, const uint8_t* vc,
+                                            const float* ksc, const float* vsc, int32_t p0, int32_t p1, int H,
+                                            int g, int lane, const RingLane8& L) {
+#pragma unroll
+  for (int be = 0; be < 2; ++be) {
+    const int64_t tile = (int64_t(be ? p1 : p0) * H + g) * (kBS * 128);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) copy16_kv<NT>(kc + tile + L.koff[be][c], stage + 2048 * be + 1024 * c);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) copy16_kv<NT>(vc + tile + 1024 * c + 16 * lane, stage + 4096 + 2048 * be + 1024 * c);
+  }
+  if (lane < 4) {
+    const int64_t sidx = int64_t((lane >> 1) ? p1 : p0) * H + g;
+    copy4_kv<NT>(((lane & 1) ? vsc : ksc) + sidx, stage + 8192);
+  }
+}
+
+// This lane's K granules, V half rows and its block's scales from a stage, in
+// one asm block that waits for them (see ring_read).
+__device__ __forceinline__ void ring_read8(u32x4 (&kseg)[2][2], u32x2 (&vr)[8], u32x2& sc, const uint8_t* stage,
+                                           const RingLane8& L) {
+  const uint32_t base = uint32_t(reinterpret_cast<uintptr_t>(stage));
+  const uint32_t a0 = base + L.krd[0][0], a1 = base + L.krd[0][1], a2 = base + L.krd[1][0],
+                 a3 = base + L.krd[1][1];
+  const uint32_t av = base + L.vrd, as = base + L.srd;
+  asm volatile(
+      "ds_read_b128 %0, %13\n"
+      "ds_read_b128 %1, %14\n"
+      "ds_read_b128 %2, %15\n"
+      "ds_read_b128 %3, %16\n"
+      "ds_read_b64 %4, %17\n"
+      "ds_read_b64 %5, %17 offset:256\n"
+      "ds_read_b64 %6, %17 offset:512\n"
+      "ds_read_b64 %7, %17 offset:768\n"
+      "ds_read_b64 %8, %17 offset:1024\n"
+      "ds_read_b64 %9, %17 offset:1280\n"
+      "ds_read_b64 %10, %17 offset:1536\n"
+      "ds_read_b64 %11, %17 offset:1792\n"
+      "ds_read_b64 %12, %18\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(kseg[0][0]), "=&v"(kseg[0][1]), "=&v"(kseg[1][0]), "=&v"(kseg[1][1]), "=&v"(vr[0]), "=&v"(vr[1]),
+        "=&v"(vr[2]), "=&v"(vr[3]), "=&v"(vr[4]), "=&v"(vr[5]), "=&v"(vr[6]), "=&v"(vr[7]), "=&v"(sc)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(av), "v"(as));
+}
+
 // A segment of a chunk: blocks [j, j1) of request b, kv-head set gs, of which
 // [j, jr1) are read from the cache (APPEND: not the request's last block when
 // it holds only the new token); u is the unit of block j.
@@ -1362,9 +1467,10 @@ __device__ __forceinline__ void ring_next(RingSeg& s, const int32_t* s_pref, int
 // grid: one workgroup per CU (at most kStreamWorkers / 4), 256 threads,
 // kRingLds bytes of dynamic LDS; B <= kRingMaxB.  Arguments and results as
 // decode_stream_kernel<kQBf16, 128, APPEND, false, NT>.
-template <bool APPEND, bool NT>
+template <int QT, bool APPEND, bool NT>
 __global__ void __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
-decode_ring_kernel(void* __restrict__ kc_, void* __restrict__ vc_, const uint16_t* __restrict__ q,
+decode_ring_kernel(void* __restrict__ kc_, void* __restrict__ vc_, float* __restrict__ kscale,
+                   float* __restrict__ vscale, const uint16_t* __restrict__ q,
                    uint16_t* __restrict__ out, const int32_t* __restrict__ tables, int max_blocks,
                    const int32_t* __restrict__ ctx_lens, int B, int max_ctx, int H, int h_q, int G, int n_hgroups,
                    int HS, float scale_log2, int chunk_fixed, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
@@ -1372,23 +1478,32 @@ decode_ring_kernel(void* __restrict__ kc_, void* __restrict__ vc_, const uint16_
                    const uint16_t* __restrict__ v_new, const int32_t* __restrict__ new_slots) {
   constexpr int D = 128;
   constexpr int T8 = D / 16;
-  extern __shared__ __attribute__((aligned(16))) uint8_t s_ring[];  // kRingLds bytes
+  constexpr bool Q8 = QT != kQBf16;
+  // bf16: two stages of 16 KiB per wave (16 copies each); 8-bit: four of 8 KiB
+  // and the scales (kRing8Copies each)
+  constexpr int NST = Q8 ? kRing8Stages : kRingStages;
+  constexpr int STB = Q8 ? kRing8Stage : kRingStage;
+  // 8-bit with APPEND: the wave owning a request's last tile applies the
+  // append's tile rule there (append8_token) before copying it, so every
+  // position, the new one included, is read from the cache
+  constexpr bool APPEND16 = APPEND && !Q8;
+  extern __shared__ __attribute__((aligned(16))) uint8_t s_ring[];  // ring_lds_bytes<QT>() bytes
   __shared__ int32_t s_pref[kRingMaxB + 1];
   __shared__ int32_t s_tmp[4];
   // APPEND: the new tokens go into the cache while the block counts are
   // summed, as in decode_stream_kernel
-  const int pieces = APPEND ? B * H * (D / 8) : 0;
+  const int pieces = APPEND16 ? B * H * (D / 8) : 0;
   const int gthreads = gridDim.x * 256;
   int piece = blockIdx.x * 256 + threadIdx.x;
   u32x4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
   int32_t pslot = -1;
-  if (APPEND && piece < pieces) {
+  if (APPEND16 && piece < pieces) {
     pslot = new_slots[piece / (H * (D / 8))];
     kx = ld16(k_new + int64_t(piece) * 8);
     vx = ld16(v_new + int64_t(piece) * 8);
   }
   block_prefix_blocks<false>(s_pref, s_tmp, ctx_lens, B, max_ctx, 0, 0);
-  if constexpr (APPEND) {
+  if constexpr (APPEND16) {
     uint16_t* kw = static_cast<uint16_t*>(kc_);
     uint16_t* vw = static_cast<uint16_t*>(vc_);
     while (piece < pieces) {
@@ -1443,7 +1558,8 @@ decode_ring_kernel(void* __restrict__ kc_, void* __restrict__ vc_, const uint16_
   const uint8_t* vc = static_cast<const uint8_t*>(vc_);
   const __amdgpu_buffer_rsrc_t rml = raw_rsrc(ws_ml), racc = raw_rsrc(ws_acc);
   const RingLane Lr = ring_lane(lane);
-  uint8_t* ring = s_ring + wv * kRingStages * kRingStage;
+  const RingLane8 L8 = ring_lane8(lane);
+  uint8_t* ring = s_ring + wv * NST * STB;
   auto noscale = [](float&, float&) {};
 
   for (int64_t c = coop ? int64_t(blockIdx.x) : int64_t(blockIdx.x) * 4 + wv; c < ch.N; c += W) {
@@ -1465,7 +1581,7 @@ decode_ring_kernel(void* __restrict__ kc_, void* __restrict__ vc_, const uint16_
     cs.j = int(rem - int64_t(cs.gs) * cs.nb);
     cs.u = u0;
     cs.live = true;
-    ring_fill<APPEND>(cs, ctx_lens, new_slots, max_ctx, u_end);
+    ring_fill<APPEND16>(cs, ctx_lens, new_slots, max_ctx, u_end);
 
     // The copy issuer walks the same stages as the steps below, one stage
     // ahead: a stage is blocks (icb, icb + 1) of segment `is` (the second
@@ -1476,7 +1592,7 @@ decode_ring_kernel(void* __restrict__ kc_, void* __restrict__ vc_, const uint16_
       while (is.live && icb >= is.jr1) {
         ring_next(is, s_pref, hsets, u_end);
         if (is.live) {
-          ring_fill<APPEND>(is, ctx_lens, new_slots, max_ctx, u_end);
+          ring_fill<APPEND16>(is, ctx_lens, new_slots, max_ctx, u_end);
           icb = is.j;
         }
       }
@@ -1487,13 +1603,36 @@ decode_ring_kernel(void* __restrict__ kc_, void* __restrict__ vc_, const uint16_
       if (!is.live) return;
       const int32_t* trow = tables + int64_t(is.b) * max_blocks;
       const int gh = coop ? 4 * is.gs + wv : is.gs;
-      ring_issue<NT>(stage, kc, vc, trow[icb], trow[min(icb + 1, is.jr1 - 1)], H, gh / n_hgroups, Lr);
+      const int g = gh / n_hgroups;
+      const int32_t p0 = trow[icb], p1 = trow[min(icb + 1, is.jr1 - 1)];
+      if constexpr (Q8) {
+        if constexpr (APPEND) {
+          // the stage holding a request's last block, whose tile takes the
+          // new token: apply the append's rule to the tile first (only this
+          // wave reads it: one kv-head group per kv head), and let its stores
+          // land before the copy reads the tile
+          const int tb = is.nb - 1;
+          const int32_t slot = __builtin_amdgcn_readfirstlane(new_slots[is.b]);
+          if (__builtin_expect(is.j1 == is.nb && slot >= 0 && unsigned(tb - icb) < 2u, 0)) {  // rare: keep it out of line
+            append8_token<D, QT == kQInt8>(static_cast<uint8_t*>(kc_), static_cast<uint8_t*>(vc_), kscale, vscale,
+                                           int64_t(slot / kBS) * H + g, slot % kBS,
+                                           k_new + (int64_t(is.b) * H + g) * D, v_new + (int64_t(is.b) * H + g) * D,
+                                           lane);
+            wait_all_memory();
+          }
+        }
+        ring_issue8<NT>(stage, kc, vc, kscale, vscale, p0, p1, H, g, lane, L8);
+      } else {
+        ring_issue<NT>(stage, kc, vc, p0, p1, H, g, Lr);
+      }
       ++issued;
       icb += 2;
       iss_skip();
     };
-#pragma unroll
-    for (int n = 0; n < kRingStages; ++n) issue_next(ring + n * kRingStage);
+    // one copy of issue_next's code for the first stages (its 8-bit append
+    // is large, and code size costs the one-workgroup-per-CU kernel)
+#pragma unroll 1
+    for (int n = 0; n < NST; ++n) issue_next(ring + n * STB);
 
     int consumed = 0;
     int role = 0;
@@ -1506,12 +1645,12 @@ decode_ring_kernel(void* __restrict__ kc_, void* __restrict__ vc_, const uint16_
       const int nh = min(16, G - hg * 16);
       const int64_t row0 = int64_t(b) * h_q + head0;
       u32x4 qv[D / 32];
-      load_q<kQBf16, D>(qv, q, row0, r, grp, nh);
+      const float qsi = load_q<QT, D>(qv, q, row0, r, grp, nh);
       WaveState<D> st;
 #pragma unroll
       for (int t = 0; t < T8; ++t) st.acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int ctx = clamp_ctx(ctx_lens, b, max_ctx);
-      const bool app = APPEND && new_slots[b] >= 0;
+      const bool app = APPEND16 && new_slots[b] >= 0;
       const int ctx_c = ctx - (app ? 1 : 0);
       // the segment that ends the request adds the new token: its rows are
       // loaded now, so that the copies in flight are not waited for at the end
@@ -1529,24 +1668,63 @@ decode_ring_kernel(void* __restrict__ kc_, void* __restrict__ vc_, const uint16_
       if (vpatch)
         vtile = static_cast<uint8_t*>(vc_) + (int64_t(tables[int64_t(b) * max_blocks + tb]) * H + g) * (kBS * D * 2);
       for (int cb = cs.j; cb < cs.jr1; cb += 2, ++consumed) {
-        uint8_t* stage = ring + (consumed % kRingStages) * kRingStage;
-        // this stage's 16 copies have landed once at most the next stage's
-        // 16 are in flight (copies complete in order)
-        if (issued > consumed + 1) __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16)
-        else __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0)
+        uint8_t* stage = ring + (consumed % NST) * STB;
         u32x4 kop[kStreamNB][D / 32];
         u32x4 vraw[T8];
-        ring_read(kop, vraw, stage, Lr);
+        float ksc = 1.0f, vsc = 1.0f;
+        if constexpr (Q8) {
+          // this stage's copies have landed once at most the later stages'
+          // copies are in flight (copies complete in order)
+          const int later = issued - consumed - 1;
+          if (later >= 3) __builtin_amdgcn_s_waitcnt(0x4F7B);       // vmcnt(27)
+          else if (later == 2) __builtin_amdgcn_s_waitcnt(0x4F72);  // vmcnt(18)
+          else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0F79);  // vmcnt(9)
+          else __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0)
+          u32x4 kseg[2][2];
+          u32x2 v8[T8];
+          u32x2 sc;
+          ring_read8(kseg, v8, sc, stage, L8);
+#pragma unroll
+          for (int j = 0; j < kStreamNB; ++j)
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk) {
+              const u32x4& sv = kseg[j][kk / 2];
+              const u32x2 a = q8x4_to_op<QT>(sv[(kk % 2) * 2 + 0]);
+              const u32x2 bq = q8x4_to_op<QT>(sv[(kk % 2) * 2 + 1]);
+              kop[j][kk] = u32x4{a[0], a[1], bq[0], bq[1]};
+            }
+#pragma unroll
+          for (int t = 0; t < T8; ++t) vraw[t] = u32x4{v8[t][0], v8[t][1], 0, 0};
+          ksc = __uint_as_float(sc[0]);
+          vsc = __uint_as_float(sc[1]);
+        } else {
+          // this stage's 16 copies have landed once at most the next stage's
+          // 16 are in flight (copies complete in order)
+          if (issued > consumed + 1) __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16)
+          else __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0)
+          ring_read(kop, vraw, stage, Lr);
+        }
         issue_next(stage);  // the stage is read: the copies two stages on refill it
-        if constexpr (APPEND) {
+        if constexpr (APPEND16) {
           if (vpatch && unsigned(tb - cb) < 2u) {
             uint32_t val[T8];
             token_v_values<D>(val, trw, r);
             patch_token_v<D>(vraw, val, vtile, tb - cb, (ctx - 1) & (kBS - 1), r, grp);
           }
         }
-        stream_step<kQBf16, D, false>(st, kop, vraw, qv, cb, cs.jr1, ctx_c, scale_log2, 1.0f, 1.0f, grp, 0, 0, 1.0f,
-                                      noscale);
+        if constexpr (Q8)
+          stream_step<QT, D, false>(st, kop, vraw, qv, cb, cs.jr1, ctx, scale_log2, ksc, vsc, grp, 0, 0, qsi,
+                                    [&](float& ks, float& vs) {
+                                      ks = ksc;
+                                      vs = vsc;
+                                    });
+        else
+          stream_step<kQBf16, D, false>(st, kop, vraw, qv, cb, cs.jr1, ctx_c, scale_log2, 1.0f, 1.0f, grp, 0, 0,
+                                        1.0f, noscale);
+      }
+      if constexpr (QT == kQInt8) {  // back to true units (acc was relative to st.vs)
+#pragma unroll
+        for (int t = 0; t < T8; ++t) st.acc[t] *= st.vs;
       }
       if (tok) fold_token<D>(st, trw, qv, scale_log2, grp);
       const float l = wave_sum16(st.l);
@@ -1585,7 +1763,7 @@ decode_ring_kernel(void* __restrict__ kc_, void* __restrict__ vc_, const uint16_
         }
       }
       ring_next(cs, s_pref, hsets, u_end);
-      if (cs.live) ring_fill<APPEND>(cs, ctx_lens, new_slots, max_ctx, u_end);
+      if (cs.live) ring_fill<APPEND16>(cs, ctx_lens, new_slots, max_ctx, u_end);
       role = 1;
     }
   }
@@ -2007,8 +2185,9 @@ int launch_decode_d(const DecodeArgs& a, hipStream_t s) {
   uint8_t* kc = static_cast<uint8_t*>(a.pool->k_cache) + lb;
   uint8_t* vc = static_cast<uint8_t*>(a.pool->v_cache) + lb;
   const int64_t so = int64_t(a.layer) * d.num_blocks * H;
-  // bf16, head_dim 128, no window: the ring decode, one workgroup per CU
-  const bool ring = d.cache_dtype == KV_BF16 && D == 128 && !(a.window > 0) && a.B <= kRingMaxB;
+  // head_dim 128, no window: the ring decode, one workgroup per CU (bf16,
+  // fp8 and int8 caches)
+  const bool ring = D == 128 && !(a.window > 0) && a.B <= kRingMaxB;
   int workers = a.workers;
   if (ring) {
     const int cus = ring_workgroups();
@@ -2042,17 +2221,19 @@ int launch_decode_d(const DecodeArgs& a, hipStream_t s) {
   };
   using F = std::false_type;
   using T = std::true_type;
-  auto go_ring = [&](auto append, auto ntc) -> int {
+  auto go_ring = [&](auto qt, auto append, auto ntc) -> int {
+    constexpr int QT = decltype(qt)::value;
     constexpr bool AP = decltype(append)::value, NT = decltype(ntc)::value;
+    constexpr int lds = QT == kQBf16 ? kRingLds : kRing8Lds;
     static bool lds_set = false;  // the ring's dynamic LDS is above the default bound
     if (!lds_set) {
-      const hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_ring_kernel<AP, NT>),
-                                                hipFuncAttributeMaxDynamicSharedMemorySize, kRingLds);
+      const hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_ring_kernel<QT, AP, NT>),
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, lds);
       if (ea != hipSuccess) return fail(KV_E_HIP, "decode: ring LDS attribute: %s", hipGetErrorString(ea));
       lds_set = true;
     }
-    decode_ring_kernel<AP, NT><<<grid, 256, kRingLds, s>>>(
-        kc, vc, q, out, a.tables, a.max_blocks, a.ctx, a.B, a.max_ctx, H, a.h_q, G, nhg, a.hs, sl, a.chunk, a.ws_ml,
+    decode_ring_kernel<QT, AP, NT><<<grid, 256, lds, s>>>(
+        kc, vc, ks, vs, q, out, a.tables, a.max_blocks, a.ctx, a.B, a.max_ctx, H, a.h_q, G, nhg, a.hs, sl, a.chunk, a.ws_ml,
         a.ws_acc, a.ws_pref, a.merge_inline ? a.ws_cnt : nullptr, static_cast<const uint16_t*>(a.k_new),
         static_cast<const uint16_t*>(a.v_new), a.new_slots);
     return ok();
@@ -2061,8 +2242,11 @@ int launch_decode_d(const DecodeArgs& a, hipStream_t s) {
   using QF = std::integral_constant<int, kQFp8>;
   using QI = std::integral_constant<int, kQInt8>;
   if (ring) {
-    const int rc = a.new_slots ? (nt ? go_ring(T{}, T{}) : go_ring(T{}, F{}))
-                               : (nt ? go_ring(F{}, T{}) : go_ring(F{}, F{}));
+    auto ring_qt = [&](auto qt) -> int {
+      return a.new_slots ? (nt ? go_ring(qt, T{}, T{}) : go_ring(qt, T{}, F{}))
+                         : (nt ? go_ring(qt, F{}, T{}) : go_ring(qt, F{}, F{}));
+    };
+    const int rc = d.cache_dtype == KV_BF16 ? ring_qt(QB{}) : d.cache_dtype == KV_FP8_E4M3 ? ring_qt(QF{}) : ring_qt(QI{});
     if (rc != KV_OK) return rc;
   } else if (d.cache_dtype == KV_BF16) {
     if (a.new_slots) {  // fused append
