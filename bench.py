@@ -111,9 +111,9 @@ DEFAULT_SEED = {"llama3_8b": 2, "llama3_70b_long": 3, "fp8": 5, "int8": 5, "pref
 # calibration there (fetch x2, write x1).  They hold for the kernel source they
 # were taken on, identified by its SHA-256; any other source reports null.
 TRAFFIC_SOURCE = "paged_kv_cache_271_amd/csrc/decode.hip"
-TRAFFIC_SHA256 = "29445fe3d561ba854c09900b9a72424457d46645bdbab94aa3b4133d7dd060ef"
-TRAFFIC_BYTES = {"llama3_8b": 592_626_960, "fp8": 1_255_186_226, "llama3_70b_long": 1_348_117_414,
-                 "int8": 1_246_682_512, "llama3_8b_window": 1_110_452_432}
+TRAFFIC_SHA256 = "c65be94e1f91fb0551f458f2ad00ac99b51c15a8c916da81152e90567d35b3c0"
+TRAFFIC_BYTES = {"llama3_8b": 592_552_528, "fp8": 1_243_870_375, "llama3_70b_long": 1_348_072_089,
+                 "int8": 1_238_830_617, "llama3_8b_window": 1_110_533_788}
 # The same per launch of prefill_kernel and of block_copy_kernel, from
 # profiles/prefill_llama3_8b_counters.md and
 # profiles/block_copy_cow_fork_hbm_counters.md: (source, its SHA-256, bytes).
