@@ -127,9 +127,10 @@ TRAFFIC_OTHER = {
 
 def decode_kernel_name(dtype, head_dim, window, batch):
     """The decode kernel the library launches for such a step: the LDS-ring
-    kernel for unwindowed bf16, fp8 and int8 batches with head_dim 128 of up
-    to 4096 requests, the register-streaming kernel otherwise."""
-    ring = dtype in ("bf16", "fp8", "int8") and head_dim == 128 and not window and batch <= 4096
+    kernel for bf16, fp8 and int8 batches with head_dim 128 of up to 4096
+    requests (windowed ones on bf16 caches), the register-streaming kernel
+    otherwise."""
+    ring = head_dim == 128 and batch <= 4096 and (dtype == "bf16" or (dtype in ("fp8", "int8") and not window))
     return "decode_ring_kernel" if ring else "decode_stream_kernel"
 
 

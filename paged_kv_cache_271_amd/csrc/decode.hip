@@ -1429,23 +1429,39 @@ __device__ __forceinline__ void ring_read8(u32x4 (&kseg)[2][2], u32x2 (&vr)[8], 
 // A segment of a chunk: blocks [j, j1) of request b, kv-head set gs, of which
 // [j, jr1) are read from the cache (APPEND: not the request's last block when
 // it holds only the new token); u is the unit of block j.
+// WIN: blocks count the pages the request visits (visited_pages); visited
+// page v is logical page v below a and v + off from a on.  A step never
+// spans the two ranges: each range is stepped from its start (ring_pend).
 struct RingSeg {
   int b, gs, j, j1, nb, jr1;
+  int a, off;
   int64_t u;
   bool live;
 };
 
-template <bool APPEND>
+template <bool APPEND, bool WIN>
 __device__ __forceinline__ void ring_fill(RingSeg& s, const int32_t* ctx_lens, const int32_t* new_slots, int max_ctx,
-                                          int64_t u_end) {
+                                          int64_t u_end, int sink, int window) {
   s.j1 = int(min<int64_t>(s.nb, s.j + (u_end - s.u)));
   s.jr1 = s.j1;
-  if constexpr (APPEND) {
+  s.a = s.nb;
+  s.off = 0;
+  if constexpr (WIN) {
+    const VisitedPages vp = visited_pages<true>(clamp_ctx(ctx_lens, s.b, max_ctx), sink, window);
+    s.a = vp.a;
+    s.off = vp.c - vp.a;
+  } else if constexpr (APPEND) {
     const int ctx = clamp_ctx(ctx_lens, s.b, max_ctx);
     const bool app = new_slots[s.b] >= 0;
     s.jr1 = min(s.j1, (ctx - (app ? 1 : 0) + kBS - 1) / kBS);
   }
 }
+
+// End (visited) of the range a step starting at visited page v lies in, the
+// logical page of visited page v, and the next step's start.
+__device__ __forceinline__ int ring_pend(const RingSeg& s, int v) { return v < s.a ? min(s.jr1, s.a) : s.jr1; }
+__device__ __forceinline__ int ring_logical(const RingSeg& s, int v) { return v < s.a ? v : v + s.off; }
+__device__ __forceinline__ int ring_step_next(const RingSeg& s, int v) { return min(v + 2, ring_pend(s, v)); }
 
 // The chunk's next segment (live false past its end).
 __device__ __forceinline__ void ring_next(RingSeg& s, const int32_t* s_pref, int hsets, int64_t u_end) {
@@ -1467,7 +1483,7 @@ __device__ __forceinline__ void ring_next(RingSeg& s, const int32_t* s_pref, int
 // grid: one workgroup per CU (at most kStreamWorkers / 4), 256 threads,
 // kRingLds bytes of dynamic LDS; B <= kRingMaxB.  Arguments and results as
 // decode_stream_kernel<kQBf16, 128, APPEND, false, NT>.
-template <int QT, bool APPEND, bool NT>
+template <int QT, bool APPEND, bool WIN, bool NT>
 __global__ void __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_ring_kernel(void* __restrict__ kc_, void* __restrict__ vc_, float* __restrict__ kscale,
                    float* __restrict__ vscale, const uint16_t* __restrict__ q,
@@ -1475,7 +1491,8 @@ decode_ring_kernel(void* __restrict__ kc_, void* __restrict__ vc_, float* __rest
                    const int32_t* __restrict__ ctx_lens, int B, int max_ctx, int H, int h_q, int G, int n_hgroups,
                    int HS, float scale_log2, int chunk_fixed, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
                    int32_t* __restrict__ ws_pref, int32_t* __restrict__ ws_cnt, const uint16_t* __restrict__ k_new,
-                   const uint16_t* __restrict__ v_new, const int32_t* __restrict__ new_slots) {
+                   const uint16_t* __restrict__ v_new, const int32_t* __restrict__ new_slots, int sink,
+                   int window) {
   constexpr int D = 128;
   constexpr int T8 = D / 16;
   constexpr bool Q8 = QT != kQBf16;
@@ -1502,7 +1519,7 @@ decode_ring_kernel(void* __restrict__ kc_, void* __restrict__ vc_, float* __rest
     kx = ld16(k_new + int64_t(piece) * 8);
     vx = ld16(v_new + int64_t(piece) * 8);
   }
-  block_prefix_blocks<false>(s_pref, s_tmp, ctx_lens, B, max_ctx, 0, 0);
+  block_prefix_blocks<WIN>(s_pref, s_tmp, ctx_lens, B, max_ctx, sink, window);
   if constexpr (APPEND16) {
     uint16_t* kw = static_cast<uint16_t*>(kc_);
     uint16_t* vw = static_cast<uint16_t*>(vc_);
@@ -1581,7 +1598,7 @@ decode_ring_kernel(void* __restrict__ kc_, void* __restrict__ vc_, float* __rest
     cs.j = int(rem - int64_t(cs.gs) * cs.nb);
     cs.u = u0;
     cs.live = true;
-    ring_fill<APPEND16>(cs, ctx_lens, new_slots, max_ctx, u_end);
+    ring_fill<APPEND16, WIN>(cs, ctx_lens, new_slots, max_ctx, u_end, sink, window);
 
     // The copy issuer walks the same stages as the steps below, one stage
     // ahead: a stage is blocks (icb, icb + 1) of segment `is` (the second
@@ -1592,7 +1609,7 @@ decode_ring_kernel(void* __restrict__ kc_, void* __restrict__ vc_, float* __rest
       while (is.live && icb >= is.jr1) {
         ring_next(is, s_pref, hsets, u_end);
         if (is.live) {
-          ring_fill<APPEND16>(is, ctx_lens, new_slots, max_ctx, u_end);
+          ring_fill<APPEND16, WIN>(is, ctx_lens, new_slots, max_ctx, u_end, sink, window);
           icb = is.j;
         }
       }
@@ -1604,7 +1621,8 @@ decode_ring_kernel(void* __restrict__ kc_, void* __restrict__ vc_, float* __rest
       const int32_t* trow = tables + int64_t(is.b) * max_blocks;
       const int gh = coop ? 4 * is.gs + wv : is.gs;
       const int g = gh / n_hgroups;
-      const int32_t p0 = trow[icb], p1 = trow[min(icb + 1, is.jr1 - 1)];
+      const int ipe = ring_pend(is, icb);
+      const int32_t p0 = trow[ring_logical(is, icb)], p1 = trow[ring_logical(is, min(icb + 1, ipe - 1))];
       if constexpr (Q8) {
         if constexpr (APPEND) {
           // the stage holding a request's last block, whose tile takes the
@@ -1626,7 +1644,7 @@ decode_ring_kernel(void* __restrict__ kc_, void* __restrict__ vc_, float* __rest
         ring_issue<NT>(stage, kc, vc, p0, p1, H, g, Lr);
       }
       ++issued;
-      icb += 2;
+      icb = min(icb + 2, ipe);
       iss_skip();
     };
     // one copy of issue_next's code for the first stages (its 8-bit append
@@ -1662,12 +1680,16 @@ decode_ring_kernel(void* __restrict__ kc_, void* __restrict__ vc_, float* __rest
       }
       // ... and, unless the token starts its block, this wave writes that
       // block's V rows with the token's values in place (patch_token_v)
-      const int tb = cs.nb - 1;
+      const int tb = (ctx + kBS - 1) / kBS - 1;  // the request's last (logical) block
       const bool vpatch = tok && ((ctx - 1) & (kBS - 1)) != 0;
       uint8_t* vtile = nullptr;
       if (vpatch)
         vtile = static_cast<uint8_t*>(vc_) + (int64_t(tables[int64_t(b) * max_blocks + tb]) * H + g) * (kBS * D * 2);
-      for (int cb = cs.j; cb < cs.jr1; cb += 2, ++consumed) {
+      const int win_lo = WIN ? max(0, ctx - window) : 0;
+      for (int cbv = cs.j; cbv < cs.jr1; cbv = ring_step_next(cs, cbv), ++consumed) {
+        // the step's first block and the end of its range, as logical pages
+        const int cb = ring_logical(cs, cbv);
+        const int pe = ring_logical(cs, ring_pend(cs, cbv) - 1) + 1;
         uint8_t* stage = ring + (consumed % NST) * STB;
         u32x4 kop[kStreamNB][D / 32];
         u32x4 vraw[T8];
@@ -1713,14 +1735,14 @@ decode_ring_kernel(void* __restrict__ kc_, void* __restrict__ vc_, float* __rest
           }
         }
         if constexpr (Q8)
-          stream_step<QT, D, false>(st, kop, vraw, qv, cb, cs.jr1, ctx, scale_log2, ksc, vsc, grp, 0, 0, qsi,
+          stream_step<QT, D, WIN>(st, kop, vraw, qv, cb, pe, ctx, scale_log2, ksc, vsc, grp, sink, win_lo, qsi,
                                     [&](float& ks, float& vs) {
                                       ks = ksc;
                                       vs = vsc;
                                     });
         else
-          stream_step<kQBf16, D, false>(st, kop, vraw, qv, cb, cs.jr1, ctx_c, scale_log2, 1.0f, 1.0f, grp, 0, 0,
-                                        1.0f, noscale);
+          stream_step<kQBf16, D, WIN>(st, kop, vraw, qv, cb, pe, ctx_c, scale_log2, 1.0f, 1.0f, grp, sink, win_lo,
+                                      1.0f, noscale);
       }
       if constexpr (QT == kQInt8) {  // back to true units (acc was relative to st.vs)
 #pragma unroll
@@ -1763,7 +1785,7 @@ decode_ring_kernel(void* __restrict__ kc_, void* __restrict__ vc_, float* __rest
         }
       }
       ring_next(cs, s_pref, hsets, u_end);
-      if (cs.live) ring_fill<APPEND16>(cs, ctx_lens, new_slots, max_ctx, u_end);
+      if (cs.live) ring_fill<APPEND16, WIN>(cs, ctx_lens, new_slots, max_ctx, u_end, sink, window);
       role = 1;
     }
   }
@@ -2185,9 +2207,9 @@ int launch_decode_d(const DecodeArgs& a, hipStream_t s) {
   uint8_t* kc = static_cast<uint8_t*>(a.pool->k_cache) + lb;
   uint8_t* vc = static_cast<uint8_t*>(a.pool->v_cache) + lb;
   const int64_t so = int64_t(a.layer) * d.num_blocks * H;
-  // head_dim 128, no window: the ring decode, one workgroup per CU (bf16,
-  // fp8 and int8 caches)
-  const bool ring = D == 128 && !(a.window > 0) && a.B <= kRingMaxB;
+  // head_dim 128: the ring decode, one workgroup per CU (bf16, fp8 and int8
+  // caches; windows on bf16 caches)
+  const bool ring = D == 128 && a.B <= kRingMaxB && (!(a.window > 0) || d.cache_dtype == KV_BF16);
   int workers = a.workers;
   if (ring) {
     const int cus = ring_workgroups();
@@ -2221,32 +2243,34 @@ int launch_decode_d(const DecodeArgs& a, hipStream_t s) {
   };
   using F = std::false_type;
   using T = std::true_type;
-  auto go_ring = [&](auto qt, auto append, auto ntc) -> int {
+  auto go_ring = [&](auto qt, auto append, auto window, auto ntc) -> int {
     constexpr int QT = decltype(qt)::value;
-    constexpr bool AP = decltype(append)::value, NT = decltype(ntc)::value;
+    constexpr bool AP = decltype(append)::value, WN = decltype(window)::value, NT = decltype(ntc)::value;
     constexpr int lds = QT == kQBf16 ? kRingLds : kRing8Lds;
     static bool lds_set = false;  // the ring's dynamic LDS is above the default bound
     if (!lds_set) {
-      const hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_ring_kernel<QT, AP, NT>),
+      const hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_ring_kernel<QT, AP, WN, NT>),
                                                 hipFuncAttributeMaxDynamicSharedMemorySize, lds);
       if (ea != hipSuccess) return fail(KV_E_HIP, "decode: ring LDS attribute: %s", hipGetErrorString(ea));
       lds_set = true;
     }
-    decode_ring_kernel<QT, AP, NT><<<grid, 256, lds, s>>>(
+    decode_ring_kernel<QT, AP, WN, NT><<<grid, 256, lds, s>>>(
         kc, vc, ks, vs, q, out, a.tables, a.max_blocks, a.ctx, a.B, a.max_ctx, H, a.h_q, G, nhg, a.hs, sl, a.chunk, a.ws_ml,
         a.ws_acc, a.ws_pref, a.merge_inline ? a.ws_cnt : nullptr, static_cast<const uint16_t*>(a.k_new),
-        static_cast<const uint16_t*>(a.v_new), a.new_slots);
+        static_cast<const uint16_t*>(a.v_new), a.new_slots, a.sink, a.window);
     return ok();
   };
   using QB = std::integral_constant<int, kQBf16>;
   using QF = std::integral_constant<int, kQFp8>;
   using QI = std::integral_constant<int, kQInt8>;
   if (ring) {
-    auto ring_qt = [&](auto qt) -> int {
-      return a.new_slots ? (nt ? go_ring(qt, T{}, T{}) : go_ring(qt, T{}, F{}))
-                         : (nt ? go_ring(qt, F{}, T{}) : go_ring(qt, F{}, F{}));
+    auto ring_qt = [&](auto qt, auto window) -> int {
+      return a.new_slots ? (nt ? go_ring(qt, T{}, window, T{}) : go_ring(qt, T{}, window, F{}))
+                         : (nt ? go_ring(qt, F{}, window, T{}) : go_ring(qt, F{}, window, F{}));
     };
-    const int rc = d.cache_dtype == KV_BF16 ? ring_qt(QB{}) : d.cache_dtype == KV_FP8_E4M3 ? ring_qt(QF{}) : ring_qt(QI{});
+    const int rc = d.cache_dtype == KV_BF16 ? (win ? ring_qt(QB{}, T{}) : ring_qt(QB{}, F{}))
+                   : d.cache_dtype == KV_FP8_E4M3 ? ring_qt(QF{}, F{})
+                                                  : ring_qt(QI{}, F{});
     if (rc != KV_OK) return rc;
   } else if (d.cache_dtype == KV_BF16) {
     if (a.new_slots) {  // fused append
