@@ -415,9 +415,10 @@ __device__ __forceinline__ void stream_step(WaveState<D>& st, const u32x4 (&kop)
   // for any m, which is all the finish and the piece merge assume.
   if (__builtin_amdgcn_ballot_w64(mx > st.m + kLazyLog2 || vs_grew) != 0) {
     const float m_new = fmaxf(st.m, mx);
-    // WIN with a fused append: a row may have read no token yet (a window
-    // of one whose only position is the new token); its state stays empty
-    const float m_ref = WIN && m_new == -INFINITY ? 0.0f : m_new;
+    // a fused append: a row may have read no cached token yet (its segment
+    // starts at the block that holds only the new token, or a window of one
+    // whose only position is that token); its state stays empty
+    const float m_ref = m_new == -INFINITY ? 0.0f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(st.m - m_ref);
     st.l *= alpha;
     st.m = m_new;
@@ -425,7 +426,7 @@ __device__ __forceinline__ void stream_step(WaveState<D>& st, const u32x4 (&kop)
 #pragma unroll
     for (int t = 0; t < T8; ++t) st.acc[t] *= afac;
   }
-  const float m_use = WIN && st.m == -INFINITY ? 0.0f : st.m;
+  const float m_use = st.m == -INFINITY ? 0.0f : st.m;
   float psum = 0.0f;
 #pragma unroll
   for (int j = 0; j < NB; ++j)
@@ -1432,6 +1433,8 @@ __device__ __forceinline__ void ring_read8(u32x4 (&kseg)[2][2], u32x2 (&vr)[8], 
 // WIN: blocks count the pages the request visits (visited_pages); visited
 // page v is logical page v below a and v + off from a on.  A step never
 // spans the two ranges: each range is stepped from its start (ring_pend).
+// Every block of the segment is read, the one holding a fused append's new
+// token included (its slot is masked; the wave writes that block's V rows).
 struct RingSeg {
   int b, gs, j, j1, nb, jr1;
   int a, off;
@@ -1439,9 +1442,9 @@ struct RingSeg {
   bool live;
 };
 
-template <bool APPEND, bool WIN>
-__device__ __forceinline__ void ring_fill(RingSeg& s, const int32_t* ctx_lens, const int32_t* new_slots, int max_ctx,
-                                          int64_t u_end, int sink, int window) {
+template <bool WIN>
+__device__ __forceinline__ void ring_fill(RingSeg& s, const int32_t* ctx_lens, int max_ctx, int64_t u_end, int sink,
+                                          int window) {
   s.j1 = int(min<int64_t>(s.nb, s.j + (u_end - s.u)));
   s.jr1 = s.j1;
   s.a = s.nb;
@@ -1450,10 +1453,6 @@ __device__ __forceinline__ void ring_fill(RingSeg& s, const int32_t* ctx_lens, c
     const VisitedPages vp = visited_pages<true>(clamp_ctx(ctx_lens, s.b, max_ctx), sink, window);
     s.a = vp.a;
     s.off = vp.c - vp.a;
-  } else if constexpr (APPEND) {
-    const int ctx = clamp_ctx(ctx_lens, s.b, max_ctx);
-    const bool app = new_slots[s.b] >= 0;
-    s.jr1 = min(s.j1, (ctx - (app ? 1 : 0) + kBS - 1) / kBS);
   }
 }
 
@@ -1507,22 +1506,21 @@ decode_ring_kernel(void* __restrict__ kc_, void* __restrict__ vc_, float* __rest
   extern __shared__ __attribute__((aligned(16))) uint8_t s_ring[];  // ring_lds_bytes<QT>() bytes
   __shared__ int32_t s_pref[kRingMaxB + 1];
   __shared__ int32_t s_tmp[4];
-  // APPEND: the new tokens go into the cache while the block counts are
-  // summed, as in decode_stream_kernel
+  // APPEND (bf16): the new tokens' K rows go into the cache while the block
+  // counts are summed; their V slots are written with the V rows of the
+  // token's block by the wave that reads it
   const int pieces = APPEND16 ? B * H * (D / 8) : 0;
   const int gthreads = gridDim.x * 256;
   int piece = blockIdx.x * 256 + threadIdx.x;
-  u32x4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
+  u32x4 kx = {0, 0, 0, 0};
   int32_t pslot = -1;
   if (APPEND16 && piece < pieces) {
     pslot = new_slots[piece / (H * (D / 8))];
     kx = ld16(k_new + int64_t(piece) * 8);
-    vx = ld16(v_new + int64_t(piece) * 8);
   }
   block_prefix_blocks<WIN>(s_pref, s_tmp, ctx_lens, B, max_ctx, sink, window);
   if constexpr (APPEND16) {
     uint16_t* kw = static_cast<uint16_t*>(kc_);
-    uint16_t* vw = static_cast<uint16_t*>(vc_);
     while (piece < pieces) {
       if (pslot >= 0) {
         const int hd = piece % (H * (D / 8));
@@ -1534,19 +1532,12 @@ decode_ring_kernel(void* __restrict__ kc_, void* __restrict__ vc_, float* __rest
         // V is dimension-major, so the slot is 2 bytes in each 32-byte row:
         // such scattered partial writes cost 6 us per Llama-3-8B call.  The
         // wave that reads the request's last block writes its V rows whole
-        // instead (below); only a block that holds nothing but the new token
-        // (offset 0), which no wave reads, gets them here.
-        if (off == 0) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            vw[tile + int64_t(d0 + e) * kBS + off] = uint16_t(vx[e / 2] >> (16 * (e & 1)));
-        }
+        // instead (patch_token_v, below).
       }
       piece += gthreads;
       if (piece < pieces) {
         pslot = new_slots[piece / (H * (D / 8))];
         kx = ld16(k_new + int64_t(piece) * 8);
-        vx = ld16(v_new + int64_t(piece) * 8);
       }
     }
   }
@@ -1598,7 +1589,7 @@ decode_ring_kernel(void* __restrict__ kc_, void* __restrict__ vc_, float* __rest
     cs.j = int(rem - int64_t(cs.gs) * cs.nb);
     cs.u = u0;
     cs.live = true;
-    ring_fill<APPEND16, WIN>(cs, ctx_lens, new_slots, max_ctx, u_end, sink, window);
+    ring_fill<WIN>(cs, ctx_lens, max_ctx, u_end, sink, window);
 
     // The copy issuer walks the same stages as the steps below, one stage
     // ahead: a stage is blocks (icb, icb + 1) of segment `is` (the second
@@ -1609,7 +1600,7 @@ decode_ring_kernel(void* __restrict__ kc_, void* __restrict__ vc_, float* __rest
       while (is.live && icb >= is.jr1) {
         ring_next(is, s_pref, hsets, u_end);
         if (is.live) {
-          ring_fill<APPEND16, WIN>(is, ctx_lens, new_slots, max_ctx, u_end, sink, window);
+          ring_fill<WIN>(is, ctx_lens, max_ctx, u_end, sink, window);
           icb = is.j;
         }
       }
@@ -1678,10 +1669,10 @@ decode_ring_kernel(void* __restrict__ kc_, void* __restrict__ vc_, float* __rest
         const int64_t nrow = (int64_t(b) * H + g) * D;
         load_token<D>(trw, k_new + nrow, v_new + nrow, grp);
       }
-      // ... and, unless the token starts its block, this wave writes that
-      // block's V rows with the token's values in place (patch_token_v)
+      // ... and this wave writes that block's V rows with the token's values
+      // in place (patch_token_v)
       const int tb = (ctx + kBS - 1) / kBS - 1;  // the request's last (logical) block
-      const bool vpatch = tok && ((ctx - 1) & (kBS - 1)) != 0;
+      const bool vpatch = tok;
       uint8_t* vtile = nullptr;
       if (vpatch)
         vtile = static_cast<uint8_t*>(vc_) + (int64_t(tables[int64_t(b) * max_blocks + tb]) * H + g) * (kBS * D * 2);
@@ -1785,7 +1776,7 @@ decode_ring_kernel(void* __restrict__ kc_, void* __restrict__ vc_, float* __rest
         }
       }
       ring_next(cs, s_pref, hsets, u_end);
-      if (cs.live) ring_fill<APPEND16, WIN>(cs, ctx_lens, new_slots, max_ctx, u_end, sink, window);
+      if (cs.live) ring_fill<WIN>(cs, ctx_lens, max_ctx, u_end, sink, window);
       role = 1;
     }
   }

@@ -33,7 +33,9 @@ def _case(dtype, H, D, h_q, seed, poison=False):
 @pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 64), ("fp8", 128), ("int8", 128)])
 def test_decode_append_matches_oracle(gpu_lib, dtype, D):
     c, appends = _case(dtype, 2, D, 8, seed=31)
-    for step, part in enumerate((0, 32)):
+    # partitions of 32 and 16 tokens start pieces at a request's last block,
+    # which after the append may hold only the new token
+    for step, part in enumerate((0, 32, 16)):
         app = appends if step == 0 else np.ones(len(FINAL), bool)
         log(f"{dtype} D={D} step {step} partition {part}")
         got = c.decode_append_step(seed=40 + step, appends=app, partition_tokens=part)
