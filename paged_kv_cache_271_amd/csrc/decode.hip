@@ -1219,8 +1219,10 @@ decode_stream_kernel(void* __restrict__ kc_, void* __restrict__ vc_,
 }
 
 // ------------------------------------------------------------------------
-// Ring decode: bf16 caches, head_dim 128, no window (the Llama-shaped decode
-// steps).  The same work split, state and piece merge as decode_stream_kernel,
+// Ring decode: head_dim 128, batches of up to kRingMaxB requests (bf16 caches,
+// with or without a window; fp8 and int8 caches without one; the bf16 layout
+// is described here, the 8-bit one below).  The same work split, state and
+// piece merge as decode_stream_kernel,
 // with its K/V loads taken off the waves' registers: each wave keeps a ring
 // of two stages in LDS (a stage is one step's K and V tiles, 16 KiB) that it
 // fills with direct-to-LDS copies (global_load_lds_dwordx4: no registers, no
@@ -1480,8 +1482,10 @@ __device__ __forceinline__ void ring_next(RingSeg& s, const int32_t* s_pref, int
 }
 
 // grid: one workgroup per CU (at most kStreamWorkers / 4), 256 threads,
-// kRingLds bytes of dynamic LDS; B <= kRingMaxB.  Arguments and results as
-// decode_stream_kernel<kQBf16, 128, APPEND, false, NT>.
+// kRingLds (bf16) or kRing8Lds (fp8, int8) bytes of dynamic LDS;
+// B <= kRingMaxB.  Arguments and results as decode_stream_kernel<QT, 128,
+// APPEND, WIN, NT> (windows and fused appends on bf16 caches; an 8-bit fused
+// append needs one kv-head group per kv head).
 template <int QT, bool APPEND, bool WIN, bool NT>
 __global__ void __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_ring_kernel(void* __restrict__ kc_, void* __restrict__ vc_, float* __restrict__ kscale,
@@ -1503,7 +1507,7 @@ decode_ring_kernel(void* __restrict__ kc_, void* __restrict__ vc_, float* __rest
   // append's tile rule there (append8_token) before copying it, so every
   // position, the new one included, is read from the cache
   constexpr bool APPEND16 = APPEND && !Q8;
-  extern __shared__ __attribute__((aligned(16))) uint8_t s_ring[];  // ring_lds_bytes<QT>() bytes
+  extern __shared__ __attribute__((aligned(16))) uint8_t s_ring[];  // NST * STB bytes per wave
   __shared__ int32_t s_pref[kRingMaxB + 1];
   __shared__ int32_t s_tmp[4];
   // APPEND (bf16): the new tokens' K rows go into the cache while the block

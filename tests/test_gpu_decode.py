@@ -323,8 +323,8 @@ def test_balanced_split_reused_workspace(gpu_lib):
 def test_largest_batch(gpu_lib, B, D):
     """The largest batches, of 0-40 tokens per request: 8192 (the bound of
     the balanced decode) and 4096 (the bound of the LDS-ring decode, which
-    bf16 pools with head_dim 128 take up to that size; larger batches fall
-    back to the register-streaming decode).  The block prefix is scanned in
+    pools with head_dim 128 take up to that size; larger batches fall back
+    to the register-streaming decode).  The block prefix is scanned in
     many passes, chunks hold many whole requests, empty requests give zeros.
     Plain decode, then the fused step (which also appends B rows); a sample
     of requests is checked against the oracle, and every output is finite."""
