@@ -192,6 +192,21 @@ def test_group_sizes_mqa_mha(gpu_lib, H, h_q):
             assert_close(got[b], ref[b], c.tol_key, f"{dtype} H={H} h_q={h_q} request {b}")
 
 
+@pytest.mark.parametrize("H,h_q", [(1, 32), (4, 4), (2, 40), (1, 1)])
+def test_group_sizes_ring(gpu_lib, H, h_q):
+    """The same group shapes at head_dim 128, where bf16, fp8 and int8 pools
+    run the LDS-ring decode: waves that do not share a request when the
+    kv-head groups do not come in fours, two head groups per kv head when
+    G > 16; balanced and 16-token partitions."""
+    for dtype in ("bf16", "fp8", "int8"):
+        c = Case(dtype, H, 128, h_q, [70, 3, 129, 1000], num_blocks=80, seed=8)
+        ref = c.oracle()
+        for part in (0, 16):
+            got = c.decode(partition_tokens=part)
+            for b in range(4):
+                assert_close(got[b], ref[b], c.tol_key, f"{dtype} H={H} h_q={h_q} part {part} request {b}")
+
+
 # ------------------------------------------------ invariance / poison -------
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8", "int8"])
 def test_poisoned_slots_do_not_leak(gpu_lib, dtype):
