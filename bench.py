@@ -111,9 +111,9 @@ DEFAULT_SEED = {"llama3_8b": 2, "llama3_70b_long": 3, "fp8": 5, "int8": 5, "pref
 # calibration there (fetch x2, write x1).  They hold for the kernel source they
 # were taken on, identified by its SHA-256; any other source reports null.
 TRAFFIC_SOURCE = "paged_kv_cache_271_amd/csrc/decode.hip"
-TRAFFIC_SHA256 = "5b1f5f649ee65a302fd4d3552ec942d0efad9d927475123842a73dd07c7cd93d"
-TRAFFIC_BYTES = {"llama3_8b": 592_539_248, "fp8": 1_243_456_352, "llama3_70b_long": 1_348_093_116,
-                 "int8": 1_238_297_126, "llama3_8b_window": 1_093_897_708}
+TRAFFIC_SHA256 = "82fdfc31accca2ee319bce921d179d13a66b41d228320e68c9f3950f6aa9dc1b"
+TRAFFIC_BYTES = {"llama3_8b": 592_628_899, "fp8": 1_243_550_214, "llama3_70b_long": 1_348_120_755,
+                 "int8": 1_238_546_374, "llama3_8b_window": 1_093_820_896}
 # The same per launch of prefill_kernel and of block_copy_kernel, from
 # profiles/prefill_llama3_8b_counters.md and
 # profiles/block_copy_cow_fork_hbm_counters.md: (source, its SHA-256, bytes).
