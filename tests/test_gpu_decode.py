@@ -334,31 +334,34 @@ def test_balanced_split_reused_workspace(gpu_lib):
     assert np.max(np.abs(fixed - got)) <= 2e-2
 
 
-@pytest.mark.parametrize("B,D", [(8192, 64), (8192, 128), (4096, 128)])
-def test_largest_batch(gpu_lib, B, D):
+@pytest.mark.parametrize("dtype,B,D", [("bf16", 8192, 64), ("bf16", 8192, 128), ("bf16", 4096, 128),
+                                       ("fp8", 8192, 128), ("int8", 4096, 128)])
+def test_largest_batch(gpu_lib, dtype, B, D):
     """The largest batches, of 0-40 tokens per request: 8192 (the bound of
     the balanced decode) and 4096 (the bound of the LDS-ring decode, which
     pools with head_dim 128 take up to that size; larger batches fall back
     to the register-streaming decode).  The block prefix is scanned in
     many passes, chunks hold many whole requests, empty requests give zeros.
     Plain decode, then the fused step (which also appends B rows); a sample
-    of requests is checked against the oracle, and every output is finite."""
+    of requests is checked against the oracle, and every output is finite.
+    8-bit pools: the register-streaming (8192) and ring (4096) decodes with
+    their fused append."""
     rng = np.random.default_rng(81)
     lens = rng.integers(0, 41, B)
     lens[rng.choice(B, 200, replace=False)] = 0
     need = int(sum(oracle.blocks_for(int(n), 16) for n in lens))
-    c = Case("bf16", 2, D, 8, lens, num_blocks=need + B, max_blocks=4, seed=81)
+    c = Case(dtype, 2, D, 8, lens, num_blocks=need + B, max_blocks=4, seed=81, mirror=dtype != "bf16")
     sample = sorted(set(rng.choice(B, 48, replace=False).tolist()) | {0, B - 1, int(np.argmax(lens))})
     got = c.decode()
     assert np.all(np.isfinite(got))
     ref = c.oracle(batch=sample)
     for b in sample:
-        assert_close(got[b], ref[b], "bf16", f"request {b} of {c.lens_list[b]} tokens")
+        assert_close(got[b], ref[b], c.tol_key, f"{dtype} request {b} of {c.lens_list[b]} tokens")
     assert np.all(got[np.array(c.lens_list) == 0] == 0)
     got = c.decode_append_step(seed=82)
     ref = c.oracle(batch=sample)
     for b in sample:
-        assert_close(got[b], ref[b], "bf16", f"fused step, request {b} of {c.lens_list[b]} tokens")
+        assert_close(got[b], ref[b], c.tol_key, f"{dtype} fused step, request {b} of {c.lens_list[b]} tokens")
 
 
 @pytest.mark.parametrize("seed", range(8))
