@@ -119,7 +119,7 @@ TRAFFIC_BYTES = {"llama3_8b": 592_628_899, "fp8": 1_243_550_214, "llama3_70b_lon
 # profiles/block_copy_cow_fork_hbm_counters.md: (source, its SHA-256, bytes).
 TRAFFIC_OTHER = {
     "prefill": ("paged_kv_cache_271_amd/csrc/prefill.hip",
-                "b945496209c1d008c3440b9416689f144f3706c8279255c5525e13a420050de5", 400_594_330),
+                "c29ff9971de46489195d14c3f72811b7f02c516321dfdac52bb9772e2b1902a3", 407_242_084),
     "cow_fork": ("paged_kv_cache_271_amd/csrc/copy.hip",
                  "60ed0088c3233bc027dc247d46fa41f24757ec97b73b00f985caaa8e05e88fc7", 1_073_810_950),
 }

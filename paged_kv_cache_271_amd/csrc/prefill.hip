@@ -21,17 +21,19 @@
 // scores of each row, so the softmax needs no data movement.
 //
 // Keys stream in chunks of 32 (two pages), three workgroups per CU (three
-// waves per SIMD: 166 VGPRs, 40 KiB of LDS each).  Waves 0-1 copy the K
+// waves per SIMD: 164 VGPRs, 40 KiB of LDS each).  Waves 0-1 copy the K
 // pages of a chunk, waves 2-3 its V pages, from HBM straight into LDS
 // (global_load_lds_dwordx4, no registers) while the workgroup computes on
 // the current chunk: three K buffers (K staged two chunks ahead, its copy
 // kept in flight across the barrier) and two V buffers (one ahead), one
 // barrier per chunk.  The copies place 16-byte granules with an XOR swizzle
 // so that the MFMA operand reads of every 16 lanes touch 16 different bank
-// groups.  Softmax per chunk: the running row maximum only moves when a
-// chunk's maximum exceeds it by more than 2^8 (then the accumulators are
-// rescaled), otherwise the weights are formed against the stale maximum and
-// stay below 256, which changes no result beyond rounding.  The causal mask
+// groups.  For head_dim 128 the operand reads and MFMAs of both products are
+// asm blocks that keep two reads in flight.  Softmax per chunk: the running
+// row maximum only moves when a chunk's maximum exceeds it by more than 2^8
+// (then the accumulators are rescaled), otherwise the weights are formed
+// against the stale maximum and stay below 256, which changes no result
+// beyond rounding.  The causal mask
 // is applied only on the chunks that reach a row's own position, and the V
 // rows past the context are zeroed in LDS on the request's last chunk
 // (unwritten slots may hold any bits).  Tiles with the most keys launch
@@ -132,9 +134,10 @@ struct Tile {
   uint32_t csrc[NI];  // element offsets within a page tile of this lane's copies (K for waves 0-1, V for 2-3)
 };
 
-// Copy the K (or V) tiles of chunk `ci` (keys 64 ci .. 64 ci + 63): wave w
-// takes page 4 ci + w, clamped to the request's last page (keys past the
-// context are masked and, for V, zeroed before use).
+// Copy the K (or V) tiles of chunk `ci` (keys 32 ci .. 32 ci + 31): a copying
+// wave takes page 2 ci + pg (pg = w for K, w - 2 for V), clamped to the
+// request's last page (keys past the context are masked and, for V, zeroed
+// before use).
 template <int D>
 __device__ __forceinline__ void issue_tiles(uint16_t* buf, const uint16_t* cache, const uint32_t (&src)[Tile<D>::NI],
                                             int ci, int nb, const int32_t* trow, int H, int g, int pg) {
@@ -190,6 +193,121 @@ __device__ __forceinline__ void chunk_scores(f32x4 (&S)[kRT][kKB][2], const uint
       }
 }
 
+// The same two products for D = 128 as asm blocks that keep two LDS operand
+// reads in flight ahead of the MFMAs using a third.  At three waves per SIMD
+// the compiler, short of registers, reads each operand right before its two
+// MFMAs and waits for it, so every read's latency lies in the wave's path.
+// Here three 16-byte buffers rotate: read i + 2 is issued as soon as the
+// MFMAs of read i - 1 have taken their buffer, and `lgkmcnt(2)` waits only
+// for read i (LDS reads return in order; a scalar load still outstanding
+// only makes the wait stricter).  Every read completes inside its block.
+// The compiler does not see the MFMAs in the blocks, so each block starts
+// with 5 wait states (VALU-written operands read by the first MFMA follow
+// three reads and a wait anyway) and ends with 18, more than an 8-pass
+// MFMA's result needs before a VALU instruction may read it.
+#define PF_MFMA_TAIL "s_nop 7\n s_nop 7\n s_nop 1\n"
+
+// Scores: read 2 kk + j is K operand (k-step kk, keys 4 j ..), at
+// LDS byte address a_kk + 1024 j; it feeds S[rt][0][j] with qv[rt][kk].
+__device__ __forceinline__ void chunk_scores128(f32x4 (&S)[kRT][kKB][2], const uint16_t* kbuf, const Tile<128>& t) {
+  const uint32_t base = uint32_t(reinterpret_cast<uintptr_t>(kbuf));  // LDS offset of the buffer
+  const uint32_t a0 = base + 2 * t.kaddr[0], a1 = base + 2 * t.kaddr[1], a2 = base + 2 * t.kaddr[2],
+                 a3 = base + 2 * t.kaddr[3];
+  u32x4 r0, r1, r2;
+  // %0 %1 = S[0][0][0..1], %2 %3 = S[1][0][0..1]; %4-%6 read buffers;
+  // %7-%10 = qv[0][0..3], %11-%14 = qv[1][0..3]; %15-%18 = a0-a3
+  asm volatile(
+      "s_nop 4\n"
+      "ds_read_b128 %4, %15\n"
+      "ds_read_b128 %5, %15 offset:1024\n"
+      "ds_read_b128 %6, %16\n"
+      "s_waitcnt lgkmcnt(2)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %4, %7, 0\n"
+      "v_mfma_f32_16x16x32_bf16 %2, %4, %11, 0\n"
+      "ds_read_b128 %4, %16 offset:1024\n"
+      "s_waitcnt lgkmcnt(2)\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %5, %7, 0\n"
+      "v_mfma_f32_16x16x32_bf16 %3, %5, %11, 0\n"
+      "ds_read_b128 %5, %17\n"
+      "s_waitcnt lgkmcnt(2)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %6, %8, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %2, %6, %12, %2\n"
+      "ds_read_b128 %6, %17 offset:1024\n"
+      "s_waitcnt lgkmcnt(2)\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %4, %8, %1\n"
+      "v_mfma_f32_16x16x32_bf16 %3, %4, %12, %3\n"
+      "ds_read_b128 %4, %18\n"
+      "s_waitcnt lgkmcnt(2)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %5, %9, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %2, %5, %13, %2\n"
+      "ds_read_b128 %5, %18 offset:1024\n"
+      "s_waitcnt lgkmcnt(2)\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %6, %9, %1\n"
+      "v_mfma_f32_16x16x32_bf16 %3, %6, %13, %3\n"
+      "s_waitcnt lgkmcnt(1)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %4, %10, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %2, %4, %14, %2\n"
+      "s_waitcnt lgkmcnt(0)\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %5, %10, %1\n"
+      "v_mfma_f32_16x16x32_bf16 %3, %5, %14, %3\n"
+      PF_MFMA_TAIL
+      : "=&v"(S[0][0][0]), "=&v"(S[0][0][1]), "=&v"(S[1][0][0]), "=&v"(S[1][0][1]), "=&v"(r0), "=&v"(r1),
+        "=&v"(r2)
+      : "v"(t.qv[0][0]), "v"(t.qv[0][1]), "v"(t.qv[0][2]), "v"(t.qv[0][3]), "v"(t.qv[1][0]), "v"(t.qv[1][1]),
+        "v"(t.qv[1][2]), "v"(t.qv[1][3]), "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+      : "memory");
+}
+
+// PV: read t8 is the V operand of output dims 16 t8 .. (LDS byte address
+// av + 512 t8); it feeds acc[rt][t8] with pop[rt][0].
+__device__ __forceinline__ void chunk_pv128(Tile<128>& t, const uint16_t* vbuf, const u32x4 (&pop)[kRT][kKB]) {
+  const uint32_t av = uint32_t(reinterpret_cast<uintptr_t>(vbuf)) + 2 * t.vaddr;
+  u32x4 r0, r1, r2;
+  // %0-%7 = acc[0][0..7], %8-%15 = acc[1][0..7]; %16-%18 read buffers;
+  // %19 %20 = pop[0][0], pop[1][0]; %21 = av
+  asm volatile(
+      "s_nop 4\n"
+      "ds_read_b128 %16, %21\n"
+      "ds_read_b128 %17, %21 offset:512\n"
+      "ds_read_b128 %18, %21 offset:1024\n"
+      "s_waitcnt lgkmcnt(2)\n"
+      "v_mfma_f32_16x16x32_bf16 %0, %16, %19, %0\n"
+      "v_mfma_f32_16x16x32_bf16 %8, %16, %20, %8\n"
+      "ds_read_b128 %16, %21 offset:1536\n"
+      "s_waitcnt lgkmcnt(2)\n"
+      "v_mfma_f32_16x16x32_bf16 %1, %17, %19, %1\n"
+      "v_mfma_f32_16x16x32_bf16 %9, %17, %20, %9\n"
+      "ds_read_b128 %17, %21 offset:2048\n"
+      "s_waitcnt lgkmcnt(2)\n"
+      "v_mfma_f32_16x16x32_bf16 %2, %18, %19, %2\n"
+      "v_mfma_f32_16x16x32_bf16 %10, %18, %20, %10\n"
+      "ds_read_b128 %18, %21 offset:2560\n"
+      "s_waitcnt lgkmcnt(2)\n"
+      "v_mfma_f32_16x16x32_bf16 %3, %16, %19, %3\n"
+      "v_mfma_f32_16x16x32_bf16 %11, %16, %20, %11\n"
+      "ds_read_b128 %16, %21 offset:3072\n"
+      "s_waitcnt lgkmcnt(2)\n"
+      "v_mfma_f32_16x16x32_bf16 %4, %17, %19, %4\n"
+      "v_mfma_f32_16x16x32_bf16 %12, %17, %20, %12\n"
+      "ds_read_b128 %17, %21 offset:3584\n"
+      "s_waitcnt lgkmcnt(2)\n"
+      "v_mfma_f32_16x16x32_bf16 %5, %18, %19, %5\n"
+      "v_mfma_f32_16x16x32_bf16 %13, %18, %20, %13\n"
+      "s_waitcnt lgkmcnt(1)\n"
+      "v_mfma_f32_16x16x32_bf16 %6, %16, %19, %6\n"
+      "v_mfma_f32_16x16x32_bf16 %14, %16, %20, %14\n"
+      "s_waitcnt lgkmcnt(0)\n"
+      "v_mfma_f32_16x16x32_bf16 %7, %17, %19, %7\n"
+      "v_mfma_f32_16x16x32_bf16 %15, %17, %20, %15\n"
+      PF_MFMA_TAIL
+      : "+v"(t.acc[0][0]), "+v"(t.acc[0][1]), "+v"(t.acc[0][2]), "+v"(t.acc[0][3]), "+v"(t.acc[0][4]),
+        "+v"(t.acc[0][5]), "+v"(t.acc[0][6]), "+v"(t.acc[0][7]), "+v"(t.acc[1][0]), "+v"(t.acc[1][1]),
+        "+v"(t.acc[1][2]), "+v"(t.acc[1][3]), "+v"(t.acc[1][4]), "+v"(t.acc[1][5]), "+v"(t.acc[1][6]),
+        "+v"(t.acc[1][7]), "=&v"(r0), "=&v"(r1), "=&v"(r2)
+      : "v"(pop[0][0]), "v"(pop[1][0]), "v"(av)
+      : "memory");
+}
+
 // Step ci of the pipeline.  K of chunk ci is in k_cur (copied two steps
 // ago), V of chunk ci in v_cur (one step ago).  Waves 0-1 copy K pages and
 // keep the copy of K(ci + 1) in flight across the barrier; waves 2-3 copy V
@@ -216,7 +334,8 @@ __device__ __forceinline__ void chunk_step(Tile<D>& t, const uint16_t* k_cur, ui
     barrier<kWaitLds>();
   }
   f32x4 S[kRT][kKB][2];
-  chunk_scores<D>(S, k_cur, t);
+  if constexpr (D == 128) chunk_scores128(S, k_cur, t);
+  else chunk_scores<D>(S, k_cur, t);
   // raw scores; sl > 0 is folded into the exponent below
   if (k0 + kChunk - 1 > pos_min) {  // some key of the chunk lies after some row of this wave
 #pragma unroll
@@ -281,6 +400,10 @@ __device__ __forceinline__ void chunk_step(Tile<D>& t, const uint16_t* k_cur, ui
     t.l[rt] += ps;
   }
   // PV: each V operand read feeds the kRT row tiles.
+  if constexpr (D == 128) {
+    chunk_pv128(t, v_cur, pop);
+    return;
+  }
 #pragma unroll
   for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
@@ -337,7 +460,7 @@ prefill_kernel(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
   T t;
   // row rt of this lane: q / out row (q0 + tok) * h_q + head, recomputed
   // where needed rather than held through the key loop
-  auto row_of = [&](int rt, bool& ok) -> int64_t {
+  auto row_of = [&](int rt, int c, bool& ok) -> int64_t {
     const int row = 16 * (kRT * w + rt) + c;
     const int tl = row / G;
     ok = tl < tpt && tok0 + tl < tok_end;
@@ -347,7 +470,7 @@ prefill_kernel(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
     bool ok;
-    const int64_t qr = row_of(rt, ok);
+    const int64_t qr = row_of(rt, c, ok);
     const int row = 16 * (kRT * w + rt) + c;
     const int tok = tok0 + (ok ? row / G : 0);
     t.pos[rt] = max(ctx - n_q + tok, 0);  // last key this row reads
@@ -422,7 +545,10 @@ prefill_kernel(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     lt += __shfl_xor(lt, 16);
     lt += __shfl_xor(lt, 32);
     bool ok;
-    const int64_t qr = row_of(rt, ok);
+    // the row's lane column again, from the lane count: the compiler would
+    // otherwise keep the rows' 64-bit column terms through the key loop
+    const int c_end = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) & 15;
+    const int64_t qr = row_of(rt, c_end, ok);
     if (ok) {
       const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
 #pragma unroll
